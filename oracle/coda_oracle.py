@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for the GEMM -> residual -> RMSNorm -> GEMM chain and its backward.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The HIP library
+never calls it and shares no code with it.
+
+Source of every formula: "CODA: Rewriting Transformer Blocks as GEMM-Epilogue
+Programs" as described on the hotdry blog page (section "GEMM-Residual-RMSNorm-
+GEMM reparameterisation": the chain's definition and its reparameterised form;
+section "backward GEMM-epilogue structure": the row statistic s) and on the
+kucoin page (section "CODA: treasure hidden in the coda": r is a row-shared
+scalar that commutes with the second GEMM).
+
+What it computes is the plain, *unfused* definition of the chain, in float64,
+from the exact values of its (bf16) inputs, with no intermediate rounding:
+
+    h   = x @ W0 + z                      (GEMM, residual add)
+    ms  = mean over the D columns of h^2  (RMSNorm statistic)
+    r   = 1 / sqrt(ms + eps)              (row-wise inverse RMS factor)
+    n   = r * h * gamma                   (normalised activation)
+    y   = n @ W1                          (second GEMM)
+
+RMSNorm form (the pages only say "row-wise inverse RMS factor r"): mean over the
+D columns, eps inside the root, no bias, no mean subtraction, gamma multiplies
+elementwise.
+
+Backward of L = <dY, y> for the saved set (h, g, y, r) of a forward, with
+g = h * gamma:
+
+    G      = dY @ W1^T                    (data-gradient GEMM)
+    s_i    = sum_n dY_in * y_in           (the pages' row statistic, moved to the
+                                           GEMM boundary: sum_cols(dY . y))
+    da_ij  = r_i gamma_j G_ij - s_i r_i^2 h_ij / D
+    dgam_j = sum_i G_ij r_i h_ij
+    dW1    = (r . g)^T @ dY               i.e. dW1_jn = sum_i g_ij r_i dY_in
+
+The da formula is the exact gradient of the definition above (d r_i / d h_ij =
+-r_i^3 h_ij / D, and sum_k G_ik gamma_k h_ik = s_i / r_i because
+sum_k G_ik n_ik = sum_n dY_in y_in); the pages print only s. It is pinned
+against torch autograd and finite differences in the tests.
+
+Matrix products use numpy's float64 matmul as a library primitive. Row subsets
+(``rows``) and column subsets are supported because rows of the forward are
+independent and the large configurations are checked on seeded samples.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def f64(t) -> np.ndarray:
+    """Exact widening of a torch tensor (bf16/fp32/fp64) or array to a float64 ndarray."""
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64, copy=False)
+    import torch  # local: the oracle itself is numpy-only
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _take(t, rows=None, cols=None) -> np.ndarray:
+    """float64 copy of t[rows][:, cols] (None = all); t is a torch tensor or ndarray."""
+    if not isinstance(t, np.ndarray):
+        import torch
+        if rows is not None:
+            t = t.index_select(0, torch.as_tensor(np.asarray(rows, dtype=np.int64)))
+        if cols is not None:
+            t = t.index_select(1, torch.as_tensor(np.asarray(cols, dtype=np.int64)))
+        return f64(t)
+    a = t if rows is None else t[np.asarray(rows, dtype=np.int64)]
+    a = a if cols is None else a[:, np.asarray(cols, dtype=np.int64)]
+    return f64(a)
+
+
+def gemm(A, B) -> np.ndarray:
+    """Plain product C = A @ B in float64."""
+    return f64(A) @ f64(B)
+
+
+def forward(x, W0, z, gamma, W1, eps: float, rows=None, chunk: int = 1024) -> dict:
+    """Unfused forward of y = RMSNorm(x @ W0 + z, gamma) @ W1 for the given rows.
+
+    Returns float64 arrays h [R,D], r [R], n [R,D], y [R,N] for R = len(rows)
+    (all rows when ``rows`` is None).
+    """
+    W0d, W1d, gd = f64(W0), f64(W1), f64(gamma)
+    M = x.shape[0]
+    idx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    D = W0d.shape[1]
+    out = {"h": [], "r": [], "n": [], "y": []}
+    for c0 in range(0, len(idx), chunk):
+        sel = idx[c0:c0 + chunk]
+        xs, zs = _take(x, sel), _take(z, sel)
+        h = xs @ W0d + zs                       # GEMM, then residual add
+        ms = (h * h).sum(axis=1) / D            # mean of squares over D columns
+        r = 1.0 / np.sqrt(ms + eps)             # row-wise inverse RMS
+        n = (r[:, None] * h) * gd[None, :]      # RMSNorm output
+        y = n @ W1d                             # second GEMM
+        for k, v in (("h", h), ("r", r), ("n", n), ("y", y)):
+            out[k].append(v)
+    return {k: np.concatenate(v, axis=0) for k, v in out.items()}
+
+
+def row_statistic(dY, y, rows=None) -> np.ndarray:
+    """s_i = sum over columns of dY_in * y_in for the given rows."""
+    return (_take(dY, rows) * _take(y, rows)).sum(axis=1)
+
+
+def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=None) -> dict:
+    """Backward of the chain for the saved set (h, g, y, r).
+
+    * ``rows``: rows i for which s_i, G_i and da_i are returned (all when None).
+    * ``dgamma_cols``: columns j of dgamma (sums over *all* M rows; all when None).
+    * ``dw1_cols``: columns n of dW1 (all D rows of each; all when None).
+    """
+    W1d, gd, rd = f64(W1), f64(gamma), f64(r)
+    M, N = dY.shape
+    D = W1d.shape[0]
+    ridx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = {}
+
+    # rows: s, G, da
+    dYr, yr, hr = _take(dY, ridx), _take(y, ridx), _take(h, ridx)
+    s = (dYr * yr).sum(axis=1)
+    G = dYr @ W1d.T
+    rr = rd[ridx]
+    da = (rr[:, None] * gd[None, :]) * G - ((s * rr * rr) / D)[:, None] * hr
+    out.update(s=s, G=G, da=da)
+    del dYr, yr
+
+    # dgamma columns: G[:, cols] for every row
+    jc = np.arange(D) if dgamma_cols is None else np.asarray(dgamma_cols, dtype=np.int64)
+    dgam = np.zeros(len(jc))
+    for c0 in range(0, M, 2048):
+        blk = np.arange(c0, min(M, c0 + 2048))
+        Gc = _take(dY, blk) @ W1d[jc, :].T
+        dgam += (Gc * rd[blk, None] * _take(h, blk, jc)).sum(axis=0)
+    out["dgamma"] = dgam
+
+    # dW1 columns: (r . g)^T @ dY[:, cols]
+    nc = np.arange(N) if dw1_cols is None else np.asarray(dw1_cols, dtype=np.int64)
+    dW1 = np.zeros((D, len(nc)))
+    for c0 in range(0, M, 2048):
+        blk = np.arange(c0, min(M, c0 + 2048))
+        gr = _take(g, blk) * rd[blk, None]
+        dW1 += gr.T @ _take(dY, blk, nc)
+    out["dW1"] = dW1
+    return out

@@ -1,0 +1,331 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test fixes the oracle against mathematics the pages determine: exact
+rational / 50-digit arithmetic on tiny inputs, a different library's RMSNorm and
+autograd, finite differences, closed forms, invariants of the backward, the
+reparameterisation identity (hotdry blog, section "GEMM-Residual-RMSNorm-GEMM
+重参数化": r is a row scalar and commutes with the second GEMM), and
+hand-worked examples under tests/golden/.
+"""
+import json
+import os
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+from oracle import coda_oracle as orc
+from transformer_gemm_epilogue_res_amd import inputs
+
+mpmath.mp.dps = 50
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _rng_int(shape, lo, hi, seed):
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float64)
+
+
+def _relerr(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- brute force
+
+def _exact_forward(x, W0, z, gamma, W1, eps):
+    """Forward with Fractions for the rational steps and 50-digit mpmath for the root."""
+    M, K0 = x.shape
+    D, N = W1.shape
+    F = lambda v: Fraction(v).limit_denominator(10**12)  # noqa: E731  inputs are small dyadics
+    h = [[sum(F(x[i, k]) * F(W0[k, j]) for k in range(K0)) + F(z[i, j]) for j in range(D)] for i in range(M)]
+    out_r, out_y = [], []
+    for i in range(M):
+        ms = sum(v * v for v in h[i]) / D
+        r = 1 / mpmath.sqrt(mpmath.mpf(ms.numerator) / ms.denominator + mpmath.mpf(eps))
+        n = [r * mpmath.mpf(F(h[i][j]).numerator) / F(h[i][j]).denominator * mpmath.mpf(gamma[j]) for j in range(D)]
+        y = [mpmath.fsum(n[j] * mpmath.mpf(W1[j, c]) for j in range(D)) for c in range(N)]
+        out_r.append(r)
+        out_y.append(y)
+    hf = np.array([[float(v) for v in row] for row in h])
+    return hf, np.array([float(v) for v in out_r]), np.array([[float(v) for v in row] for row in out_y])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_forward_brute_force_exact(seed):
+    M, K0, D, N = 2, 4, 4, 3
+    x = _rng_int((M, K0), -3, 3, seed)
+    W0 = _rng_int((K0, D), -2, 2, seed + 10) / 2
+    z = _rng_int((M, D), -3, 3, seed + 20)
+    gamma = 1 + _rng_int((D,), -2, 2, seed + 30) / 8
+    W1 = _rng_int((D, N), -3, 3, seed + 40) / 4
+    eps = 1e-5
+    h, r, y = _exact_forward(x, W0, z, gamma, W1, eps)
+    o = orc.forward(x, W0, z, gamma, W1, eps)
+    assert _relerr(o["h"], h) == 0.0          # small dyadic rationals: exact in fp64
+    assert _relerr(o["r"], r) < 1e-15
+    assert _relerr(o["y"], y) < 1e-14
+
+
+def _exact_backward_by_derivative(x, W0, z, gamma, W1, dY, eps):
+    """dL/dh, dL/dgamma, dL/dW1 for L = <dY, y> by 50-digit numerical differentiation.
+
+    This uses no backward formula: L is re-evaluated from the forward definition
+    and differentiated by mpmath.diff (Richardson-extrapolated differences).
+    """
+    M, D = z.shape
+    N = W1.shape[1]
+    h0 = [[mpmath.mpf(float(v)) for v in row] for row in (x @ W0 + z)]
+    g0 = [mpmath.mpf(float(v)) for v in gamma]
+    w0 = [[mpmath.mpf(float(v)) for v in row] for row in W1]
+    dy = [[mpmath.mpf(float(v)) for v in row] for row in dY]
+
+    def L(h, g, w):
+        tot = mpmath.mpf(0)
+        for i in range(M):
+            ms = mpmath.fsum(v * v for v in h[i]) / D
+            r = 1 / mpmath.sqrt(ms + eps)
+            n = [r * h[i][j] * g[j] for j in range(D)]
+            for c in range(N):
+                tot += dy[i][c] * mpmath.fsum(n[j] * w[j][c] for j in range(D))
+        return tot
+
+    def dh(i, j):
+        def f(t):
+            h = [row[:] for row in h0]
+            h[i][j] = t
+            return L(h, g0, w0)
+        return mpmath.diff(f, h0[i][j])
+
+    def dg(j):
+        def f(t):
+            g = g0[:]
+            g[j] = t
+            return L(h0, g, w0)
+        return mpmath.diff(f, g0[j])
+
+    def dw(j, c):
+        def f(t):
+            w = [row[:] for row in w0]
+            w[j][c] = t
+            return L(h0, g0, w)
+        return mpmath.diff(f, w0[j][c])
+
+    da = np.array([[float(dh(i, j)) for j in range(D)] for i in range(M)])
+    dgam = np.array([float(dg(j)) for j in range(D)])
+    dW1 = np.array([[float(dw(j, c)) for c in range(N)] for j in range(D)])
+    return da, dgam, dW1
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_brute_force_derivative(seed):
+    M, K0, D, N = 2, 3, 4, 3
+    x = _rng_int((M, K0), -3, 3, seed)
+    W0 = _rng_int((K0, D), -2, 2, seed + 10) / 2
+    z = _rng_int((M, D), -3, 3, seed + 20)
+    gamma = 1 + _rng_int((D,), -2, 2, seed + 30) / 8
+    W1 = _rng_int((D, N), -3, 3, seed + 40) / 4
+    dY = _rng_int((M, N), -3, 3, seed + 50)
+    eps = 1e-5
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    b = orc.backward(dY, f["y"], f["h"], f["h"] * gamma[None, :], f["r"], gamma, W1)
+    da, dgam, dW1 = _exact_backward_by_derivative(x, W0, z, gamma, W1, dY, eps)
+    assert _relerr(b["da"], da) < 1e-12
+    assert _relerr(b["dgamma"], dgam) < 1e-12
+    assert _relerr(b["dW1"], dW1) < 1e-12
+    # G and s from their definitions in exact arithmetic
+    assert _relerr(b["G"], dY @ W1.T) == 0.0
+
+
+# --------------------------------------------------------- library special case
+
+def _rand_problem(M, K0, D, N, seed, eps=1e-5):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K0, generator=g, dtype=torch.float64)
+    W0 = torch.randn(K0, D, generator=g, dtype=torch.float64) / K0 ** 0.5
+    z = torch.randn(M, D, generator=g, dtype=torch.float64)
+    gamma = 1 + 0.1 * torch.randn(D, generator=g, dtype=torch.float64)
+    W1 = torch.randn(D, N, generator=g, dtype=torch.float64) / D ** 0.5
+    dY = torch.randn(M, N, generator=g, dtype=torch.float64)
+    return x, W0, z, gamma, W1, dY, eps
+
+
+def test_forward_matches_torch_rms_norm():
+    x, W0, z, gamma, W1, _, eps = _rand_problem(16, 32, 48, 40, 0)
+    h = x @ W0 + z
+    y_ref = torch.nn.functional.rms_norm(h, (h.shape[1],), gamma, eps) @ W1
+    o = orc.forward(x, W0, z, gamma, W1, eps)
+    assert _relerr(o["y"], y_ref.numpy()) < 1e-12
+    assert _relerr(o["h"], h.numpy()) < 1e-14
+
+
+def test_backward_matches_torch_autograd():
+    x, W0, z, gamma, W1, dY, eps = _rand_problem(12, 24, 32, 40, 1)
+    h = (x @ W0 + z).requires_grad_(True)
+    gam = gamma.clone().requires_grad_(True)
+    W = W1.clone().requires_grad_(True)
+    y = torch.nn.functional.rms_norm(h, (h.shape[1],), gam, eps) @ W
+    (y * dY).sum().backward()
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    b = orc.backward(dY, f["y"], f["h"], f["h"] * gamma.numpy()[None, :], f["r"], gamma, W1)
+    assert _relerr(b["da"], h.grad.numpy()) < 1e-10
+    assert _relerr(b["dgamma"], gam.grad.numpy()) < 1e-10
+    assert _relerr(b["dW1"], W.grad.numpy()) < 1e-10
+
+
+# ------------------------------------------------------------ finite differences
+
+def test_backward_finite_differences():
+    M, K0, D, N = 6, 8, 16, 12
+    x, W0, z, gamma, W1, dY, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                     for t in _rand_problem(M, K0, D, N, 2))
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    b = orc.backward(dY, f["y"], f["h"], f["h"] * gamma[None, :], f["r"], gamma, W1)
+    h = f["h"]
+
+    def L(hh, gg, ww):
+        ms = (hh * hh).mean(axis=1)
+        n = hh / np.sqrt(ms + eps)[:, None] * gg[None, :]
+        return float(((n @ ww) * dY).sum())
+
+    step = 1e-6
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        i, j = rng.integers(M), rng.integers(D)
+        hp, hm = h.copy(), h.copy()
+        hp[i, j] += step
+        hm[i, j] -= step
+        fd = (L(hp, gamma, W1) - L(hm, gamma, W1)) / (2 * step)
+        assert abs(fd - b["da"][i, j]) <= 1e-7 * max(1.0, abs(fd))
+        j = rng.integers(D)
+        gp, gm = gamma.copy(), gamma.copy()
+        gp[j] += step
+        gm[j] -= step
+        fd = (L(h, gp, W1) - L(h, gm, W1)) / (2 * step)
+        assert abs(fd - b["dgamma"][j]) <= 1e-7 * max(1.0, abs(fd))
+        j, c = rng.integers(D), rng.integers(N)
+        wp, wm = W1.copy(), W1.copy()
+        wp[j, c] += step
+        wm[j, c] -= step
+        fd = (L(h, gamma, wp) - L(h, gamma, wm)) / (2 * step)
+        assert abs(fd - b["dW1"][j, c]) <= 1e-7 * max(1.0, abs(fd))
+
+
+# ----------------------------------------------------------------- identities
+
+def test_reparameterised_order_equals_definition():
+    x, W0, z, gamma, W1, _, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                   for t in _rand_problem(32, 64, 96, 80, 3))
+    o = orc.forward(x, W0, z, gamma, W1, eps)
+    h = x @ W0 + z
+    r = 1 / np.sqrt((h * h).mean(axis=1) + eps)
+    y_reparam = r[:, None] * ((h * gamma[None, :]) @ W1)
+    assert _relerr(o["y"], y_reparam) < 1e-13
+
+
+def test_constant_and_zero_rows():
+    M, K0, D, N = 4, 8, 16, 8
+    x, W0, z, gamma, W1, _, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                   for t in _rand_problem(M, K0, D, N, 4))
+    x[1] = 0.0
+    z[1] = 1.5            # constant row: h = c
+    x[2] = 0.0
+    z[2] = 0.0            # zero row
+    o = orc.forward(x, W0, z, gamma, W1, eps)
+    c = 1.5
+    assert abs(o["r"][1] - 1 / np.sqrt(c * c + eps)) < 1e-15
+    assert _relerr(o["y"][1], o["r"][1] * c * (gamma @ W1)) < 1e-13
+    assert abs(o["r"][2] - eps ** -0.5) < 1e-10
+    assert np.all(o["y"][2] == 0.0)
+
+
+def test_unit_rms_and_scale_invariance_without_eps():
+    x, W0, z, _, W1, _, _ = (t.numpy() if isinstance(t, torch.Tensor) else t
+                             for t in _rand_problem(8, 16, 32, 24, 5))
+    ones = np.ones(32)
+    o = orc.forward(x, W0, z, ones, W1, 0.0)
+    assert np.max(np.abs((o["n"] ** 2).mean(axis=1) - 1)) < 1e-13
+    o2 = orc.forward(3.0 * x, W0, 3.0 * z, ones, W1, 0.0)
+    assert _relerr(o2["y"], o["y"]) < 1e-13
+
+
+def test_row_isolation_nan():
+    x, W0, z, gamma, W1, _, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                   for t in _rand_problem(6, 8, 16, 8, 6))
+    x = x.copy()
+    x[3, 2] = np.nan
+    o = orc.forward(x, W0, z, gamma, W1, eps)
+    bad = ~np.isfinite(o["y"]).all(axis=1)
+    assert bad.tolist() == [False, False, False, True, False, False]
+    assert np.isnan(o["r"][3]) and np.isfinite(np.delete(o["r"], 3)).all()
+
+
+def test_backward_invariants_and_zero_grad():
+    x, W0, z, gamma, W1, dY, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                    for t in _rand_problem(10, 16, 24, 20, 7, eps=1e-3))
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    g = f["h"] * gamma[None, :]
+    b = orc.backward(dY, f["y"], f["h"], g, f["r"], gamma, W1)
+    s = b["s"]
+    lhs = (b["da"] * f["h"]).sum(axis=1)
+    assert np.max(np.abs(lhs - s * eps * f["r"] ** 2)) < 1e-12 * np.max(np.abs(s))
+    assert abs((gamma * b["dgamma"]).sum() - s.sum()) < 1e-11 * np.abs(s).sum()
+    assert abs((b["dW1"] * W1).sum() - s.sum()) < 1e-11 * np.abs(s).sum()
+    z0 = orc.backward(np.zeros_like(dY), f["y"], f["h"], g, f["r"], gamma, W1)
+    for k in ("s", "da", "dgamma", "dW1"):
+        assert np.all(z0[k] == 0.0)
+
+
+def test_subsets_match_full_computation():
+    x, W0, z, gamma, W1, dY, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                    for t in _rand_problem(40, 16, 24, 36, 8))
+    full = orc.forward(x, W0, z, gamma, W1, eps)
+    rows = [0, 5, 17, 39]
+    part = orc.forward(x, W0, z, gamma, W1, eps, rows=rows, chunk=3)
+    for k in ("h", "r", "n", "y"):   # BLAS blocking may differ with the batch: compare to fp64 rounding
+        assert _relerr(part[k], full[k][rows]) < 1e-14
+    g = full["h"] * gamma[None, :]
+    bf = orc.backward(dY, full["y"], full["h"], g, full["r"], gamma, W1)
+    bp = orc.backward(dY, full["y"], full["h"], g, full["r"], gamma, W1,
+                      rows=rows, dgamma_cols=[1, 7, 23], dw1_cols=[0, 35])
+    assert np.allclose(bp["da"], bf["da"][rows], rtol=0, atol=1e-13)
+    assert np.allclose(bp["dgamma"], bf["dgamma"][[1, 7, 23]], rtol=0, atol=1e-12)
+    assert np.allclose(bp["dW1"], bf["dW1"][:, [0, 35]], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- hand-worked
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_golden_hand_worked(case):
+    a = {k: np.array(v, dtype=np.float64) for k, v in case.items() if isinstance(v, list)}
+    o = orc.forward(a["x"], a["W0"], a["z"], a["gamma"], a["W1"], case["eps"])
+    assert np.allclose(o["h"], a["h"], rtol=0, atol=1e-15)
+    assert np.allclose(o["r"], a["r"], rtol=1e-15, atol=0)
+    assert np.allclose(o["y"], a["y"], rtol=1e-15, atol=1e-15)
+    if "dY" in a:
+        g = o["h"] * a["gamma"][None, :]
+        b = orc.backward(a["dY"], o["y"], o["h"], g, o["r"], a["gamma"], a["W1"])
+        for k in ("s", "da", "dgamma", "dW1"):
+            assert np.allclose(b[k], a[k], rtol=1e-14, atol=1e-14), k
+
+
+# ------------------------------------------------------------------- inputs
+
+def test_inputs_are_seeded_and_distributed_as_stated():
+    a = inputs.forward_inputs(64, 256, 256, 512, seed=0)
+    b = inputs.forward_inputs(64, 256, 256, 512, seed=0)
+    c = inputs.forward_inputs(64, 256, 256, 512, seed=1)
+    for k in a:
+        assert a[k].dtype == torch.bfloat16
+        assert torch.equal(a[k], b[k])
+        assert not torch.equal(a[k], c[k])
+    assert a["x"].shape == (64, 256) and a["W0"].shape == (256, 256)
+    assert a["W1"].shape == (256, 512) and a["gamma"].shape == (256,)
+    assert abs(a["x"].float().std().item() - 1) < 0.05
+    assert abs(a["W1"].float().std().item() * 16 - 1) < 0.05          # 1/sqrt(D), D = 256
+    assert abs(a["gamma"].float().mean().item() - 1) < 0.02
+    assert abs(a["gamma"].float().std().item() - 0.1) < 0.02
+    rows = inputs.sample(8192, 256, 0, "rows")
+    assert rows.tolist() == sorted(set(rows.tolist())) and len(rows) == 256
+    assert inputs.sample(64, 256, 0, "rows").tolist() == list(range(64))

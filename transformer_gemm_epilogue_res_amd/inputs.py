@@ -1,0 +1,76 @@
+"""Seeded synthetic inputs for the GEMM -> residual -> RMSNorm -> GEMM chain.
+
+This module is shared by the oracle tests and the HIP-path tests/bench. It draws
+random tensors and nothing else: it holds none of the chain's arithmetic.
+
+Recipe (the pages use Llama-3-style layer shapes, no dataset; CODA: Rewriting
+Transformer Blocks as GEMM-Epilogue Programs, hotdry blog, "performance
+expectations" paragraph, and the kucoin article, "experimental results"):
+
+* every tensor has its own CPU ``torch.Generator`` seeded ``seed*100 + id``
+  with ids x=1, W0=2, z=3, gamma=4, W1=5, dY=6 (row sample 7, dgamma column
+  sample 8, dW1 column sample 9);
+* each draw is fp32 ``randn`` scaled and then cast to bfloat16 (round to
+  nearest even): x, z, dY ~ N(0, 1); W0 ~ N(0, 1/K0); W1 ~ N(0, 1/D)
+  (fan-in = rows of the ``[in, out]`` weight); gamma = 1 + 0.1 N(0, 1);
+* eps = 1e-5.
+
+W1's columns are read as interleaved gate/up pairs (column 2f = gate f,
+column 2f+1 = up f); for independent draws that is only a relabelling.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+EPS = 1e-5
+
+IDS = {"x": 1, "W0": 2, "z": 3, "gamma": 4, "W1": 5, "dY": 6,
+       "rows": 7, "dgamma_cols": 8, "dw1_cols": 9}
+
+# name -> (M tokens, K0, D, N = 2 * ffn)
+CONFIGS = {
+    "tiny": dict(M=64, K0=256, D=256, N=512),
+    "llama3_1b": dict(M=8192, K0=2048, D=2048, N=16384),
+    "llama3_8b": dict(M=8192, K0=4096, D=4096, N=28672),
+    "llama3_70b": dict(M=8192, K0=8192, D=8192, N=57344),
+}
+
+
+def generator(seed: int, name: str) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 100 + IDS[name])
+    return g
+
+
+def _randn_bf16(shape, seed, name, scale=1.0, shift=0.0):
+    t = torch.randn(*shape, generator=generator(seed, name), dtype=torch.float32)
+    if scale != 1.0:
+        t.mul_(scale)
+    if shift != 0.0:
+        t.add_(shift)
+    return t.to(torch.bfloat16)
+
+
+def forward_inputs(M: int, K0: int, D: int, N: int, seed: int = 0) -> dict:
+    """x [M,K0], W0 [K0,D], z [M,D], gamma [D], W1 [D,N]; bf16, CPU, row-major."""
+    return {
+        "x": _randn_bf16((M, K0), seed, "x"),
+        "W0": _randn_bf16((K0, D), seed, "W0", scale=1.0 / math.sqrt(K0)),
+        "z": _randn_bf16((M, D), seed, "z"),
+        "gamma": _randn_bf16((D,), seed, "gamma", scale=0.1, shift=1.0),
+        "W1": _randn_bf16((D, N), seed, "W1", scale=1.0 / math.sqrt(D)),
+    }
+
+
+def output_grad(M: int, N: int, seed: int = 0) -> torch.Tensor:
+    """dY [M,N] bf16 ~ N(0,1)."""
+    return _randn_bf16((M, N), seed, "dY")
+
+
+def sample(n: int, count: int, seed: int, name: str) -> torch.Tensor:
+    """Sorted seeded sample of ``count`` distinct indices in [0, n) (all of them if count >= n)."""
+    if count >= n:
+        return torch.arange(n)
+    return torch.randperm(n, generator=generator(seed, name))[:count].sort().values
