@@ -1,0 +1,191 @@
+/*
+ * coda.h - C ABI of the fused GEMM -> residual -> RMSNorm -> GEMM chain for
+ * AMD MI355X (gfx950), forward and backward.
+ *
+ * The operation (CODA: Rewriting Transformer Blocks as GEMM-Epilogue Programs,
+ * hotdry blog page, section "GEMM-Residual-RMSNorm-GEMM 重参数化"):
+ *
+ *     y = RMSNorm(x @ W0 + z, gamma) @ W1
+ *
+ * evaluated in the reparameterised order of the same section, where the row
+ * scale r commutes with the second GEMM:
+ *
+ *     h = x @ W0 + z,   g = h * gamma,   r_i = 1 / sqrt(mean_j h_ij^2 + eps),
+ *     y = r (row-broadcast) * (g @ W1).
+ *
+ * The first GEMM's epilogue adds the residual, stores h and g and emits tile
+ * partial sums of squares; a light reduction turns them into r; the second
+ * GEMM's epilogue applies r (same section, steps 1-3).
+ *
+ * Backward of L = <dY, y> (same page, section "反向传播的 GEMM-Epilogue 结构":
+ * the backward keeps the GEMM-epilogue form and the row statistic s is taken at
+ * the GEMM boundary as s = sum_cols(dY * y)):
+ *
+ *     s_i   = sum_n dY_in y_in
+ *     G     = dY @ W1^T               (epilogue: da and dgamma column partials)
+ *     da_ij = r_i gamma_j G_ij - s_i r_i^2 h_ij / D
+ *     dgamma_j = sum_i G_ij r_i h_ij
+ *     dW1   = (r * g)^T @ dY          (r * g rounded once to bf16 before the GEMM)
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense and row-major. bf16 means IEEE bfloat16 (stored as
+ *     uint16); f32 means IEEE binary32. W0 is [K0, D] and W1 is [D, N] ([in, out]).
+ *   - Pointers are device pointers (HIP device memory), 16-byte aligned. The
+ *     caller owns every buffer, including the workspace; the library never
+ *     allocates, frees or synchronises. Work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the default stream) and the call returns at once.
+ *     Calls on one stream with distinct outputs/workspaces are independent; the
+ *     library keeps no global state.
+ *   - Shapes: 1 <= M <= 2^24 (any value; the last row tile is masked); K0, D
+ *     and N are multiples of 256 in [256, 2^20]. Anything else returns
+ *     CODA_ERR_SHAPE.
+ *   - eps must be finite and > 0.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is enqueued and the status is returned. A failed launch
+ *     returns CODA_ERR_HIP. Device faults surface at the caller's next sync.
+ *   - NaN/Inf inputs are not trapped; they propagate row-locally (a non-finite
+ *     value in row i of x/z/dY/h/y affects row i's outputs and, through the
+ *     column sums, dgamma/dW1).
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CODA_OK = 0,
+  CODA_ERR_NULL = 1,      /* a required pointer is NULL                      */
+  CODA_ERR_SHAPE = 2,     /* unsupported or inconsistent sizes               */
+  CODA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                */
+  CODA_ERR_WORKSPACE = 4, /* workspace NULL or smaller than required          */
+  CODA_ERR_ARG = 5,       /* bad scalar argument (eps, dtype, op, layout)     */
+  CODA_ERR_HIP = 6        /* a HIP launch failed                              */
+} coda_status_t;
+
+typedef enum { CODA_BF16 = 0, CODA_F32 = 1 } coda_dtype_t;
+
+/* Operations, for coda_workspace_bytes. */
+typedef enum {
+  CODA_OP_FWD = 0,          /* coda_fwd                      */
+  CODA_OP_BWD = 1,          /* coda_bwd                      */
+  CODA_OP_UNFUSED_FWD = 2,  /* coda_unfused_ref(CODA_OP_FWD)  */
+  CODA_OP_UNFUSED_BWD = 3   /* coda_unfused_ref(CODA_OP_BWD)  */
+} coda_op_t;
+
+/* Forward arguments.
+ *   in : x [M,K0] bf16, W0 [K0,D] bf16, z [M,D] bf16 (residual), gamma [D] bf16,
+ *        W1 [D,N] bf16 (columns 2f / 2f+1 are the gate / up pair of feature f;
+ *        the chain's arithmetic does not depend on this labelling).
+ *   out: h [M,D] bf16 (= x@W0 + z, rounded once from fp32),
+ *        g [M,D] bf16 (= h*gamma rounded once from the fp32 h),
+ *        r [M] f32 (row inverse RMS), y [M,N] in y_dtype.
+ * h, g, r and y are what the backward needs; the fused forward writes all four. */
+typedef struct {
+  int64_t M, K0, D, N;
+  float eps;
+  const void* x;
+  const void* W0;
+  const void* z;
+  const void* gamma;
+  const void* W1;
+  void* h;
+  void* g;
+  float* r;
+  void* y;
+  coda_dtype_t y_dtype;
+} coda_fwd_args_t;
+
+/* Backward arguments.
+ *   in : dY [M,N] bf16; the forward's saved y [M,N] bf16, h [M,D] bf16,
+ *        g [M,D] bf16, r [M] f32; gamma [D] bf16; W1 [D,N] bf16.
+ *   out: da [M,D] in da_dtype (gradient w.r.t. the RMSNorm input h),
+ *        dgamma [D] f32, dW1 [D,N] in dW1_dtype, s [M] f32 (the row statistic). */
+typedef struct {
+  int64_t M, D, N;
+  const void* dY;
+  const void* y;
+  const void* h;
+  const void* g;
+  const float* r;
+  const void* gamma;
+  const void* W1;
+  void* da;
+  float* dgamma;
+  void* dW1;
+  float* s;
+  coda_dtype_t da_dtype;
+  coda_dtype_t dW1_dtype;
+} coda_bwd_args_t;
+
+/* Operand layouts for coda_gemm. */
+typedef enum {
+  CODA_ROW = 0, /* A: element (m,k) at A[m*lda + k];  B: element (k,n) at B[k*ldb + n] */
+  CODA_COL = 1  /* A: element (m,k) at A[k*lda + m];  B: element (k,n) at B[n*ldb + k] */
+} coda_layout_t;
+
+/* Plain GEMM C[M,N] = A[M,K] @ B[K,N] with bf16 operands and fp32 accumulation,
+ * output in c_dtype with leading dimension ldc. This is the mainloop every
+ * fused kernel shares, with a store-only epilogue; the unfused baseline is
+ * built from it. M >= 1, N and K multiples of 256, lda/ldb/ldc >= the
+ * contiguous extent and multiples of 8. */
+typedef struct {
+  int64_t M, N, K;
+  const void* A;
+  int64_t lda;
+  coda_layout_t a_layout;
+  const void* B;
+  int64_t ldb;
+  coda_layout_t b_layout;
+  void* C;
+  int64_t ldc;
+  coda_dtype_t c_dtype;
+} coda_gemm_args_t;
+
+/* Bytes of device workspace `op` needs for these sizes (0 when none). The
+ * workspace of the fused forward holds the partial sums of squares; the
+ * fused backward holds bf16(r*g) [M,D] and the dgamma column partials; the
+ * unfused baseline also holds its materialised intermediates. */
+size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N);
+
+/* Host-only argument checks (no HIP call). Return CODA_OK or the first error. */
+coda_status_t coda_validate_fwd(const coda_fwd_args_t* a, const void* ws, size_t ws_bytes);
+coda_status_t coda_validate_bwd(const coda_bwd_args_t* a, const void* ws, size_t ws_bytes);
+coda_status_t coda_validate_gemm(const coda_gemm_args_t* a);
+/* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD or CODA_OP_BWD). */
+coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
+
+/* Fused forward: GEMM0 + epilogue (residual, h, g, sum-of-squares partials) ->
+ * row-statistic combine (r) -> GEMM1 + epilogue (row scale r). */
+coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Fused backward: row statistic s and bf16(r*g) -> G = dY@W1^T with the
+ * RMSNorm-backward epilogue (da, dgamma column partials) -> dgamma combine ->
+ * dW1 = bf16(r*g)^T @ dY. */
+coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Unfused baseline with the same mainloop and separate row kernels.
+ *   op = CODA_OP_FWD, args = coda_fwd_args_t*: t = x@W0 (bf16, workspace) ->
+ *     add+RMSNorm row kernel (h, r, n = bf16(r*h*gamma) into the workspace) ->
+ *     y = n@W1. Writes h, r and y; g is not written (this chain feeds n, not g,
+ *     to the second GEMM).
+ *   op = CODA_OP_BWD, args = coda_bwd_args_t*: same s / bf16(r*g) kernel ->
+ *     G = dY@W1^T stored as bf16 in the workspace -> RMSNorm-backward row kernel
+ *     (da, dgamma partials) -> dgamma combine -> same dW1 GEMM. */
+coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Plain GEMM (see coda_gemm_args_t); needs no workspace. */
+coda_status_t coda_gemm(const coda_gemm_args_t* a, void* stream);
+
+/* Static description of a status code. */
+const char* coda_status_string(coda_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H */

@@ -1,0 +1,174 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/coda.h declares, its structs match the C layout, workspace sizes
+follow the documented formulas, and every invalid argument is rejected before
+anything is launched."""
+import ctypes
+import math
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+from transformer_gemm_epilogue_res_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000  # fake, 16-byte aligned "device" addresses: validation never dereferences them
+
+
+def fake(i):
+    return ctypes.c_void_p(A + 0x1000 * i)
+
+
+def test_library_exports_every_declared_function():
+    names = L.declared_functions()
+    assert {"coda_fwd", "coda_bwd", "coda_unfused_ref", "coda_workspace_bytes", "coda_gemm"} <= set(names)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_c_header():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "coda.h"
+#define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
+int main(void) {
+  printf("fwd %zu bwd %zu gemm %zu\n", sizeof(coda_fwd_args_t), sizeof(coda_bwd_args_t), sizeof(coda_gemm_args_t));
+  O(coda_fwd_args_t, eps); O(coda_fwd_args_t, x); O(coda_fwd_args_t, y); O(coda_fwd_args_t, y_dtype);
+  O(coda_bwd_args_t, dY); O(coda_bwd_args_t, s); O(coda_bwd_args_t, da_dtype); O(coda_bwd_args_t, dW1_dtype);
+  O(coda_gemm_args_t, a_layout); O(coda_gemm_args_t, B); O(coda_gemm_args_t, b_layout); O(coda_gemm_args_t, c_dtype);
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    head = out[0].split()
+    assert int(head[1]) == ctypes.sizeof(L.FwdArgs)
+    assert int(head[3]) == ctypes.sizeof(L.BwdArgs)
+    assert int(head[5]) == ctypes.sizeof(L.GemmArgs)
+    types = {"coda_fwd_args_t": L.FwdArgs, "coda_bwd_args_t": L.BwdArgs, "coda_gemm_args_t": L.GemmArgs}
+    for line in out[1:]:
+        if not line:
+            continue
+        key, off = line.split()
+        t, f = key.split(".")
+        assert getattr(types[t], f).offset == int(off), key
+
+
+def test_workspace_sizes():
+    def a256(v):
+        return (v + 255) // 256 * 256
+    M, D, N = 300, 512, 768
+    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == a256(M * (D // 128) * 4)
+    assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4)
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD, M, D, N) == 2 * a256(M * D * 2)
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)
+    assert L.workspace_bytes(L.CODA_OP_FWD, 0, D, N) == 0
+    assert L.workspace_bytes(L.CODA_OP_FWD, M, 100, N) == 0
+
+
+def _fwd(**kw):
+    a = L.FwdArgs(64, 256, 256, 512, 1e-5, *[fake(i) for i in range(9)], L.CODA_BF16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _bwd(**kw):
+    a = L.BwdArgs(64, 256, 512, *[fake(i) for i in range(11)], L.CODA_BF16, L.CODA_F32)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+WS = fake(40)
+
+
+def vfwd(a, ws=WS, n=1 << 30):
+    return L.lib().coda_validate_fwd(ctypes.byref(a), ws, n)
+
+
+def vbwd(a, ws=WS, n=1 << 30):
+    return L.lib().coda_validate_bwd(ctypes.byref(a), ws, n)
+
+
+def test_validate_fwd_ok_and_errors():
+    assert vfwd(_fwd()) == L.CODA_OK
+    assert vfwd(_fwd(M=300)) == L.CODA_OK          # ragged M is supported
+    assert L.lib().coda_validate_fwd(None, WS, 1 << 30) == L.CODA_ERR_NULL
+    for f in ("x", "W0", "z", "gamma", "W1", "h", "g", "r", "y"):
+        assert vfwd(_fwd(**{f: None})) == L.CODA_ERR_NULL, f
+        assert vfwd(_fwd(**{f: ctypes.c_void_p(A + 8)})) == L.CODA_ERR_ALIGN, f
+    for k, v in (("M", 0), ("M", -5), ("M", (1 << 24) + 1), ("K0", 128), ("D", 300), ("N", 0), ("N", 1 << 21)):
+        assert vfwd(_fwd(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
+    for eps in (0.0, -1e-5, float("nan"), float("inf")):
+        assert vfwd(_fwd(eps=eps)) == L.CODA_ERR_ARG, eps
+    assert vfwd(_fwd(y_dtype=7)) == L.CODA_ERR_ARG
+    need = L.workspace_bytes(L.CODA_OP_FWD, 64, 256, 512)
+    assert vfwd(_fwd(), None, need) == L.CODA_ERR_WORKSPACE
+    assert vfwd(_fwd(), WS, need - 1) == L.CODA_ERR_WORKSPACE
+    assert vfwd(_fwd(), WS, need) == L.CODA_OK
+    assert vfwd(_fwd(), ctypes.c_void_p(A + 4), need) == L.CODA_ERR_ALIGN
+
+
+def test_validate_bwd_ok_and_errors():
+    assert vbwd(_bwd()) == L.CODA_OK
+    assert vbwd(_bwd(M=1)) == L.CODA_OK
+    for f in ("dY", "y", "h", "g", "r", "gamma", "W1", "da", "dgamma", "dW1", "s"):
+        assert vbwd(_bwd(**{f: None})) == L.CODA_ERR_NULL, f
+        assert vbwd(_bwd(**{f: ctypes.c_void_p(A + 2)})) == L.CODA_ERR_ALIGN, f
+    for k, v in (("M", 0), ("D", 64), ("N", 1000)):
+        assert vbwd(_bwd(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
+    assert vbwd(_bwd(da_dtype=2)) == L.CODA_ERR_ARG
+    assert vbwd(_bwd(dW1_dtype=-1)) == L.CODA_ERR_ARG
+    need = L.workspace_bytes(L.CODA_OP_BWD, 64, 256, 512)
+    assert vbwd(_bwd(), WS, need - 16) == L.CODA_ERR_WORKSPACE
+
+
+def test_validate_unfused_and_gemm():
+    lib = L.lib()
+    a = _fwd(g=None)  # the unfused forward does not write g
+    need = L.workspace_bytes(L.CODA_OP_UNFUSED_FWD, 64, 256, 512)
+    assert lib.coda_validate_unfused(L.CODA_OP_FWD, ctypes.byref(a), WS, need) == L.CODA_OK
+    assert lib.coda_validate_unfused(L.CODA_OP_FWD, ctypes.byref(a), WS, need - 1) == L.CODA_ERR_WORKSPACE
+    assert lib.coda_validate_unfused(9, ctypes.byref(a), WS, need) == L.CODA_ERR_ARG
+    b = _bwd()
+    need = L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, 64, 256, 512)
+    assert lib.coda_validate_unfused(L.CODA_OP_BWD, ctypes.byref(b), WS, need) == L.CODA_OK
+    g = L.GemmArgs(100, 256, 512, fake(1), 512, L.CODA_ROW, fake(2), 256, L.CODA_ROW, fake(3), 256, L.CODA_F32)
+    assert lib.coda_validate_gemm(ctypes.byref(g)) == L.CODA_OK
+    for k, v, want in (("K", 300, L.CODA_ERR_SHAPE), ("lda", 256, L.CODA_ERR_SHAPE), ("ldc", 260, L.CODA_ERR_ALIGN),
+                       ("a_layout", 5, L.CODA_ERR_ARG), ("c_dtype", 3, L.CODA_ERR_ARG), ("A", None, L.CODA_ERR_NULL)):
+        g2 = L.GemmArgs.from_buffer_copy(g)
+        setattr(g2, k, v)
+        assert lib.coda_validate_gemm(ctypes.byref(g2)) == want, k
+
+
+def test_entry_points_reject_without_launching():
+    """Invalid arguments come back as a status from every entry point (no HIP call is made)."""
+    lib = L.lib()
+    bad = _fwd(eps=0.0)
+    assert lib.coda_fwd(ctypes.byref(bad), WS, 1 << 30, None) == L.CODA_ERR_ARG
+    assert lib.coda_unfused_ref(L.CODA_OP_FWD, ctypes.byref(bad), WS, 1 << 30, None) == L.CODA_ERR_ARG
+    assert lib.coda_bwd(ctypes.byref(_bwd(N=100)), WS, 1 << 30, None) == L.CODA_ERR_SHAPE
+    assert lib.coda_unfused_ref(L.CODA_OP_BWD, None, WS, 1 << 30, None) == L.CODA_ERR_NULL
+    g = L.GemmArgs(100, 256, 512, None, 512, L.CODA_ROW, fake(2), 256, L.CODA_ROW, fake(3), 256, L.CODA_F32)
+    assert lib.coda_gemm(ctypes.byref(g), None) == L.CODA_ERR_NULL
+    assert L.status_string(L.CODA_ERR_WORKSPACE) == "workspace missing or too small"
+
+
+@pytest.mark.parametrize("name", ["coda_fwd", "coda_bwd"])
+def test_python_binding_checks_dtypes(name):
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        if name == "coda_fwd":
+            L.fwd(x, x, x, x[0], x, 1e-5)
+        else:
+            L.bwd(x, x, x, x, x[:, 0], x[0], x)

@@ -1,0 +1,294 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on one MI355X.
+
+Inputs are the seeded synthetic tensors of transformer_gemm_epilogue_res_amd.inputs;
+expected values come only from oracle/. Small shapes are compared in full
+(several 256-tiles, a ragged last row tile, a single row); the Llama-3 shapes run
+in the same launch configuration the benchmark times and are compared on a
+seeded 256-row sample (rows are independent) and, for the backward's column
+sums, on seeded 256-column samples.
+"""
+import numpy as np
+import pytest
+import torch
+
+import metrics as mt
+from oracle import coda_oracle as orc
+from transformer_gemm_epilogue_res_amd import _lib as L
+from transformer_gemm_epilogue_res_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+EPS = inputs.EPS
+
+
+def announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+
+
+def to_dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+# ------------------------------------------------------------------ mainloop
+
+@pytest.mark.parametrize("a_layout", [L.CODA_ROW, L.CODA_COL], ids=["A_row", "A_col"])
+@pytest.mark.parametrize("b_layout", [L.CODA_ROW, L.CODA_COL], ids=["B_row", "B_col"])
+@pytest.mark.parametrize("M", [320, 1])
+def test_gemm_mainloop_layouts(a_layout, b_layout, M):
+    N, K = 512, 768
+    announce(f"coda_gemm M={M} N={N} K={K} a_layout={a_layout} b_layout={b_layout}")
+    g = torch.Generator().manual_seed(11)
+    Am = torch.randn(M, K, generator=g).to(torch.bfloat16)     # logical A [M, K]
+    Bm = torch.randn(K, N, generator=g).to(torch.bfloat16)     # logical B [K, N]
+    if a_layout == L.CODA_ROW:
+        A = Am
+    else:  # [K, lda] with lda padded to a multiple of 8
+        A = torch.zeros(K, (M + 7) // 8 * 8, dtype=torch.bfloat16)
+        A[:, :M] = Am.t()
+    B = Bm if b_layout == L.CODA_ROW else Bm.t().contiguous()
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C32 = L.gemm(Ad, Bd, a_layout, b_layout, torch.float32, M=M, N=N, K=K)
+    C16 = L.gemm(Ad, Bd, a_layout, b_layout, torch.bfloat16, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    ref = orc.gemm(Am, Bm)
+    assert mt.normwise(C32, ref) <= 1e-4
+    assert torch.equal(mt.rne_bf16(C32).cpu().view(torch.int16), C16.cpu().view(torch.int16))
+
+
+# ------------------------------------------------------------------ forward
+
+FWD_SMALL = {
+    "tiny": dict(M=64, K0=256, D=256, N=512),
+    "ragged": dict(M=300, K0=256, D=512, N=768),
+    "one_row": dict(M=1, K0=256, D=256, N=256),
+    "k0_ne_d": dict(M=130, K0=768, D=256, N=512),
+}
+
+
+def run_fwd_both(dev_in, unfused=False):
+    o32 = L.fwd(dev_in["x"], dev_in["W0"], dev_in["z"], dev_in["gamma"], dev_in["W1"], EPS, torch.float32,
+                unfused=unfused)
+    o16 = L.fwd(dev_in["x"], dev_in["W0"], dev_in["z"], dev_in["gamma"], dev_in["W1"], EPS, torch.bfloat16,
+                unfused=unfused)
+    torch.cuda.synchronize()
+    return o32, o16
+
+
+def check_fwd(o32, o16, ref, gamma, rows=None, unfused=False):
+    def sel(t):
+        return t.cpu() if rows is None else t.index_select(0, torch.as_tensor(rows, device=t.device)).cpu()
+    y32, y16, r, h = sel(o32["y"]), sel(o16["y"]), sel(o32["r"]), sel(o32["h"])
+    e_y = mt.normwise(y32, ref["y"])
+    e_r = mt.max_rel(r, ref["r"])
+    print(f"  y(fp32) max|d|/rms={e_y:.3e}  r max rel={e_r:.3e}")
+    # the bf16 output is the round-to-nearest-even of the fp32 output of the same kernel
+    assert torch.equal(mt.rne_bf16(y32).view(torch.int16), y16.view(torch.int16))
+    assert torch.equal(sel(o16["r"]), r) and torch.equal(sel(o16["h"]), h)
+    if unfused:
+        assert e_y <= 3 * mt.Y_TOL
+        assert mt.bf16_within(y16, ref["y"], 3 * mt.Y_TOL) <= 1.0
+        # h = bf16(bf16(x@W0) + z): the rounding of t can exceed ulps of h where z cancels t
+        assert mt.bf16_within(h, ref["h"], 3 * mt.Y_TOL) <= 1.0
+    else:
+        assert e_y <= mt.Y_TOL
+        assert mt.bf16_within(y16, ref["y"]) <= 1.0
+        assert mt.bf16_one_ulp(h, ref["h"]) <= 1.0
+        g = sel(o32["g"])
+        assert torch.equal(sel(o16["g"]), g)
+        assert mt.bf16_one_ulp(g, ref["h"] * mt.f64(gamma)[None, :]) <= 1.0
+    assert e_r <= mt.R_TOL
+
+
+@pytest.mark.parametrize("name", list(FWD_SMALL))
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_fwd_small_full(name, unfused):
+    c = FWD_SMALL[name]
+    announce(f"{'coda_unfused_ref' if unfused else 'coda_fwd'} {name} {c} seed=0")
+    inp = inputs.forward_inputs(**c, seed=0)
+    o32, o16 = run_fwd_both(to_dev(inp), unfused)
+    ref = orc.forward(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
+    check_fwd(o32, o16, ref, inp["gamma"], unfused=unfused)
+
+
+def test_fwd_special_rows():
+    """Zero rows, constant rows and a NaN row (row isolation) through the fused kernels."""
+    c = FWD_SMALL["ragged"]
+    announce(f"coda_fwd special rows {c}")
+    inp = inputs.forward_inputs(**c, seed=3)
+    inp["x"][5] = 0
+    inp["z"][5] = 0                                       # h row = 0 -> r = eps^-1/2, y row = 0
+    inp["x"][7] = 0
+    inp["z"][7] = 1.5                                     # constant row
+    inp["x"][299, 3] = float("nan")                       # last (ragged) row
+    o32, _ = run_fwd_both(to_dev(inp))
+    y, r = o32["y"].cpu(), o32["r"].cpu()
+    assert abs(r[5].item() / EPS ** -0.5 - 1) < 1e-6 and torch.all(y[5] == 0)
+    assert abs(r[7].item() * (1.5 ** 2 + EPS) ** 0.5 - 1) < 1e-6
+    bad = ~torch.isfinite(y).all(dim=1)
+    assert bad.nonzero().flatten().tolist() == [299]
+    keep = [i for i in range(c["M"]) if i != 299]
+    ref = orc.forward(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, rows=keep)
+    assert mt.normwise(y[keep], ref["y"]) <= mt.Y_TOL
+
+
+FWD_LARGE = ["llama3_1b", "llama3_8b", "llama3_70b"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FWD_LARGE)
+def test_fwd_llama_shapes_sampled(name):
+    c = inputs.CONFIGS[name]
+    announce(f"coda_fwd {name} {c} seed=0, 256 sampled rows")
+    inp = inputs.forward_inputs(**c, seed=0)
+    rows = inputs.sample(c["M"], 256, 0, "rows").numpy()
+    o32, o16 = run_fwd_both(to_dev(inp))
+    ref = orc.forward(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, rows=rows)
+    check_fwd(o32, o16, ref, inp["gamma"], rows=rows)
+
+
+# ------------------------------------------------------------------ backward
+
+def saved_set(inp, eps=EPS):
+    """The forward's saved tensors, from the oracle forward rounded to their storage types."""
+    f = orc.forward(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], eps)
+    gam = orc.f64(inp["gamma"])
+    return {"h": torch.from_numpy(f["h"]).to(torch.bfloat16),
+            "g": torch.from_numpy(f["h"] * gam[None, :]).to(torch.bfloat16),
+            "y": torch.from_numpy(f["y"]).to(torch.bfloat16),
+            "r": torch.from_numpy(f["r"]).to(torch.float32)}
+
+
+def run_bwd_both(dev, unfused=False):
+    args = (dev["dY"], dev["y"], dev["h"], dev["g"], dev["r"], dev["gamma"], dev["W1"])
+    o32 = L.bwd(*args, da_dtype=torch.float32, dW1_dtype=torch.float32, unfused=unfused)
+    o16 = L.bwd(*args, da_dtype=torch.bfloat16, dW1_dtype=torch.bfloat16, unfused=unfused)
+    torch.cuda.synchronize()
+    return o32, o16
+
+
+def check_bwd(o32, o16, host, rows=None, jcols=None, ncols=None, unfused=False):
+    ref = orc.backward(host["dY"], host["y"], host["h"], host["g"], host["r"], host["gamma"], host["W1"],
+                       rows=rows, dgamma_cols=jcols, dw1_cols=ncols)
+
+    def rsel(t):
+        return t.cpu() if rows is None else t.index_select(0, torch.as_tensor(rows, device=t.device)).cpu()
+
+    def csel(t, cols):
+        return t.cpu() if cols is None else t.index_select(-1, torch.as_tensor(cols, device=t.device)).cpu()
+
+    s, da = rsel(o32["s"]), rsel(o32["da"])
+    dg, dW1 = csel(o32["dgamma"], jcols), csel(o32["dW1"], ncols)
+    e = {"s": mt.normwise(s, ref["s"]), "da": mt.normwise(da, ref["da"]),
+         "dgamma": mt.normwise(dg, ref["dgamma"]), "dW1": mt.normwise(dW1, ref["dW1"])}
+    print("  " + "  ".join(f"{k} max|d|/rms={v:.3e}" for k, v in e.items()))
+    assert torch.equal(mt.rne_bf16(da).view(torch.int16), rsel(o16["da"]).view(torch.int16))
+    assert torch.equal(mt.rne_bf16(dW1).view(torch.int16), csel(o16["dW1"], ncols).view(torch.int16))
+    assert torch.equal(rsel(o16["s"]), s) and torch.equal(csel(o16["dgamma"], jcols), dg)
+    allow = mt.operand_rounding_allowance(host["g"], host["r"], host["dY"], ncols)
+    e_w = mt.within_allowance(dW1, ref["dW1"], allow)
+    print(f"  dW1 |d| / (1e-2 rms + operand-rounding bound) max = {e_w:.3f}")
+    assert e["s"] <= mt.S_TOL
+    assert e_w <= 1.0
+    tol = 3 * mt.Y_TOL if unfused else mt.Y_TOL
+    assert e["da"] <= tol and e["dgamma"] <= tol
+
+
+BWD_SMALL = {
+    "tiny": dict(M=64, K0=256, D=256, N=512),
+    "ragged": dict(M=300, K0=256, D=512, N=768),
+    "one_row": dict(M=1, K0=256, D=256, N=256),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_SMALL))
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_bwd_small_full(name, unfused):
+    c = BWD_SMALL[name]
+    announce(f"{'coda_unfused_ref' if unfused else 'coda_bwd'} {name} {c} seed=0")
+    inp = inputs.forward_inputs(**c, seed=0)
+    host = dict(saved_set(inp), dY=inputs.output_grad(c["M"], c["N"], seed=0), gamma=inp["gamma"], W1=inp["W1"])
+    o32, o16 = run_bwd_both(to_dev(host), unfused)
+    check_bwd(o32, o16, host, unfused=unfused)
+
+
+@pytest.mark.slow
+def test_bwd_llama3_8b_sampled():
+    c = inputs.CONFIGS["llama3_8b"]
+    announce(f"coda_bwd llama3_8b {c} seed=0 (saved set from the oracle forward), sampled")
+    inp = inputs.forward_inputs(**c, seed=0)
+    host = dict(saved_set(inp), dY=inputs.output_grad(c["M"], c["N"], seed=0), gamma=inp["gamma"], W1=inp["W1"])
+    del inp
+    rows = inputs.sample(c["M"], 256, 0, "rows").numpy()
+    jcols = inputs.sample(c["D"], 256, 0, "dgamma_cols").numpy()
+    ncols = inputs.sample(c["N"], 256, 0, "dw1_cols").numpy()
+    o32, o16 = run_bwd_both(to_dev(host))
+    check_bwd(o32, o16, host, rows=rows, jcols=jcols, ncols=ncols)
+
+
+# ------------------------------------------------------ determinism, canaries
+
+def test_run_to_run_bitwise_determinism():
+    c = FWD_SMALL["ragged"]
+    announce(f"determinism coda_fwd/coda_bwd {c}")
+    inp = to_dev(inputs.forward_inputs(**c, seed=1))
+    a = L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
+    b = L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
+    torch.cuda.synchronize()
+    for k in ("h", "g", "r", "y"):
+        assert torch.equal(a[k], b[k]), k
+    dY = inputs.output_grad(c["M"], c["N"], seed=1).to(DEV)
+    args = (dY, a["y"], a["h"], a["g"], a["r"], inp["gamma"], inp["W1"])
+    p, q = L.bwd(*args), L.bwd(*args)
+    torch.cuda.synchronize()
+    for k in ("da", "dgamma", "dW1", "s"):
+        assert torch.equal(p[k], q[k]), k
+
+
+GUARD = 4096  # elements of guard band on each side of every output
+
+
+def guarded(shape, dtype):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * GUARD,), 0, dtype=dtype, device=DEV)
+    buf.view(torch.uint8).fill_(0x5A)
+    return buf, buf[GUARD:GUARD + n].view(*shape)
+
+
+def guards_intact(buf):
+    n = buf.numel()
+    g = torch.cat([buf[:GUARD], buf[n - GUARD:]]).view(torch.uint8)
+    return bool(torch.all(g == 0x5A).item())
+
+
+@pytest.mark.parametrize("M", [300, 1])
+def test_no_writes_outside_outputs(M):
+    c = dict(FWD_SMALL["ragged"], M=M)
+    announce(f"canaries coda_fwd/coda_bwd {c}")
+    inp = to_dev(inputs.forward_inputs(**c, seed=2))
+    D, N = c["D"], c["N"]
+    bufs, out = {}, {}
+    for k, shp, dt in (("h", (M, D), torch.bfloat16), ("g", (M, D), torch.bfloat16), ("r", (M,), torch.float32),
+                       ("y", (M, N), torch.bfloat16)):
+        bufs[k], out[k] = guarded(shp, dt)
+    wsb = L.workspace_bytes(L.CODA_OP_FWD, M, D, N)
+    bufs["ws"], ws = guarded((wsb,), torch.uint8)
+    L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, ws=ws, out=out)
+    dY = inputs.output_grad(M, N, seed=2).to(DEV)
+    bo = {}
+    for k, shp, dt in (("da", (M, D), torch.float32), ("dgamma", (D,), torch.float32),
+                       ("dW1", (D, N), torch.bfloat16), ("s", (M,), torch.float32)):
+        bufs["b" + k], bo[k] = guarded(shp, dt)
+    wsb = L.workspace_bytes(L.CODA_OP_BWD, M, D, N)
+    bufs["bws"], bws = guarded((wsb,), torch.uint8)
+    L.bwd(dY, out["y"], out["h"], out["g"], out["r"], inp["gamma"], inp["W1"], ws=bws, out=bo)
+    torch.cuda.synchronize()
+    for k, b in bufs.items():
+        assert guards_intact(b), k
+    assert torch.isfinite(out["y"].float()).all() and torch.isfinite(bo["da"]).all()
+
+
+def test_binding_reports_errors_without_launch():
+    inp = to_dev(inputs.forward_inputs(**FWD_SMALL["tiny"], seed=0))
+    with pytest.raises(L.CodaError) as e:
+        L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], 0.0)
+    assert e.value.status == L.CODA_ERR_ARG

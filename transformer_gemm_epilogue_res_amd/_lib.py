@@ -1,0 +1,211 @@
+"""ctypes binding of libcoda.so (include/coda.h). Argument marshalling only.
+
+torch tensors supply device memory and the current stream; every step of the
+chain runs in the library's HIP kernels. If the library is missing this module
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import POINTER, c_float, c_int, c_int64, c_size_t, c_void_p
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcoda.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "coda.h")
+
+CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA_ERR_ARG, CODA_ERR_HIP = range(7)
+CODA_BF16, CODA_F32 = 0, 1
+CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD = range(4)
+CODA_ROW, CODA_COL = 0, 1
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("K0", c_int64), ("D", c_int64), ("N", c_int64), ("eps", c_float),
+                ("x", c_void_p), ("W0", c_void_p), ("z", c_void_p), ("gamma", c_void_p), ("W1", c_void_p),
+                ("h", c_void_p), ("g", c_void_p), ("r", c_void_p), ("y", c_void_p), ("y_dtype", c_int)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("D", c_int64), ("N", c_int64),
+                ("dY", c_void_p), ("y", c_void_p), ("h", c_void_p), ("g", c_void_p), ("r", c_void_p),
+                ("gamma", c_void_p), ("W1", c_void_p),
+                ("da", c_void_p), ("dgamma", c_void_p), ("dW1", c_void_p), ("s", c_void_p),
+                ("da_dtype", c_int), ("dW1_dtype", c_int)]
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("N", c_int64), ("K", c_int64),
+                ("A", c_void_p), ("lda", c_int64), ("a_layout", c_int),
+                ("B", c_void_p), ("ldb", c_int64), ("b_layout", c_int),
+                ("C", c_void_p), ("ldc", c_int64), ("c_dtype", c_int)]
+
+
+class CodaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcoda.so (built by __graft_entry__.build() / build.py); raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.coda_workspace_bytes.restype = c_size_t
+        L.coda_workspace_bytes.argtypes = [c_int, c_int64, c_int64, c_int64]
+        for name, argt in (("coda_validate_fwd", [POINTER(FwdArgs), c_void_p, c_size_t]),
+                           ("coda_validate_bwd", [POINTER(BwdArgs), c_void_p, c_size_t]),
+                           ("coda_validate_gemm", [POINTER(GemmArgs)]),
+                           ("coda_validate_unfused", [c_int, c_void_p, c_void_p, c_size_t]),
+                           ("coda_fwd", [POINTER(FwdArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_bwd", [POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_unfused_ref", [c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+                           ("coda_gemm", [POINTER(GemmArgs), c_void_p])):
+            fn = getattr(L, name)
+            fn.restype = c_int
+            fn.argtypes = argt
+        L.coda_status_string.restype = ctypes.c_char_p
+        L.coda_status_string.argtypes = [c_int]
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/coda.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\**(coda_[a-z_]+)\s*\(", text, re.M)))
+
+
+def status_string(s: int) -> str:
+    return lib().coda_status_string(s).decode()
+
+
+def _check(status: int, where: str):
+    if status != CODA_OK:
+        raise CodaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return CODA_BF16
+    if dtype == torch.float32:
+        return CODA_F32
+    raise ValueError(f"unsupported output dtype {dtype}")
+
+
+def _want(t, name, dtype, shape=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(device) -> c_void_p:
+    return c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes(op: int, M: int, D: int, N: int) -> int:
+    return int(lib().coda_workspace_bytes(op, M, D, N))
+
+
+def workspace(op: int, M: int, D: int, N: int, device) -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(op, M, D, N), 16), dtype=torch.uint8, device=device)
+
+
+def _fwd_args(x, W0, z, gamma, W1, eps, h, g, r, y):
+    M, K0 = x.shape
+    D, N = W1.shape
+    _want(x, "x", torch.bfloat16, (M, K0))
+    _want(W0, "W0", torch.bfloat16, (K0, D))
+    _want(z, "z", torch.bfloat16, (M, D))
+    _want(gamma, "gamma", torch.bfloat16, (D,))
+    _want(W1, "W1", torch.bfloat16, (D, N))
+    return FwdArgs(M, K0, D, N, float(eps), _ptr(x), _ptr(W0), _ptr(z), _ptr(gamma), _ptr(W1),
+                   _ptr(h), _ptr(g), _ptr(r), _ptr(y), _dt(y.dtype))
+
+
+def fwd(x, W0, z, gamma, W1, eps, y_dtype=torch.bfloat16, ws=None, out=None, unfused=False):
+    """Forward of the chain. Returns dict(h, g, r, y) (g is None for the unfused baseline)."""
+    M, D, N = x.shape[0], W1.shape[0], W1.shape[1]
+    dev = x.device
+    if out is None:
+        out = {"h": torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+               "g": None if unfused else torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+               "r": torch.empty(M, dtype=torch.float32, device=dev),
+               "y": torch.empty(M, N, dtype=y_dtype, device=dev)}
+    a = _fwd_args(x, W0, z, gamma, W1, eps, out["h"], out["g"], out["r"], out["y"])
+    op = CODA_OP_UNFUSED_FWD if unfused else CODA_OP_FWD
+    if ws is None:
+        ws = workspace(op, M, D, N, dev)
+    if unfused:
+        st = lib().coda_unfused_ref(CODA_OP_FWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+    else:
+        st = lib().coda_fwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "coda_unfused_ref(fwd)" if unfused else "coda_fwd")
+    return out
+
+
+def _bwd_args(dY, y, h, g, r, gamma, W1, da, dgamma, dW1, s):
+    M, N = dY.shape
+    D = W1.shape[0]
+    _want(dY, "dY", torch.bfloat16, (M, N))
+    _want(y, "y", torch.bfloat16, (M, N))
+    _want(h, "h", torch.bfloat16, (M, D))
+    _want(g, "g", torch.bfloat16, (M, D))
+    _want(r, "r", torch.float32, (M,))
+    _want(gamma, "gamma", torch.bfloat16, (D,))
+    _want(W1, "W1", torch.bfloat16, (D, N))
+    return BwdArgs(M, D, N, _ptr(dY), _ptr(y), _ptr(h), _ptr(g), _ptr(r), _ptr(gamma), _ptr(W1),
+                   _ptr(da), _ptr(dgamma), _ptr(dW1), _ptr(s), _dt(da.dtype), _dt(dW1.dtype))
+
+
+def bwd(dY, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_dtype=torch.bfloat16, ws=None, out=None,
+        unfused=False):
+    """Backward of the chain. Returns dict(da, dgamma, dW1, s)."""
+    M, N = dY.shape
+    D = W1.shape[0]
+    dev = dY.device
+    if out is None:
+        out = {"da": torch.empty(M, D, dtype=da_dtype, device=dev),
+               "dgamma": torch.empty(D, dtype=torch.float32, device=dev),
+               "dW1": torch.empty(D, N, dtype=dW1_dtype, device=dev),
+               "s": torch.empty(M, dtype=torch.float32, device=dev)}
+    a = _bwd_args(dY, y, h, g, r, gamma, W1, out["da"], out["dgamma"], out["dW1"], out["s"])
+    op = CODA_OP_UNFUSED_BWD if unfused else CODA_OP_BWD
+    if ws is None:
+        ws = workspace(op, M, D, N, dev)
+    if unfused:
+        st = lib().coda_unfused_ref(CODA_OP_BWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+    else:
+        st = lib().coda_bwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "coda_unfused_ref(bwd)" if unfused else "coda_bwd")
+    return out
+
+
+def gemm(A, B, a_layout=CODA_ROW, b_layout=CODA_ROW, out_dtype=torch.float32, M=None, N=None, K=None):
+    """C[M,N] = A @ B with the shared mainloop. Layouts as in coda_layout_t."""
+    _want(A, "A", torch.bfloat16)
+    _want(B, "B", torch.bfloat16)
+    if M is None:
+        M, K = (A.shape[0], A.shape[1]) if a_layout == CODA_ROW else (A.shape[1], A.shape[0])
+    if N is None:
+        N = B.shape[1] if b_layout == CODA_ROW else B.shape[0]
+    C = torch.empty(M, N, dtype=out_dtype, device=A.device)
+    a = GemmArgs(M, N, K, _ptr(A), A.shape[1], a_layout, _ptr(B), B.shape[1], b_layout, _ptr(C), N, _dt(out_dtype))
+    _check(lib().coda_gemm(ctypes.byref(a), _stream(A.device)), "coda_gemm")
+    return C

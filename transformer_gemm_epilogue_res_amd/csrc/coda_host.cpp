@@ -1,0 +1,147 @@
+// Host-only part of the C ABI: workspace sizes, argument validation and status
+// strings. Nothing here calls HIP, so the checks run (and are tested) without a GPU.
+#include <math.h>
+
+#include "../../include/coda.h"
+#include "coda_internal.h"
+
+using namespace coda;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dim_ok(int64_t v) { return v >= kDimQuantum && v <= kMaxDim && v % kDimQuantum == 0; }
+
+bool rows_ok(int64_t M) { return M >= 1 && M <= kMaxRows; }
+
+bool dtype_ok(coda_dtype_t t) { return t == CODA_BF16 || t == CODA_F32; }
+
+// First failing pointer check over a list: NULL beats misalignment.
+coda_status_t check_ptrs(const void* const* ps, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ps[i] == nullptr) return CODA_ERR_NULL;
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(ps[i])) return CODA_ERR_ALIGN;
+  return CODA_OK;
+}
+
+coda_status_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return CODA_OK;
+  if (ws == nullptr || ws_bytes < need) return CODA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return CODA_ERR_ALIGN;
+  return CODA_OK;
+}
+
+size_t fwd_ws(int64_t M, int64_t D) { return align256(size_t(M) * size_t(ssq_cols(D)) * 4); }
+
+size_t bwd_ws(int64_t M, int64_t D) {
+  return align256(size_t(M) * size_t(D) * 2) + align256(size_t(dgamma_rows(M)) * size_t(D) * 4);
+}
+
+size_t unfused_fwd_ws(int64_t M, int64_t D) { return 2 * align256(size_t(M) * size_t(D) * 2); }
+
+size_t unfused_bwd_ws(int64_t M, int64_t D) {
+  return 2 * align256(size_t(M) * size_t(D) * 2) +
+         align256(size_t(ceil_div(M, kUnfusedBwdRows)) * size_t(D) * 4);
+}
+
+coda_status_t validate_fwd_common(const coda_fwd_args_t* a, bool need_g) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->x, a->W0, a->z, a->gamma, a->W1, a->h, a->r, a->y, a->g};
+  coda_status_t st = check_ptrs(ps, need_g ? 9 : 8);
+  if (st != CODA_OK) return st;
+  if (!need_g && a->g != nullptr && !aligned16(a->g)) return CODA_ERR_ALIGN;
+  if (!rows_ok(a->M) || !dim_ok(a->K0) || !dim_ok(a->D) || !dim_ok(a->N)) return CODA_ERR_SHAPE;
+  if (!(isfinite(a->eps) && a->eps > 0.0f)) return CODA_ERR_ARG;
+  if (!dtype_ok(a->y_dtype)) return CODA_ERR_ARG;
+  return CODA_OK;
+}
+
+coda_status_t validate_bwd_common(const coda_bwd_args_t* a) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1, a->da, a->dgamma, a->dW1, a->s};
+  coda_status_t st = check_ptrs(ps, 11);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N)) return CODA_ERR_SHAPE;
+  if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype)) return CODA_ERR_ARG;
+  return CODA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
+  (void)N;
+  if (!rows_ok(M) || !dim_ok(D)) return 0;
+  switch (op) {
+    case CODA_OP_FWD: return fwd_ws(M, D);
+    case CODA_OP_BWD: return bwd_ws(M, D);
+    case CODA_OP_UNFUSED_FWD: return unfused_fwd_ws(M, D);
+    case CODA_OP_UNFUSED_BWD: return unfused_bwd_ws(M, D);
+  }
+  return 0;
+}
+
+coda_status_t coda_validate_fwd(const coda_fwd_args_t* a, const void* ws, size_t ws_bytes) {
+  coda_status_t st = validate_fwd_common(a, true);
+  if (st != CODA_OK) return st;
+  return check_ws(ws, ws_bytes, fwd_ws(a->M, a->D));
+}
+
+coda_status_t coda_validate_bwd(const coda_bwd_args_t* a, const void* ws, size_t ws_bytes) {
+  coda_status_t st = validate_bwd_common(a);
+  if (st != CODA_OK) return st;
+  return check_ws(ws, ws_bytes, bwd_ws(a->M, a->D));
+}
+
+// Used by the unfused entry point (g is optional there).
+coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes) {
+  if (args == nullptr) return CODA_ERR_NULL;
+  if (op == CODA_OP_FWD) {
+    const coda_fwd_args_t* a = static_cast<const coda_fwd_args_t*>(args);
+    coda_status_t st = validate_fwd_common(a, false);
+    if (st != CODA_OK) return st;
+    return check_ws(ws, ws_bytes, unfused_fwd_ws(a->M, a->D));
+  }
+  if (op == CODA_OP_BWD) {
+    const coda_bwd_args_t* a = static_cast<const coda_bwd_args_t*>(args);
+    coda_status_t st = validate_bwd_common(a);
+    if (st != CODA_OK) return st;
+    return check_ws(ws, ws_bytes, unfused_bwd_ws(a->M, a->D));
+  }
+  return CODA_ERR_ARG;
+}
+
+coda_status_t coda_validate_gemm(const coda_gemm_args_t* a) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->A, a->B, a->C};
+  coda_status_t st = check_ptrs(ps, 3);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->N) || !dim_ok(a->K)) return CODA_ERR_SHAPE;
+  if ((a->a_layout != CODA_ROW && a->a_layout != CODA_COL) ||
+      (a->b_layout != CODA_ROW && a->b_layout != CODA_COL) || !dtype_ok(a->c_dtype))
+    return CODA_ERR_ARG;
+  const int64_t a_min = a->a_layout == CODA_ROW ? a->K : a->M;
+  const int64_t b_min = a->b_layout == CODA_ROW ? a->N : a->K;
+  if (a->lda < a_min || a->ldb < b_min || a->ldc < a->N) return CODA_ERR_SHAPE;
+  if (a->lda % 8 || a->ldb % 8 || a->ldc % 8) return CODA_ERR_ALIGN;
+  if (a->lda > kMaxDim || a->ldb > kMaxDim || a->ldc > kMaxDim) return CODA_ERR_SHAPE;
+  return CODA_OK;
+}
+
+const char* coda_status_string(coda_status_t s) {
+  switch (s) {
+    case CODA_OK: return "ok";
+    case CODA_ERR_NULL: return "a required pointer is NULL";
+    case CODA_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case CODA_ERR_ALIGN: return "a pointer or leading dimension is not 16-byte aligned";
+    case CODA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CODA_ERR_ARG: return "bad scalar argument";
+    case CODA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

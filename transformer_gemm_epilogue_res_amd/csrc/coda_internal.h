@@ -1,0 +1,38 @@
+// Internal constants shared by the host checks and the HIP kernels.
+#ifndef CODA_INTERNAL_H
+#define CODA_INTERNAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace coda {
+
+// Block tile of every GEMM: 256 x 256 outputs, K step 64, 4 waves in a 2 x 2
+// grid, each wave owning a 128 x 128 sub-tile.
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kBK = 64;
+constexpr int kWaveTileM = 128;
+constexpr int kWaveTileN = 128;
+constexpr int kThreads = 256;
+
+// K0, D and N must be multiples of this.
+constexpr int64_t kDimQuantum = 256;
+// Largest accepted K0 / D / N and M (keeps every per-tile buffer offset < 2^31).
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+
+// Row block of the unfused RMSNorm-backward kernel (its dgamma partial granularity).
+constexpr int kUnfusedBwdRows = 32;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Column count of the forward's sum-of-squares partials P[M, D / kWaveTileN].
+inline int64_t ssq_cols(int64_t D) { return D / kWaveTileN; }
+// Row count of the fused backward's dgamma partials Pg[ceil(M / kWaveTileM), D].
+inline int64_t dgamma_rows(int64_t M) { return ceil_div(M, kWaveTileM); }
+
+}  // namespace coda
+
+#endif

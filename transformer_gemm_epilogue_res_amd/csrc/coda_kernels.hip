@@ -1,0 +1,689 @@
+// HIP kernels for gfx950 (MI355X) and the launching half of the C ABI.
+//
+// One MFMA bf16 mainloop is shared by every GEMM; what differs is the epilogue
+// that runs on the fp32 accumulator tile while it is still in registers
+// (CODA: Rewriting Transformer Blocks as GEMM-Epilogue Programs; hotdry blog,
+// section "核心观察": mainloop + epilogue split, and section "五类 Epilogue
+// 原语": elementwise maps, vector loads, tile loads/stores, tile reductions).
+//
+// Mainloop design (gfx950):
+//   * block tile 256 x 256, K step 64, 256 threads = 4 waves in a 2 x 2 grid,
+//     each wave owning a 128 x 128 sub-tile = 8 x 8 MFMA 16x16x32 bf16 tiles
+//     (256 fp32 accumulators per lane);
+//   * A/B tiles move global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//     round trip), double-buffered (2 x 64 KB of the 160 KB LDS);
+//   * buffer descriptors are rebased per tile and per K step, so a row beyond
+//     the tensor's last row reads as zero: ragged M (and a ragged K = M in the
+//     weight-gradient GEMM) needs no special path;
+//   * LDS layouts are XOR-swizzled in 16-byte chunks so that fragment reads hit
+//     all 64 LDS banks once per cycle; operands stored MN-major (W0/W1 as
+//     [in, out], and both wgrad operands) are read with ds_read_b64_tr_b16;
+//   * the MFMA operands are swapped (the weight-side fragment is src0) so each
+//     lane ends up holding 4 *adjacent columns of one row* of C: lane l, reg e of
+//     tile (tm, tn) is C[16 tm + l % 16][16 tn + 4 (l / 16) + e]. Row sums then
+//     need only two cross-lane steps and stores are 8/16-byte vectors;
+//   * blocks are remapped so that consecutive output tiles land on the same XCD
+//     (the dispatcher deals blocks round-robin over the 8 XCDs, each with its
+//     own L2), and tiles are rastered in groups of 4 tile-rows.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/coda.h"
+#include "coda_internal.h"
+
+namespace coda {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+#define LDS_AS __attribute__((address_space(3)))
+typedef LDS_AS char lds_char_t;
+
+// ----------------------------------------------------------------- helpers
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
+}
+
+__device__ __forceinline__ void unpack4_bf16(uint2 v, float* o) {
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void unpack8_bf16(uint4 v, float* o) {
+  unpack4_bf16(make_uint2(v.x, v.y), o);
+  unpack4_bf16(make_uint2(v.z, v.w), o + 4);
+}
+
+__device__ __forceinline__ int64_t dceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  // Raw buffer (stride 0): a lane whose offset is past num_records reads 0.
+  const int64_t nr = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, 0x00020000);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ------------------------------------------------------ LDS tile layouts
+//
+// "K-rows" tile: R rows (an M or N index) x 64 k, 128 bytes per row, eight
+// 16-byte chunks; chunk c of row r sits at chunk c ^ ((r >> 1) & 7). A fragment
+// read (16 consecutive rows, one chunk) then covers all 64 banks.
+//
+// "K-cols" tile: 64 k-rows x C columns (C = 256), 512 bytes per k-row; chunk c
+// of k-row k sits at c ^ (((k & 3) << 1) | (k & 8)). The transposed reads of a
+// fragment (rows {4j..4j+3} and {8+4j..}, 32 bytes each) then cover all banks.
+
+__device__ __forceinline__ int swz_krows(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_kcols(int k) { return ((k & 3) << 1) | (k & 8); }
+
+// Global -> LDS copy of a K-rows tile (256 rows x 64 k) starting at element
+// (row0, k0) of a [nrows, ld] row-major tensor. 32 wave-instructions of 1 KB;
+// wave w issues segments w, w + 4, ...
+__device__ __forceinline__ void load_krows(lds_char_t* dst, const void* base, int64_t ld, int64_t row0,
+                                           int64_t nrows, int64_t k0, int wave, int lane) {
+  const char* tile = static_cast<const char*>(base) + (row0 * ld + k0) * 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (nrows - row0) * ld * 2 - k0 * 2);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int seg = q * 4 + wave;
+    const int row = seg * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_krows(row);
+    const uint32_t voff = uint32_t((int64_t(row) * ld + chunk * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + seg * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// Global -> LDS copy of a K-cols tile (64 k-rows x 256 columns) starting at
+// element (k0, col0) of a [nk, ld] row-major tensor (k-rows past nk read 0).
+__device__ __forceinline__ void load_kcols(lds_char_t* dst, const void* base, int64_t ld, int64_t k0,
+                                           int64_t nk, int64_t col0, int wave, int lane) {
+  const char* tile = static_cast<const char*>(base) + (k0 * ld + col0) * 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (nk - k0) * ld * 2 - col0 * 2);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int seg = q * 4 + wave;
+    const int k = seg * 2 + (lane >> 5);
+    const int chunk = (lane & 31) ^ swz_kcols(k);
+    const uint32_t voff = uint32_t((int64_t(k) * ld + chunk * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + seg * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// MFMA operand fragment (8 consecutive k for one row/column of C) for the
+// 16 rows starting at row_base of a K-rows tile, k slab kk (32 k each):
+// lane l gets row row_base + l % 16, k = 32 kk + 8 (l / 16) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_krows(const lds_char_t* tile, int row_base, int kk, int lane) {
+  const int row = row_base + (lane & 15);
+  const int chunk = (kk * 4 + (lane >> 4)) ^ swz_krows(row);
+  return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * 128 + chunk * 16);
+}
+
+// Same fragment from a K-cols tile, for the 16 columns starting at col_base:
+// two ds_read_b64_tr_b16. In each 16-lane block the instruction hands lane i
+// element (i % 4) of the 8 bytes fetched by lane 4 e + i / 4 as its element e;
+// so lane s of the block points at k-row (kb + s / 4), columns 4 (s % 4)..+3,
+// and every lane receives 4 consecutive k of its own column.
+__device__ __forceinline__ bf16x8_t frag_kcols(const lds_char_t* tile, int col_base, int kk, int lane) {
+  const int s = lane & 15;
+  const int col = col_base + 4 * (s & 3);
+  const int chunk = col >> 3;
+  const int sub = (col & 7) * 2;
+  const int k_lo = kk * 32 + (lane >> 4) * 8 + (s >> 2);
+  const int k_hi = k_lo + 4;
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (LDS_AS bf16x4_t*)(tile + k_lo * 512 + ((chunk ^ swz_kcols(k_lo)) * 16) + sub));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (LDS_AS bf16x4_t*)(tile + k_hi * 512 + ((chunk ^ swz_kcols(k_hi)) * 16) + sub));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ------------------------------------------------------------ mainloop
+
+struct GemmShape {
+  int64_t M, N, K;       // C is M x N, contraction over K
+  const void* A;         // A_K: [M, lda] (k contiguous); else [K, lda] (m contiguous)
+  int64_t lda;
+  const void* B;         // B_K: [N, ldb] (k contiguous); else [K, ldb] (n contiguous)
+  int64_t ldb;
+};
+
+// Block -> output tile. Consecutive logical tiles go to one XCD; within the
+// logical order tiles are rastered down groups of kGroupM tile-rows.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void map_tile(int64_t M, int64_t N, int& tile_m, int& tile_n) {
+  const int tiles_m = int(dceil_div(M, kBM));
+  const int tiles_n = int(N / kBN);
+  const int nb = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + (b / 8) : b;
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (t / per_group) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int r = t % per_group;
+  tile_m = first_m + r % gsz;
+  tile_n = r / gsz;
+}
+
+template <bool A_K, bool B_K>
+__device__ __forceinline__ void load_stage(lds_char_t* sa, lds_char_t* sb, const GemmShape& p, int64_t m0,
+                                           int64_t n0, int64_t k0, int wave, int lane) {
+  if constexpr (A_K) load_krows(sa, p.A, p.lda, m0, p.M, k0, wave, lane);
+  else load_kcols(sa, p.A, p.lda, k0, p.K, m0, wave, lane);
+  if constexpr (B_K) load_krows(sb, p.B, p.ldb, n0, p.N, k0, wave, lane);
+  else load_kcols(sb, p.B, p.ldb, k0, p.K, n0, wave, lane);
+}
+
+// acc[tm][tn] (lane l, reg e) = C[m0 + 128 wm + 16 tm + l % 16][n0 + 128 wn + 16 tn + 4 (l / 16) + e]
+template <bool A_K, bool B_K>
+__device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
+                                         f32x4_t (&acc)[8][8]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = int(dceil_div(p.K, kBK));
+  constexpr int kStage = (kBM + kBN) * kBK * 2;  // 64 KB
+  load_stage<A_K, B_K>(smem, smem + kBM * kBK * 2, p, m0, n0, 0, wave, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    lds_char_t* sa = smem + (kt & 1) * kStage;
+    lds_char_t* sb = sa + kBM * kBK * 2;
+    if (kt + 1 < KT) {
+      lds_char_t* na = smem + ((kt + 1) & 1) * kStage;
+      load_stage<A_K, B_K>(na, na + kBM * kBK * 2, p, m0, n0, int64_t(kt + 1) * kBK, wave, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t af[8], bfr[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        af[t] = A_K ? frag_krows(sa, wm * 128 + 16 * t, kk, lane) : frag_kcols(sa, wm * 128 + 16 * t, kk, lane);
+        bfr[t] = B_K ? frag_krows(sb, wn * 128 + 16 * t, kk, lane) : frag_kcols(sb, wn * 128 + 16 * t, kk, lane);
+      }
+#pragma unroll
+      for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 8; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[tn], af[tm], acc[tm][tn], 0, 0, 0);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ epilogues
+// Each epilogue gets the wave's 128 x 128 accumulator block whose first row is
+// mb and first column nb. Lane l owns rows mb + 16 tm + l % 16 and columns
+// nb + 16 tn + 4 (l / 16) + {0..3}.
+
+// Plain store C = acc (bf16 or fp32).
+template <bool F32>
+struct EpiStore {
+  void* C;
+  int64_t ldc, M;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+    const int li = lane & 15, lj = 4 * (lane >> 4);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      if (i >= M) continue;
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) {
+        const int64_t j = nb + 16 * tn + lj;
+        const f32x4_t v = acc[tm][tn];
+        if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(C) + i * ldc + j) = make_float4(v[0], v[1], v[2], v[3]);
+        else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + i * ldc + j) = pack4_bf16(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+};
+
+// GEMM0 epilogue: h = acc + z (fp32) -> store bf16 h; g = bf16(h * gamma) from
+// the fp32 h; per-row sum of squares of the fp32 h over the wave's 128 columns
+// -> P[i, nb / 128].
+struct EpiResidualSsq {
+  const uint16_t* z;
+  const uint16_t* gamma;
+  uint16_t* h;
+  uint16_t* g;
+  float* P;
+  int64_t M, D, pcols;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+    const int li = lane & 15, lj = 4 * (lane >> 4);
+    float gam[8][4];
+#pragma unroll
+    for (int tn = 0; tn < 8; ++tn) unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      const bool ok = i < M;
+      float ssq = 0.f;
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) {
+        const int64_t off = i * D + nb + 16 * tn + lj;
+        float zz[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(z + off), zz);
+        float hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hv[e] = acc[tm][tn][e] + zz[e];
+          ssq += hv[e] * hv[e];
+        }
+        if (ok) {
+          *reinterpret_cast<uint2*>(h + off) = pack4_bf16(hv[0], hv[1], hv[2], hv[3]);
+          *reinterpret_cast<uint2*>(g + off) =
+              pack4_bf16(hv[0] * gam[tn][0], hv[1] * gam[tn][1], hv[2] * gam[tn][2], hv[3] * gam[tn][3]);
+        }
+      }
+      // the 4 lanes l % 16 == li hold the rest of row i's 128 columns
+      ssq += shfl_xor(ssq, 16);
+      ssq += shfl_xor(ssq, 32);
+      if (lane < 16 && ok) P[i * pcols + nb / kWaveTileN] = ssq;
+    }
+  }
+};
+
+// GEMM1 epilogue: y = r_i * acc (the deferred RMSNorm row scale).
+template <bool F32>
+struct EpiRowScale {
+  const float* r;
+  void* y;
+  int64_t M, N;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+    const int li = lane & 15, lj = 4 * (lane >> 4);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      if (i >= M) continue;
+      const float ri = r[i];
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) {
+        const int64_t off = i * N + nb + 16 * tn + lj;
+        const f32x4_t v = acc[tm][tn];
+        if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(ri * v[0], ri * v[1], ri * v[2], ri * v[3]);
+        else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) = pack4_bf16(ri * v[0], ri * v[1], ri * v[2], ri * v[3]);
+      }
+    }
+  }
+};
+
+// Data-gradient epilogue on G = dY @ W1^T:
+//   da = r gamma G - (s r^2 / D) h,  Pg[row tile, j] = sum over the wave's 128 rows of G r h.
+template <bool F32>
+struct EpiRmsNormBwd {
+  const uint16_t* h;
+  const float* r;
+  const float* s;
+  const uint16_t* gamma;
+  void* da;
+  float* Pg;
+  int64_t M, D;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+    const int li = lane & 15, lj = 4 * (lane >> 4);
+    const float invD = 1.0f / float(D);
+    float gam[8][4], cs[8][4];
+#pragma unroll
+    for (int tn = 0; tn < 8; ++tn) {
+      unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cs[tn][e] = 0.f;
+    }
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      const bool ok = i < M;
+      const float ri = ok ? r[i] : 0.f;
+      const float c2 = ok ? s[i] * ri * ri * invD : 0.f;
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) {
+        const int64_t off = i * D + nb + 16 * tn + lj;
+        float hv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(h + off), hv);
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float G = acc[tm][tn][e];
+          d[e] = ri * gam[tn][e] * G - c2 * hv[e];
+          cs[tn][e] += G * ri * hv[e];
+        }
+        if (ok) {
+          if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(da) + off) = make_float4(d[0], d[1], d[2], d[3]);
+          else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(da) + off) = pack4_bf16(d[0], d[1], d[2], d[3]);
+        }
+      }
+    }
+    // column sums over the 16 lanes sharing l / 16 (they hold the 16 rows of each tile)
+#pragma unroll
+    for (int tn = 0; tn < 8; ++tn)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = cs[tn][e];
+        v += shfl_xor(v, 1);
+        v += shfl_xor(v, 2);
+        v += shfl_xor(v, 4);
+        v += shfl_xor(v, 8);
+        cs[tn][e] = v;
+      }
+    if (li == 0 && mb < M) {  // a wave whose rows all lie past M has no Pg row
+      float* dst = Pg + (mb / kWaveTileM) * D + nb + lj;
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn)
+        *reinterpret_cast<float4*>(dst + 16 * tn) = make_float4(cs[tn][0], cs[tn][1], cs[tn][2], cs[tn][3]);
+    }
+  }
+};
+
+template <bool A_K, bool B_K, class Epi>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * (kBM + kBN) * kBK * 2];
+  lds_char_t* smem = (lds_char_t*)smem_raw;
+  int tile_m, tile_n;
+  map_tile(p.M, p.N, tile_m, tile_n);
+  const int64_t m0 = int64_t(tile_m) * kBM, n0 = int64_t(tile_n) * kBN;
+  f32x4_t acc[8][8];
+  mainloop<A_K, B_K>(p, m0, n0, smem, acc);
+  const int wave = threadIdx.x >> 6;
+  epi(acc, m0 + (wave >> 1) * kWaveTileM, n0 + (wave & 1) * kWaveTileN, threadIdx.x & 63);
+}
+
+// ------------------------------------------------------- small kernels
+
+// r_i = 1 / sqrt(sum_t P[i, t] / D + eps), fixed summation order.
+__global__ __launch_bounds__(256) void rms_combine_kernel(const float* P, float* r, int64_t M, int64_t pcols,
+                                                          float D, float eps) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M) return;
+  float acc = 0.f;
+  for (int64_t t = 0; t < pcols; ++t) acc += P[i * pcols + t];
+  r[i] = 1.0f / sqrtf(acc / D + eps);
+}
+
+// Block-wide sum over 256 threads, fixed order (wave shuffles, then LDS).
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  const float t = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return t;
+}
+
+// One block per row i: s_i = sum_n dY_in y_in (fp32) and gr_i = bf16(r_i g_i).
+__global__ __launch_bounds__(256) void rowstat_kernel(const uint16_t* dY, const uint16_t* y, const uint16_t* g,
+                                                      const float* r, float* s, uint16_t* gr, int64_t N,
+                                                      int64_t D) {
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const uint4* a = reinterpret_cast<const uint4*>(dY + i * N);
+  const uint4* b = reinterpret_cast<const uint4*>(y + i * N);
+  float acc = 0.f;
+  for (int64_t v = threadIdx.x; v < N / 8; v += 256) {
+    float fa[8], fb[8];
+    unpack8_bf16(a[v], fa);
+    unpack8_bf16(b[v], fb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += fa[e] * fb[e];
+  }
+  const float tot = block_sum256(acc, red);
+  if (threadIdx.x == 0) s[i] = tot;
+  const float ri = r[i];
+  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
+  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
+  for (int64_t v = threadIdx.x; v < D / 8; v += 256) {
+    float f[8];
+    unpack8_bf16(gs[v], f);
+    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
+    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
+    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// dgamma_j = sum_t Pg[t, j], fixed order.
+__global__ __launch_bounds__(256) void dgamma_combine_kernel(const float* Pg, float* dgamma, int64_t rows,
+                                                             int64_t D) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= D) return;
+  float acc = 0.f;
+  for (int64_t t = 0; t < rows; ++t) acc += Pg[t * D + j];
+  dgamma[j] = acc;
+}
+
+// Unfused: one block per row. h = t + z (fp32, stored bf16), r from the fp32 h,
+// n = bf16(r h gamma) for the second GEMM.
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* t, const uint16_t* z,
+                                                          const uint16_t* gamma, uint16_t* h, float* r,
+                                                          uint16_t* n, int64_t D, float eps) {
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const uint4* tv = reinterpret_cast<const uint4*>(t + i * D);
+  const uint4* zv = reinterpret_cast<const uint4*>(z + i * D);
+  float ssq = 0.f;
+  for (int64_t v = threadIdx.x; v < D / 8; v += 256) {
+    float a[8], b[8];
+    unpack8_bf16(tv[v], a);
+    unpack8_bf16(zv[v], b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float hv = a[e] + b[e];
+      ssq += hv * hv;
+    }
+  }
+  const float tot = block_sum256(ssq, red);
+  const float ri = 1.0f / sqrtf(tot / float(D) + eps);
+  if (threadIdx.x == 0) r[i] = ri;
+  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
+  uint4* ho = reinterpret_cast<uint4*>(h + i * D);
+  uint4* no = reinterpret_cast<uint4*>(n + i * D);
+  for (int64_t v = threadIdx.x; v < D / 8; v += 256) {
+    float a[8], b[8], gm[8], hv[8];
+    unpack8_bf16(tv[v], a);
+    unpack8_bf16(zv[v], b);
+    unpack8_bf16(gv[v], gm);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = a[e] + b[e];
+    uint2 lo = pack4_bf16(hv[0], hv[1], hv[2], hv[3]), hi = pack4_bf16(hv[4], hv[5], hv[6], hv[7]);
+    ho[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    lo = pack4_bf16(ri * hv[0] * gm[0], ri * hv[1] * gm[1], ri * hv[2] * gm[2], ri * hv[3] * gm[3]);
+    hi = pack4_bf16(ri * hv[4] * gm[4], ri * hv[5] * gm[5], ri * hv[6] * gm[6], ri * hv[7] * gm[7]);
+    no[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// Unfused RMSNorm backward on a materialised bf16 G: block (bx, by) covers
+// columns [2048 bx, +2048) (8 per thread) and rows [32 by, +32).
+template <bool F32>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* G, const uint16_t* h, const float* r,
+                                                          const float* s, const uint16_t* gamma, void* da,
+                                                          float* Pg, int64_t M, int64_t D) {
+  const int64_t j = int64_t(blockIdx.x) * 2048 + threadIdx.x * 8;
+  if (j >= D) return;
+  const int64_t i0 = int64_t(blockIdx.y) * kUnfusedBwdRows;
+  const float invD = 1.0f / float(D);
+  float gm[8], cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  unpack8_bf16(*reinterpret_cast<const uint4*>(gamma + j), gm);
+  for (int64_t i = i0; i < min(M, i0 + kUnfusedBwdRows); ++i) {
+    float gv[8], hv[8], d[8];
+    unpack8_bf16(*reinterpret_cast<const uint4*>(G + i * D + j), gv);
+    unpack8_bf16(*reinterpret_cast<const uint4*>(h + i * D + j), hv);
+    const float ri = r[i], c2 = s[i] * ri * ri * invD;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      d[e] = ri * gm[e] * gv[e] - c2 * hv[e];
+      cs[e] += gv[e] * ri * hv[e];
+    }
+    if constexpr (F32) {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(da) + i * D + j);
+      o[0] = make_float4(d[0], d[1], d[2], d[3]);
+      o[1] = make_float4(d[4], d[5], d[6], d[7]);
+    } else {
+      const uint2 lo = pack4_bf16(d[0], d[1], d[2], d[3]), hi = pack4_bf16(d[4], d[5], d[6], d[7]);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(da) + i * D + j) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+  float4* o = reinterpret_cast<float4*>(Pg + int64_t(blockIdx.y) * D + j);
+  o[0] = make_float4(cs[0], cs[1], cs[2], cs[3]);
+  o[1] = make_float4(cs[4], cs[5], cs[6], cs[7]);
+}
+
+// ----------------------------------------------------------- launchers
+
+template <bool A_K, bool B_K, class Epi>
+hipError_t launch_gemm(const GemmShape& p, const Epi& epi, hipStream_t st) {
+  const int64_t blocks = ceil_div(p.M, kBM) * (p.N / kBN);
+  hipLaunchKernelGGL((gemm_kernel<A_K, B_K, Epi>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p, epi);
+  return hipGetLastError();
+}
+
+template <bool A_K, bool B_K>
+hipError_t launch_store(const GemmShape& p, void* C, int64_t ldc, bool f32, hipStream_t st) {
+  if (f32) return launch_gemm<A_K, B_K>(p, EpiStore<true>{C, ldc, p.M}, st);
+  return launch_gemm<A_K, B_K>(p, EpiStore<false>{C, ldc, p.M}, st);
+}
+
+hipError_t gemm_plain(const GemmShape& p, bool a_k, bool b_k, void* C, int64_t ldc, bool f32, hipStream_t st) {
+  if (a_k && b_k) return launch_store<true, true>(p, C, ldc, f32, st);
+  if (a_k && !b_k) return launch_store<true, false>(p, C, ldc, f32, st);
+  if (!a_k && b_k) return launch_store<false, true>(p, C, ldc, f32, st);
+  return launch_store<false, false>(p, C, ldc, f32, st);
+}
+
+char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// s and bf16(r * g), then the weight gradient dW1 = bf16(r g)^T @ dY.
+hipError_t bwd_rowstat(const coda_bwd_args_t* a, uint16_t* gr, hipStream_t st) {
+  hipLaunchKernelGGL(rowstat_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, (const uint16_t*)a->dY,
+                     (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, a->s, gr, a->N, a->D);
+  return hipGetLastError();
+}
+
+hipError_t bwd_wgrad(const coda_bwd_args_t* a, const uint16_t* gr, hipStream_t st) {
+  // C = dW1 [D, N]: rows j (m index) from gr^T (m contiguous), columns n from dY (n contiguous), K = M
+  const GemmShape p{a->D, a->N, a->M, gr, a->D, a->dY, a->N};
+  return gemm_plain(p, false, false, a->dW1, a->N, a->dW1_dtype == CODA_F32, st);
+}
+
+hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, hipStream_t st) {
+  hipLaunchKernelGGL(dgamma_combine_kernel, dim3(unsigned(ceil_div(a->D, 256))), dim3(256), 0, st, Pg, a->dgamma,
+                     rows, a->D);
+  return hipGetLastError();
+}
+
+coda_status_t to_status(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
+
+}  // namespace coda
+
+using namespace coda;
+
+extern "C" {
+
+coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  coda_status_t v = coda_validate_fwd(a, ws, ws_bytes);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* P = reinterpret_cast<float*>(ws);
+  const int64_t pcols = ssq_cols(a->D);
+  // 1. GEMM0 x @ W0 with the residual / h / g / sum-of-squares epilogue
+  const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
+  hipError_t e = launch_gemm<true, false>(
+      p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  // 2. partial sums -> r
+  hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, 256))), dim3(256), 0, st, P, a->r, a->M, pcols,
+                     float(a->D), a->eps);
+  if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+  // 3. GEMM1 g @ W1 with the row-scale epilogue
+  const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
+  if (a->y_dtype == CODA_F32) e = launch_gemm<true, false>(p1, EpiRowScale<true>{a->r, a->y, a->M, a->N}, st);
+  else e = launch_gemm<true, false>(p1, EpiRowScale<false>{a->r, a->y, a->M, a->N}, st);
+  return to_status(e);
+}
+
+coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  coda_status_t v = coda_validate_bwd(a, ws, ws_bytes);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
+  float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
+  hipError_t e = bwd_rowstat(a, gr, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  // G = dY @ W1^T: A = dY [M, N] (k contiguous), B(k=n, j) = W1[j, n] (k contiguous)
+  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
+  if (a->da_dtype == CODA_F32)
+    e = launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
+  else
+    e = launch_gemm<true, true>(pd, EpiRmsNormBwd<false>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_dgamma(Pg, dgamma_rows(a->M), a, st)) != hipSuccess) return CODA_ERR_HIP;
+  return to_status(bwd_wgrad(a, gr, st));
+}
+
+coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream) {
+  coda_status_t v = coda_validate_unfused(op, args, ws, ws_bytes);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (op == CODA_OP_FWD) {
+    const coda_fwd_args_t* a = static_cast<const coda_fwd_args_t*>(args);
+    const size_t md = align256(size_t(a->M) * size_t(a->D) * 2);
+    uint16_t* t = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* n = reinterpret_cast<uint16_t*>(ws_at(ws, md));
+    const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
+    hipError_t e = gemm_plain(p0, true, false, t, a->D, false, st);
+    if (e != hipSuccess) return CODA_ERR_HIP;
+    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, t, (const uint16_t*)a->z,
+                       (const uint16_t*)a->gamma, (uint16_t*)a->h, a->r, n, a->D, a->eps);
+    if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+    const GemmShape p1{a->M, a->N, a->D, n, a->D, a->W1, a->N};
+    return to_status(gemm_plain(p1, true, false, a->y, a->N, a->y_dtype == CODA_F32, st));
+  }
+  const coda_bwd_args_t* a = static_cast<const coda_bwd_args_t*>(args);
+  const size_t md = align256(size_t(a->M) * size_t(a->D) * 2);
+  uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, md));
+  float* Pg = reinterpret_cast<float*>(ws_at(ws, 2 * md));
+  hipError_t e = bwd_rowstat(a, gr, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
+  if ((e = gemm_plain(pd, true, true, G, a->D, false, st)) != hipSuccess) return CODA_ERR_HIP;
+  const dim3 grid(unsigned(ceil_div(a->D, 2048)), unsigned(ceil_div(a->M, kUnfusedBwdRows)));
+  if (a->da_dtype == CODA_F32)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<true>, grid, dim3(256), 0, st, G, (const uint16_t*)a->h, a->r, a->s,
+                       (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<false>, grid, dim3(256), 0, st, G, (const uint16_t*)a->h, a->r, a->s,
+                       (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D);
+  if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_dgamma(Pg, ceil_div(a->M, kUnfusedBwdRows), a, st)) != hipSuccess) return CODA_ERR_HIP;
+  return to_status(bwd_wgrad(a, gr, st));
+}
+
+coda_status_t coda_gemm(const coda_gemm_args_t* a, void* stream) {
+  coda_status_t v = coda_validate_gemm(a);
+  if (v != CODA_OK) return v;
+  const GemmShape p{a->M, a->N, a->K, a->A, a->lda, a->B, a->ldb};
+  return to_status(gemm_plain(p, a->a_layout == CODA_ROW, a->b_layout == CODA_COL, a->C, a->ldc,
+                              a->c_dtype == CODA_F32, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
