@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM -> residual -> RMSNorm -> GEMM chain on one MI355X.
+
+One step = the fused forward (coda_fwd) and the fused backward (coda_bwd, on the
+forward's saved h, g, y, r) at the Llama-3-8B layer shape: M = 8192 tokens,
+K0 = D = 4096, N = 28672 (ffn 14336, gate/up interleaved), bf16 storage, fp32
+accumulation, eps = 1e-5. Inputs are seeded synthetic tensors with the value
+distributions of the parity tests, already resident in HBM when timing starts.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value     = algorithmic TFLOP per step / seconds per step (forward 2MK0D + 2MDN,
+              backward 4MDN; epilogue arithmetic is not counted),
+  roofline  = the longest kernel of the step against the bf16 dense MFMA peak,
+              its duration from HIP events recorded around it on its stream,
+  cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (MI355X)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "fused GEMM-Res-RMSNorm-GEMM TFLOP/s & % bf16 MFMA peak, Llama-3-8B shape"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(M, K0, D, N):
+    """Per-launch algorithmic work: ('flop', F) for MFMA kernels, ('byte', B) for HBM-bound ones."""
+    return {
+        "gemm0_residual_ssq": ("flop", 2 * M * K0 * D),
+        "rms_combine": ("byte", M * (D // 128) * 4 + M * 4),
+        "gemm1_rowscale": ("flop", 2 * M * D * N),
+        "rowstat_s_rg": ("byte", 2 * M * N * 2 + 2 * M * D * 2 + 2 * M * 4),
+        "dgrad_rmsnorm_bwd": ("flop", 2 * M * N * D),
+        "dgamma_combine": ("byte", ((M + 127) // 128) * D * 4 + D * 4),
+        "wgrad": ("flop", 2 * M * D * N),
+    }
+
+
+def cpu_baseline(host, rows, ncols, seed=0):
+    """Time the fp64 oracle (as it is) on a sub-batch of sampled rows of the workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import coda_oracle as orc
+    from transformer_gemm_epilogue_res_amd import inputs
+
+    M, K0 = host["x"].shape
+    D, N = host["W1"].shape
+    R = len(rows)
+    eps = inputs.EPS
+    t0 = time.perf_counter()
+    f = orc.forward(host["x"], host["W0"], host["z"], host["gamma"], host["W1"], eps)
+    t1 = time.perf_counter()
+    # the sub-batch's saved set in its storage types (outside the timing)
+    gam = orc.f64(host["gamma"])
+    h_s = torch.from_numpy(f["h"]).to(torch.bfloat16)
+    g_s = torch.from_numpy(f["h"] * gam[None, :]).to(torch.bfloat16)
+    y_s = torch.from_numpy(f["y"]).to(torch.bfloat16)
+    r_s = torch.from_numpy(f["r"]).to(torch.float32)
+    jc = inputs.sample(D, ncols, seed, "dgamma_cols").numpy()
+    nc = inputs.sample(N, ncols, seed, "dw1_cols").numpy()
+    t2 = time.perf_counter()
+    orc.backward(host["dY"], y_s, h_s, g_s, r_s, host["gamma"], host["W1"], dgamma_cols=jc, dw1_cols=nc)
+    t3 = time.perf_counter()
+    flops = 2 * R * (K0 * D + D * N) + 2 * R * N * D + 2 * R * N + 2 * R * N * ncols + 2 * R * D * ncols
+    secs = (t1 - t0) + (t3 - t2)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {R} sampled rows of the 8B workload: forward of those rows, then "
+                       f"the backward of that {R}-row sub-batch (s, G, da for every row; dgamma and dW1 on "
+                       f"{ncols} sampled columns each); {flops / 1e9:.1f} GFLOP in {secs:.2f} s"),
+            "seconds": secs, "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows in the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-cols", type=int, default=64)
+    ap.add_argument("--no-unfused", action="store_true", help="skip timing the unfused baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the chain's kernels run on a single "
+              "device and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from transformer_gemm_epilogue_res_amd import _lib as L
+    from transformer_gemm_epilogue_res_amd import inputs
+
+    c = inputs.CONFIGS["llama3_8b"]
+    M, K0, D, N = c["M"], c["K0"], c["D"], c["N"]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    bf = torch.bfloat16
+    log(f"[bench] llama3_8b M={M} K0={K0} D={D} N={N}: generating inputs on {dev}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def rnd(*shape, scale=1.0, shift=0.0):
+        return (torch.randn(*shape, generator=gen, device=dev) * scale + shift).to(bf)
+
+    x, W0 = rnd(M, K0), rnd(K0, D, scale=K0 ** -0.5)
+    z, gamma = rnd(M, D), rnd(D, scale=0.1, shift=1.0)
+    W1, dY = rnd(D, N, scale=D ** -0.5), rnd(M, N)
+    fo = {"h": torch.empty(M, D, dtype=bf, device=dev), "g": torch.empty(M, D, dtype=bf, device=dev),
+          "r": torch.empty(M, dtype=torch.float32, device=dev), "y": torch.empty(M, N, dtype=bf, device=dev)}
+    bo = {"da": torch.empty(M, D, dtype=bf, device=dev), "dgamma": torch.empty(D, dtype=torch.float32, device=dev),
+          "dW1": torch.empty(D, N, dtype=bf, device=dev), "s": torch.empty(M, dtype=torch.float32, device=dev)}
+    fws = L.workspace(L.CODA_OP_FWD, M, D, N, dev)
+    bws = L.workspace(L.CODA_OP_BWD, M, D, N, dev)
+    F = L.bind_fwd(x, W0, z, gamma, W1, inputs.EPS, fo, fws)
+    B = L.bind_bwd(dY, fo["y"], fo["h"], fo["g"], fo["r"], gamma, W1, bo, bws)
+    stream = torch.cuda.current_stream(dev)
+    sp = L.current_stream(dev)
+    names = list(L.FWD_STAGE_NAMES) + list(L.BWD_STAGE_NAMES)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        F.run(sp)
+        B.run(sp)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        for i in range(F.nstages):
+            F.stage(i, sp)
+            e[1 + i].record(stream)
+        for i in range(B.nstages):
+            B.stage(i, sp)
+            e[1 + F.nstages + i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = {n: 0.0 for n in names}
+    step_ms = []
+    for e in ev:
+        for i, n in enumerate(names):
+            per[n] += e[i].elapsed_time(e[i + 1])
+        step_ms.append(e[0].elapsed_time(e[-1]))
+    per = {n: v / args.steps for n, v in per.items()}          # ms per launch
+    ms_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps    # whole timed region / steps
+    fwd_ms = sum(per[n] for n in L.FWD_STAGE_NAMES)
+    bwd_ms = sum(per[n] for n in L.BWD_STAGE_NAMES)
+    fwd_flop = 2 * M * K0 * D + 2 * M * D * N
+    bwd_flop = 4 * M * D * N
+    value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
+    work = stage_work(M, K0, D, N)
+    kernels = {}
+    for n in names:
+        kind, amount = work[n]
+        rate = amount / (per[n] * 1e-3)
+        kernels[n] = {"us": round(per[n] * 1e3, 2),
+                      ("tflops" if kind == "flop" else "gbps"): round(rate / (1e12 if kind == "flop" else 1e9), 1)}
+    dom = max(names, key=lambda n: per[n])
+    dk, damount = work[dom]
+    if dk == "flop":
+        ach = damount / (per[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "per_launch": f"{damount / 1e12:.4f} TFLOP", "avg_us": round(per[dom] * 1e3, 1)}
+    else:
+        ach = damount / (per[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "per_launch": f"{damount / 1e9:.3f} GB", "avg_us": round(per[dom] * 1e3, 1)}
+    log(f"[bench] step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
+        f"fwd {fwd_ms:.3f} ms, bwd {bwd_ms:.3f} ms")
+    for n in names:
+        log(f"[bench]   {n:20s} {kernels[n]}")
+
+    unfused = None
+    if not args.no_unfused:
+        log("[bench] timing the unfused baseline")
+        ufo = dict(fo, g=None)
+        uF = L.bind_fwd(x, W0, z, gamma, W1, inputs.EPS, ufo, L.workspace(L.CODA_OP_UNFUSED_FWD, M, D, N, dev))
+        uB = L.bind_bwd(dY, fo["y"], fo["h"], fo["g"], fo["r"], gamma, W1, bo,
+                        L.workspace(L.CODA_OP_UNFUSED_BWD, M, D, N, dev))
+        t = {}
+        for name, obj in (("fwd", uF), ("bwd", uB)):
+            for _ in range(2):
+                obj.run(sp, unfused=True)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                obj.run(sp, unfused=True)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t[name] = a.elapsed_time(b) / args.steps
+        unfused = {"fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
+                   "fused_fwd_speedup": round(t["fwd"] / fwd_ms, 3), "fused_bwd_speedup": round(t["bwd"] / bwd_ms, 3)}
+        log(f"[bench] unfused fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms")
+
+    cpu = None
+    if args.cpu_rows > 0:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        rows = inputs.sample(M, args.cpu_rows, 0, "rows").to(dev)
+        host = {"x": x.index_select(0, rows).cpu(), "z": z.index_select(0, rows).cpu(), "W0": W0.cpu(),
+                "gamma": gamma.cpu(), "W1": W1.cpu(), "dY": dY.index_select(0, rows).cpu()}
+        cpu = cpu_baseline(host, rows.cpu().numpy(), args.cpu_cols)
+        log(f"[bench] cpu baseline {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3_8b fused forward + backward", "M": M, "K0": K0, "D": D, "N": N,
+                   "eps": inputs.EPS, "parallelism": "single GPU"},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / fwd_ms / 1e9, 1),
+                "pct_peak": round(100 * fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
+                "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
+        "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

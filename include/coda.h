@@ -168,6 +168,20 @@ coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void
  * dW1 = bf16(r*g)^T @ dY. */
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
+/* The stages of coda_fwd and coda_bwd, one kernel each, for callers that
+ * interleave their own work or time the kernels. Running stages 0..n-1 in order
+ * on one stream is exactly coda_fwd / coda_bwd; a stage reads what earlier
+ * stages wrote into the outputs and the workspace. Each call validates the
+ * whole argument set; a stage index out of range returns CODA_ERR_ARG.
+ *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine,
+ *             2 GEMM1 + row-scale epilogue
+ *   backward: 0 s and bf16(r*g), 1 G = dY@W1^T + RMSNorm-backward epilogue,
+ *             2 dgamma combine, 3 dW1 GEMM */
+#define CODA_FWD_STAGES 3
+#define CODA_BWD_STAGES 4
+coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
+coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
+
 /* Unfused baseline with the same mainloop and separate row kernels.
  *   op = CODA_OP_FWD, args = coda_fwd_args_t*: t = x@W0 (bf16, workspace) ->
  *     add+RMSNorm row kernel (h, r, n = bf16(r*h*gamma) into the workspace) ->

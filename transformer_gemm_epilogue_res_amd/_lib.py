@@ -21,6 +21,9 @@ CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA
 CODA_BF16, CODA_F32 = 0, 1
 CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD = range(4)
 CODA_ROW, CODA_COL = 0, 1
+CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 4
+FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
+BWD_STAGE_NAMES = ("rowstat_s_rg", "dgrad_rmsnorm_bwd", "dgamma_combine", "wgrad")
 
 
 class FwdArgs(ctypes.Structure):
@@ -69,6 +72,8 @@ def lib() -> ctypes.CDLL:
                            ("coda_fwd", [POINTER(FwdArgs), c_void_p, c_size_t, c_void_p]),
                            ("coda_bwd", [POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
                            ("coda_unfused_ref", [c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+                           ("coda_fwd_stage", [c_int, POINTER(FwdArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_bwd_stage", [c_int, POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
                            ("coda_gemm", [POINTER(GemmArgs), c_void_p])):
             fn = getattr(L, name)
             fn.restype = c_int
@@ -195,6 +200,42 @@ def bwd(dY, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_dtype=torch.bflo
         st = lib().coda_bwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "coda_unfused_ref(bwd)" if unfused else "coda_bwd")
     return out
+
+
+class Bound:
+    """A forward or backward call with its arguments marshalled once, for repeated
+    launches (benchmarks): .run() enqueues the whole call, .stage(i) one stage."""
+
+    def __init__(self, kind, args, ws, keep):
+        self.kind, self.args, self.ws, self._keep = kind, args, ws, keep
+        self.nstages = CODA_FWD_STAGES if kind == "fwd" else CODA_BWD_STAGES
+
+    def stage(self, i, stream):
+        fn = lib().coda_fwd_stage if self.kind == "fwd" else lib().coda_bwd_stage
+        _check(fn(i, ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}_stage({i})")
+
+    def run(self, stream, unfused=False):
+        if unfused:
+            op = CODA_OP_FWD if self.kind == "fwd" else CODA_OP_BWD
+            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream),
+                   "coda_unfused_ref")
+        else:
+            fn = lib().coda_fwd if self.kind == "fwd" else lib().coda_bwd
+            _check(fn(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}")
+
+
+def bind_fwd(x, W0, z, gamma, W1, eps, out, ws):
+    return Bound("fwd", _fwd_args(x, W0, z, gamma, W1, eps, out["h"], out["g"], out["r"], out["y"]), ws,
+                 (x, W0, z, gamma, W1, out))
+
+
+def bind_bwd(dY, y, h, g, r, gamma, W1, out, ws):
+    return Bound("bwd", _bwd_args(dY, y, h, g, r, gamma, W1, out["da"], out["dgamma"], out["dW1"], out["s"]), ws,
+                 (dY, y, h, g, r, gamma, W1, out))
+
+
+def current_stream(device="cuda:0") -> c_void_p:
+    return _stream(device)
 
 
 def gemm(A, B, a_layout=CODA_ROW, b_layout=CODA_ROW, out_dtype=torch.float32, M=None, N=None, K=None):

@@ -598,45 +598,62 @@ using namespace coda;
 
 extern "C" {
 
-coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
   coda_status_t v = coda_validate_fwd(a, ws, ws_bytes);
   if (v != CODA_OK) return v;
+  if (stage < 0 || stage >= CODA_FWD_STAGES) return CODA_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* P = reinterpret_cast<float*>(ws);
   const int64_t pcols = ssq_cols(a->D);
-  // 1. GEMM0 x @ W0 with the residual / h / g / sum-of-squares epilogue
-  const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
-  hipError_t e = launch_gemm<true, false>(
-      p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st);
-  if (e != hipSuccess) return CODA_ERR_HIP;
-  // 2. partial sums -> r
-  hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, 256))), dim3(256), 0, st, P, a->r, a->M, pcols,
-                     float(a->D), a->eps);
-  if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
-  // 3. GEMM1 g @ W1 with the row-scale epilogue
+  if (stage == 0) {  // GEMM0 x @ W0 with the residual / h / g / sum-of-squares epilogue
+    const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
+    return to_status(launch_gemm<true, false>(
+        p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st));
+  }
+  if (stage == 1) {  // partial sums of squares -> r
+    hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, 256))), dim3(256), 0, st, P, a->r, a->M,
+                       pcols, float(a->D), a->eps);
+    return to_status(hipGetLastError());
+  }
+  // GEMM1 g @ W1 with the row-scale epilogue
   const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
-  if (a->y_dtype == CODA_F32) e = launch_gemm<true, false>(p1, EpiRowScale<true>{a->r, a->y, a->M, a->N}, st);
-  else e = launch_gemm<true, false>(p1, EpiRowScale<false>{a->r, a->y, a->M, a->N}, st);
-  return to_status(e);
+  if (a->y_dtype == CODA_F32) return to_status(launch_gemm<true, false>(p1, EpiRowScale<true>{a->r, a->y, a->M, a->N}, st));
+  return to_status(launch_gemm<true, false>(p1, EpiRowScale<false>{a->r, a->y, a->M, a->N}, st));
 }
 
-coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  for (int s = 0; s < CODA_FWD_STAGES; ++s) {
+    const coda_status_t v = coda_fwd_stage(s, a, ws, ws_bytes, stream);
+    if (v != CODA_OK) return v;
+  }
+  return CODA_OK;
+}
+
+coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
   coda_status_t v = coda_validate_bwd(a, ws, ws_bytes);
   if (v != CODA_OK) return v;
+  if (stage < 0 || stage >= CODA_BWD_STAGES) return CODA_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
   float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
-  hipError_t e = bwd_rowstat(a, gr, st);
-  if (e != hipSuccess) return CODA_ERR_HIP;
-  // G = dY @ W1^T: A = dY [M, N] (k contiguous), B(k=n, j) = W1[j, n] (k contiguous)
-  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
-  if (a->da_dtype == CODA_F32)
-    e = launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
-  else
-    e = launch_gemm<true, true>(pd, EpiRmsNormBwd<false>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
-  if (e != hipSuccess) return CODA_ERR_HIP;
-  if ((e = bwd_dgamma(Pg, dgamma_rows(a->M), a, st)) != hipSuccess) return CODA_ERR_HIP;
+  if (stage == 0) return to_status(bwd_rowstat(a, gr, st));
+  if (stage == 1) {
+    // G = dY @ W1^T: A = dY [M, N] (k contiguous), B(k=n, j) = W1[j, n] (k contiguous)
+    const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
+    if (a->da_dtype == CODA_F32)
+      return to_status(launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st));
+    return to_status(launch_gemm<true, true>(pd, EpiRmsNormBwd<false>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st));
+  }
+  if (stage == 2) return to_status(bwd_dgamma(Pg, dgamma_rows(a->M), a, st));
   return to_status(bwd_wgrad(a, gr, st));
+}
+
+coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  for (int s = 0; s < CODA_BWD_STAGES; ++s) {
+    const coda_status_t v = coda_bwd_stage(s, a, ws, ws_bytes, stream);
+    if (v != CODA_OK) return v;
+  }
+  return CODA_OK;
 }
 
 coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream) {
