@@ -1,48 +1,22 @@
 // HIP kernels for gfx950 (MI355X) and the launching half of the C ABI.
 //
-// One MFMA bf16 mainloop is shared by every GEMM; what differs is the epilogue
-// that runs on the fp32 accumulator tile while it is still in registers
-// (CODA: Rewriting Transformer Blocks as GEMM-Epilogue Programs; hotdry blog,
-// section "核心观察": mainloop + epilogue split, and section "五类 Epilogue
-// 原语": elementwise maps, vector loads, tile loads/stores, tile reductions).
-//
-// Mainloop design (gfx950):
-//   * block tile 256 x 256, K step 64, 256 threads = 4 waves in a 2 x 2 grid,
-//     each wave owning a 128 x 128 sub-tile = 8 x 8 MFMA 16x16x32 bf16 tiles
-//     (256 fp32 accumulators per lane);
-//   * A/B tiles move global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
-//     round trip), double-buffered (2 x 64 KB of the 160 KB LDS);
-//   * buffer descriptors are rebased per tile and per K step, so a row beyond
-//     the tensor's last row reads as zero: ragged M (and a ragged K = M in the
-//     weight-gradient GEMM) needs no special path;
-//   * LDS layouts are XOR-swizzled in 16-byte chunks so that fragment reads hit
-//     all 64 LDS banks once per cycle; operands stored MN-major (W0/W1 as
-//     [in, out], and both wgrad operands) are read with ds_read_b64_tr_b16;
-//   * the MFMA operands are swapped (the weight-side fragment is src0) so each
-//     lane ends up holding 4 *adjacent columns of one row* of C: lane l, reg e of
-//     tile (tm, tn) is C[16 tm + l % 16][16 tn + 4 (l / 16) + e]. Row sums then
-//     need only two cross-lane steps and stores are 8/16-byte vectors;
-//   * blocks are remapped so that consecutive output tiles land on the same XCD
-//     (the dispatcher deals blocks round-robin over the 8 XCDs, each with its
-//     own L2), and tiles are rastered in groups of 4 tile-rows.
+// Every GEMM of the chain runs the same MFMA mainloop (gemm_mainloop.hpp); what
+// differs is the epilogue that runs on the fp32 accumulator tile while it is
+// still in registers (CODA: Rewriting Transformer Blocks as GEMM-Epilogue
+// Programs; hotdry blog, section "核心观察": mainloop + epilogue split, and
+// section "五类 Epilogue 原语": elementwise maps, vector loads, tile loads and
+// stores, tile reductions finished by a light auxiliary kernel).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "../../include/coda.h"
 #include "coda_internal.h"
+#include "gemm_mainloop.hpp"
 
 namespace coda {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-#define LDS_AS __attribute__((address_space(3)))
-typedef LDS_AS char lds_char_t;
-
 // ----------------------------------------------------------------- helpers
-
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 // Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
@@ -66,170 +40,7 @@ __device__ __forceinline__ void unpack8_bf16(uint4 v, float* o) {
   unpack4_bf16(make_uint2(v.z, v.w), o + 4);
 }
 
-__device__ __forceinline__ int64_t dceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  // Raw buffer (stride 0): a lane whose offset is past num_records reads 0.
-  const int64_t nr = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, 0x00020000);
-}
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// ------------------------------------------------------ LDS tile layouts
-//
-// "K-rows" tile: R rows (an M or N index) x 64 k, 128 bytes per row, eight
-// 16-byte chunks; chunk c of row r sits at chunk c ^ ((r >> 1) & 7). A fragment
-// read (16 consecutive rows, one chunk) then covers all 64 banks.
-//
-// "K-cols" tile: 64 k-rows x C columns (C = 256), 512 bytes per k-row; chunk c
-// of k-row k sits at c ^ (((k & 3) << 1) | (k & 8)). The transposed reads of a
-// fragment (rows {4j..4j+3} and {8+4j..}, 32 bytes each) then cover all banks.
-
-__device__ __forceinline__ int swz_krows(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_kcols(int k) { return ((k & 3) << 1) | (k & 8); }
-
-// Global -> LDS copy of a K-rows tile (256 rows x 64 k) starting at element
-// (row0, k0) of a [nrows, ld] row-major tensor. 32 wave-instructions of 1 KB;
-// wave w issues segments w, w + 4, ...
-__device__ __forceinline__ void load_krows(lds_char_t* dst, const void* base, int64_t ld, int64_t row0,
-                                           int64_t nrows, int64_t k0, int wave, int lane) {
-  const char* tile = static_cast<const char*>(base) + (row0 * ld + k0) * 2;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (nrows - row0) * ld * 2 - k0 * 2);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int seg = q * 4 + wave;
-    const int row = seg * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz_krows(row);
-    const uint32_t voff = uint32_t((int64_t(row) * ld + chunk * 8) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + seg * 1024), 16, voff, 0, 0, 0);
-  }
-}
-
-// Global -> LDS copy of a K-cols tile (64 k-rows x 256 columns) starting at
-// element (k0, col0) of a [nk, ld] row-major tensor (k-rows past nk read 0).
-__device__ __forceinline__ void load_kcols(lds_char_t* dst, const void* base, int64_t ld, int64_t k0,
-                                           int64_t nk, int64_t col0, int wave, int lane) {
-  const char* tile = static_cast<const char*>(base) + (k0 * ld + col0) * 2;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tile, (nk - k0) * ld * 2 - col0 * 2);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int seg = q * 4 + wave;
-    const int k = seg * 2 + (lane >> 5);
-    const int chunk = (lane & 31) ^ swz_kcols(k);
-    const uint32_t voff = uint32_t((int64_t(k) * ld + chunk * 8) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + seg * 1024), 16, voff, 0, 0, 0);
-  }
-}
-
-// MFMA operand fragment (8 consecutive k for one row/column of C) for the
-// 16 rows starting at row_base of a K-rows tile, k slab kk (32 k each):
-// lane l gets row row_base + l % 16, k = 32 kk + 8 (l / 16) + 0..7.
-__device__ __forceinline__ bf16x8_t frag_krows(const lds_char_t* tile, int row_base, int kk, int lane) {
-  const int row = row_base + (lane & 15);
-  const int chunk = (kk * 4 + (lane >> 4)) ^ swz_krows(row);
-  return *reinterpret_cast<const LDS_AS bf16x8_t*>(tile + row * 128 + chunk * 16);
-}
-
-// Same fragment from a K-cols tile, for the 16 columns starting at col_base:
-// two ds_read_b64_tr_b16. In each 16-lane block the instruction hands lane i
-// element (i % 4) of the 8 bytes fetched by lane 4 e + i / 4 as its element e;
-// so lane s of the block points at k-row (kb + s / 4), columns 4 (s % 4)..+3,
-// and every lane receives 4 consecutive k of its own column.
-__device__ __forceinline__ bf16x8_t frag_kcols(const lds_char_t* tile, int col_base, int kk, int lane) {
-  const int s = lane & 15;
-  const int col = col_base + 4 * (s & 3);
-  const int chunk = col >> 3;
-  const int sub = (col & 7) * 2;
-  const int k_lo = kk * 32 + (lane >> 4) * 8 + (s >> 2);
-  const int k_hi = k_lo + 4;
-  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (LDS_AS bf16x4_t*)(tile + k_lo * 512 + ((chunk ^ swz_kcols(k_lo)) * 16) + sub));
-  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (LDS_AS bf16x4_t*)(tile + k_hi * 512 + ((chunk ^ swz_kcols(k_hi)) * 16) + sub));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// ------------------------------------------------------------ mainloop
-
-struct GemmShape {
-  int64_t M, N, K;       // C is M x N, contraction over K
-  const void* A;         // A_K: [M, lda] (k contiguous); else [K, lda] (m contiguous)
-  int64_t lda;
-  const void* B;         // B_K: [N, ldb] (k contiguous); else [K, ldb] (n contiguous)
-  int64_t ldb;
-};
-
-// Block -> output tile. Consecutive logical tiles go to one XCD; within the
-// logical order tiles are rastered down groups of kGroupM tile-rows.
-constexpr int kGroupM = 4;
-__device__ __forceinline__ void map_tile(int64_t M, int64_t N, int& tile_m, int& tile_n) {
-  const int tiles_m = int(dceil_div(M, kBM));
-  const int tiles_n = int(N / kBN);
-  const int nb = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + (b / 8) : b;
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (t / per_group) * kGroupM;
-  const int gsz = min(tiles_m - first_m, kGroupM);
-  const int r = t % per_group;
-  tile_m = first_m + r % gsz;
-  tile_n = r / gsz;
-}
-
-template <bool A_K, bool B_K>
-__device__ __forceinline__ void load_stage(lds_char_t* sa, lds_char_t* sb, const GemmShape& p, int64_t m0,
-                                           int64_t n0, int64_t k0, int wave, int lane) {
-  if constexpr (A_K) load_krows(sa, p.A, p.lda, m0, p.M, k0, wave, lane);
-  else load_kcols(sa, p.A, p.lda, k0, p.K, m0, wave, lane);
-  if constexpr (B_K) load_krows(sb, p.B, p.ldb, n0, p.N, k0, wave, lane);
-  else load_kcols(sb, p.B, p.ldb, k0, p.K, n0, wave, lane);
-}
-
-// acc[tm][tn] (lane l, reg e) = C[m0 + 128 wm + 16 tm + l % 16][n0 + 128 wn + 16 tn + 4 (l / 16) + e]
-template <bool A_K, bool B_K>
-__device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
-                                         f32x4_t (&acc)[8][8]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int KT = int(dceil_div(p.K, kBK));
-  constexpr int kStage = (kBM + kBN) * kBK * 2;  // 64 KB
-  load_stage<A_K, B_K>(smem, smem + kBM * kBK * 2, p, m0, n0, 0, wave, lane);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    lds_char_t* sa = smem + (kt & 1) * kStage;
-    lds_char_t* sb = sa + kBM * kBK * 2;
-    if (kt + 1 < KT) {
-      lds_char_t* na = smem + ((kt + 1) & 1) * kStage;
-      load_stage<A_K, B_K>(na, na + kBM * kBK * 2, p, m0, n0, int64_t(kt + 1) * kBK, wave, lane);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[8], bfr[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        af[t] = A_K ? frag_krows(sa, wm * 128 + 16 * t, kk, lane) : frag_kcols(sa, wm * 128 + 16 * t, kk, lane);
-        bfr[t] = B_K ? frag_krows(sb, wn * 128 + 16 * t, kk, lane) : frag_kcols(sb, wn * 128 + 16 * t, kk, lane);
-      }
-#pragma unroll
-      for (int tm = 0; tm < 8; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 8; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[tn], af[tm], acc[tm][tn], 0, 0, 0);
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-}
 
 // ------------------------------------------------------------ epilogues
 // Each epilogue gets the wave's 128 x 128 accumulator block whose first row is
@@ -341,61 +152,57 @@ struct EpiRmsNormBwd {
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
     const float invD = 1.0f / float(D);
-    float gam[8][4], cs[8][4];
-#pragma unroll
-    for (int tn = 0; tn < 8; ++tn) {
-      unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cs[tn][e] = 0.f;
-    }
+    float rr[8], c2[8];
 #pragma unroll
     for (int tm = 0; tm < 8; ++tm) {
       const int64_t i = mb + 16 * tm + li;
       const bool ok = i < M;
-      const float ri = ok ? r[i] : 0.f;
-      const float c2 = ok ? s[i] * ri * ri * invD : 0.f;
+      rr[tm] = ok ? r[i] : 0.f;
+      c2[tm] = ok ? s[i] * rr[tm] * rr[tm] * invD : 0.f;
+    }
 #pragma unroll
-      for (int tn = 0; tn < 8; ++tn) {
-        const int64_t off = i * D + nb + 16 * tn + lj;
+    for (int tn = 0; tn < 8; ++tn) {
+      const int64_t j = nb + 16 * tn + lj;
+      float gam[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
+      unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gam);
+#pragma unroll
+      for (int tm = 0; tm < 8; ++tm) {
+        const int64_t i = mb + 16 * tm + li;
+        const bool ok = i < M;
+        const int64_t off = i * D + j;
         float hv[4] = {0.f, 0.f, 0.f, 0.f};
         if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(h + off), hv);
         float d[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float G = acc[tm][tn][e];
-          d[e] = ri * gam[tn][e] * G - c2 * hv[e];
-          cs[tn][e] += G * ri * hv[e];
+          d[e] = rr[tm] * gam[e] * G - c2[tm] * hv[e];
+          cs[e] += G * rr[tm] * hv[e];
         }
         if (ok) {
           if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(da) + off) = make_float4(d[0], d[1], d[2], d[3]);
           else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(da) + off) = pack4_bf16(d[0], d[1], d[2], d[3]);
         }
       }
-    }
-    // column sums over the 16 lanes sharing l / 16 (they hold the 16 rows of each tile)
-#pragma unroll
-    for (int tn = 0; tn < 8; ++tn)
+      // column sums over the 16 lanes sharing l / 16 (they hold the 16 rows of each tile)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v = cs[tn][e];
+        float v = cs[e];
         v += shfl_xor(v, 1);
         v += shfl_xor(v, 2);
         v += shfl_xor(v, 4);
         v += shfl_xor(v, 8);
-        cs[tn][e] = v;
+        cs[e] = v;
       }
-    if (li == 0 && mb < M) {  // a wave whose rows all lie past M has no Pg row
-      float* dst = Pg + (mb / kWaveTileM) * D + nb + lj;
-#pragma unroll
-      for (int tn = 0; tn < 8; ++tn)
-        *reinterpret_cast<float4*>(dst + 16 * tn) = make_float4(cs[tn][0], cs[tn][1], cs[tn][2], cs[tn][3]);
+      if (li == 0 && mb < M)  // a wave whose rows all lie past M has no Pg row
+        *reinterpret_cast<float4*>(Pg + (mb / kWaveTileM) * D + j) = make_float4(cs[0], cs[1], cs[2], cs[3]);
     }
   }
 };
 
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const Epi epi) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * (kBM + kBN) * kBK * 2];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   int tile_m, tile_n;
   map_tile(p.M, p.N, tile_m, tile_n);
