@@ -48,6 +48,36 @@ def stage_work(M, K0, D, N):
     }
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources the kernels are built from (identifies a counter measurement)."""
+    import hashlib
+    d = os.path.join(ROOT, "transformer_gemm_epilogue_res_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/hbm_traffic_llama3_8b.md (FETCH_SIZE and WRITE_SIZE
+    passes, each scaled by the same counter's reading for a plain copy of known size), or None when that
+    measurement was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if blob.get("source_digest") != kernel_source_digest():
+        return None
+    k = blob.get("kernels", {}).get(kernel)
+    return None if k is None else k["bytes_per_launch"]
+
+
 def cpu_baseline(host, rows, ncols, seed=0):
     """Time the fp64 oracle (as it is) on a sub-batch of sampled rows of the workload."""
     import numpy as np
@@ -93,6 +123,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows in the oracle's timed sample (0 = skip)")
     ap.add_argument("--cpu-cols", type=int, default=64)
     ap.add_argument("--no-unfused", action="store_true", help="skip timing the unfused baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="before timing, run 3 plain device copies of this many bytes (a reference kernel of "
+                         "known traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the chain's kernels run on a single "
@@ -130,6 +163,15 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = L.current_stream(dev)
     names = list(L.FWD_STAGE_NAMES) + list(L.BWD_STAGE_NAMES)
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy: 3 x {args.copy_bytes} bytes read + written")
+        del src, dst
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -177,12 +219,12 @@ def main():
     if dk == "flop":
         ach = damount / (per[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "per_launch": f"{damount / 1e12:.4f} TFLOP", "avg_us": round(per[dom] * 1e3, 1)}
     else:
         ach = damount / (per[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "per_launch": f"{damount / 1e9:.3f} GB", "avg_us": round(per[dom] * 1e3, 1)}
     log(f"[bench] step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
         f"fwd {fwd_ms:.3f} ms, bwd {bwd_ms:.3f} ms")
@@ -233,6 +275,7 @@ def main():
                 "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
         "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
+        "kernel_source_digest": kernel_source_digest(),
     }
     print(json.dumps(rec), flush=True)
 

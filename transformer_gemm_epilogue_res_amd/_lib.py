@@ -14,7 +14,8 @@ from ctypes import POINTER, c_float, c_int, c_int64, c_size_t, c_void_p
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libcoda.so")
+# CODA_LIB may name another build of the library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("CODA_LIB") or os.path.join(PKG, "libcoda.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "coda.h")
 
 CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA_ERR_ARG, CODA_ERR_HIP = range(7)

@@ -195,14 +195,14 @@ def merge(a, b):
     return tuple(x | y for x, y in zip(a2, b2))
 
 
-def device_asm(src=None) -> str:
+def device_asm(src=None, extra_flags=()) -> str:
     here = os.path.dirname(os.path.abspath(__file__))
     src = src or os.path.join(here, "csrc", "coda_kernels.hip")
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
         from .build import FLAGS, HIPCC
         flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
-        subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", out], check=True,
+        subprocess.run([HIPCC, *flags, *extra_flags, "--cuda-device-only", "-S", src, "-o", out], check=True,
                        capture_output=True)
         return open(out).read()
 

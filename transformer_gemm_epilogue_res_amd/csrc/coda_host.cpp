@@ -2,7 +2,7 @@
 // strings. Nothing here calls HIP, so the checks run (and are tested) without a GPU.
 #include <math.h>
 
-#include "../../include/coda.h"
+#include "coda.h"
 #include "coda_internal.h"
 
 using namespace coda;

@@ -10,7 +10,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/coda.h"
+#include "coda.h"
 #include "coda_internal.h"
 #include "gemm_mainloop.hpp"
 

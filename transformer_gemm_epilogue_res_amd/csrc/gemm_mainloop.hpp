@@ -53,7 +53,21 @@ typedef LDS_AS char lds_char_t;
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 64 KB: A tile then B tile
 constexpr int kTileBytes = kBM * kBK * 2;           // 32 KB
 constexpr int kSmemBytes = 2 * kStageBytes;
-constexpr int kBarrierAt = 16;                      // slab-1 MFMA index of the block barrier
+#ifndef CODA_BARRIER_AT
+#define CODA_BARRIER_AT 28
+#endif
+#ifndef CODA_DMA_EVERY
+#define CODA_DMA_EVERY 2
+#endif
+#ifndef CODA_READ_EVERY
+#define CODA_READ_EVERY 2
+#endif
+#ifndef CODA_GROUP_M
+#define CODA_GROUP_M 4
+#endif
+constexpr int kBarrierAt = CODA_BARRIER_AT;  // slab-1 MFMA index of the block barrier
+constexpr int kDmaEvery = CODA_DMA_EVERY;    // slab-0 MFMAs per DMA instruction
+constexpr int kReadEvery = CODA_READ_EVERY;  // slab-0 MFMAs per LDS read of slab 1
 
 // ------------------------------------------------------------ utilities
 
@@ -270,7 +284,7 @@ constexpr int slab_reads() {
 // Block -> output tile. Consecutive logical tiles go to one XCD (the
 // dispatcher deals blocks round-robin over the 8 XCDs); logical tiles are
 // rastered down groups of kGroupM tile-rows.
-constexpr int kGroupM = 4;
+constexpr int kGroupM = CODA_GROUP_M;
 __device__ __forceinline__ void map_tile(int64_t M, int64_t N, int& tile_m, int& tile_n) {
   const int tiles_m = int(dceil_div(M, kBM));
   const int tiles_n = int(N / kBN);
@@ -314,12 +328,13 @@ __device__ __forceinline__ void kstep(f32x4_t (&acc)[8][8], Frag (&a0)[8], Frag 
     constexpr int i = decltype(I)::value;
     if constexpr (FIRST) mfma_16x16x32_first(acc[i / 8][i % 8], b0[i % 8], a0[i / 8]);
     else mfma_16x16x32(acc[i / 8][i % 8], b0[i % 8], a0[i / 8]);
-    if constexpr (NEXT && i % 2 == 0 && i < 32) {
-      constexpr int q = i / 2;  // 0..15: 8 A-tile then 8 B-tile instructions
+    if constexpr (NEXT && i % kDmaEvery == 0 && i / kDmaEvery < 16) {
+      constexpr int q = i / kDmaEvery;  // 0..15: 8 A-tile then 8 B-tile instructions
       if constexpr (q < 8) opa.dma(ra, nxt, q, wave);
       else opb.dma(rb, nxt + kTileBytes, q - 8, wave);
     }
-    if constexpr (i % 2 == 1 && i / 2 < NR) slab_read<A_K, B_K, ST, 1, i / 2>(a1, b1, fa, fb);
+    if constexpr (i % kReadEvery == kReadEvery - 1 && i / kReadEvery < NR)
+      slab_read<A_K, B_K, ST, 1, i / kReadEvery>(a1, b1, fa, fb);
   });
   // ---- slab 1: MFMAs on (a1, b1); barrier; reads of the next step's slab 0
   wait_lgkm<0>();
@@ -340,7 +355,8 @@ template <bool A_K, bool B_K>
 __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
                                          f32x4_t (&acc)[8][8]) {
   static_assert(slab_reads<A_K, B_K>() <= 64 - kBarrierAt - 1, "slab-0 reads must fit after the barrier");
-  static_assert(slab_reads<A_K, B_K>() <= 32, "slab-1 reads must fit in slab 0 (one per odd MFMA)");
+  static_assert(slab_reads<A_K, B_K>() * kReadEvery <= 64, "slab-1 reads must fit in slab 0");
+  static_assert(16 * kDmaEvery <= 64, "the DMA must fit in slab 0");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
