@@ -39,7 +39,7 @@ def stage_work(M, K0, D, N):
     """Per-launch algorithmic work: ('flop', F) for MFMA kernels, ('byte', B) for HBM-bound ones."""
     return {
         "gemm0_residual_ssq": ("flop", 2 * M * K0 * D),
-        "rms_combine": ("byte", M * (D // 128) * 4 + M * 4),
+        "rms_combine": ("byte", M * (D // 64) * 4 + M * 4),
         "gemm1_rowscale": ("flop", 2 * M * D * N),
         "rowstat_s_rg": ("byte", 2 * M * N * 2 + 2 * M * D * 2 + 2 * M * 4),
         "dgrad_rmsnorm_bwd": ("flop", 2 * M * N * D),

@@ -65,7 +65,7 @@ def test_workspace_sizes():
     def a256(v):
         return (v + 255) // 256 * 256
     M, D, N = 300, 512, 768
-    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == a256(M * (D // 128) * 4)
+    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == a256(M * (D // 64) * 4)
     assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD, M, D, N) == 2 * a256(M * D * 2)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)

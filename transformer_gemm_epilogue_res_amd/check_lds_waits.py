@@ -162,6 +162,8 @@ def check_function(name: str, body: str):
                         changed = True
                 if op == "s_branch":
                     state, mf, va = (), {}, {}
+            if op == "s_endpgm":  # nothing falls through past the end of the program
+                state, mf, va = (), {}, {}
         if not changed:
             break
     seen, uniq = set(), []

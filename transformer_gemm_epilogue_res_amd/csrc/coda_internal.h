@@ -7,14 +7,14 @@
 
 namespace coda {
 
-// Block tile of every GEMM: 256 x 256 outputs, K step 64, 4 waves in a 2 x 2
-// grid, each wave owning a 128 x 128 sub-tile.
+// Block tile of every GEMM: 256 x 256 outputs, K step 64, 8 waves in two
+// groups of four; each group owns 128 rows, each wave a 128 x 64 sub-tile.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
 constexpr int kWaveTileM = 128;
-constexpr int kWaveTileN = 128;
-constexpr int kThreads = 256;
+constexpr int kWaveTileN = 64;
+constexpr int kThreads = 512;
 
 // K0, D and N must be multiples of this.
 constexpr int64_t kDimQuantum = 256;

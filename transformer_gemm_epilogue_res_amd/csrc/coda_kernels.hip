@@ -43,7 +43,7 @@ __device__ __forceinline__ void unpack8_bf16(uint4 v, float* o) {
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // ------------------------------------------------------------ epilogues
-// Each epilogue gets the wave's 128 x 128 accumulator block whose first row is
+// Each epilogue gets the wave's 128 x 64 accumulator block whose first row is
 // mb and first column nb. Lane l owns rows mb + 16 tm + l % 16 and columns
 // nb + 16 tn + 4 (l / 16) + {0..3}.
 
@@ -52,14 +52,14 @@ template <bool F32>
 struct EpiStore {
   void* C;
   int64_t ldc, M;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm) {
+    for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
       if (i >= M) continue;
 #pragma unroll
-      for (int tn = 0; tn < 8; ++tn) {
+      for (int tn = 0; tn < kTN; ++tn) {
         const int64_t j = nb + 16 * tn + lj;
         const f32x4_t v = acc[tm][tn];
         if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(C) + i * ldc + j) = make_float4(v[0], v[1], v[2], v[3]);
@@ -70,8 +70,8 @@ struct EpiStore {
 };
 
 // GEMM0 epilogue: h = acc + z (fp32) -> store bf16 h; g = bf16(h * gamma) from
-// the fp32 h; per-row sum of squares of the fp32 h over the wave's 128 columns
-// -> P[i, nb / 128].
+// the fp32 h; per-row sum of squares of the fp32 h over the wave's 64 columns
+// -> P[i, nb / 64].
 struct EpiResidualSsq {
   const uint16_t* z;
   const uint16_t* gamma;
@@ -79,18 +79,18 @@ struct EpiResidualSsq {
   uint16_t* g;
   float* P;
   int64_t M, D, pcols;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
-    float gam[8][4];
+    float gam[kTN][4];
 #pragma unroll
-    for (int tn = 0; tn < 8; ++tn) unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
+    for (int tn = 0; tn < kTN; ++tn) unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm) {
+    for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
       const bool ok = i < M;
       float ssq = 0.f;
 #pragma unroll
-      for (int tn = 0; tn < 8; ++tn) {
+      for (int tn = 0; tn < kTN; ++tn) {
         const int64_t off = i * D + nb + 16 * tn + lj;
         float zz[4] = {0.f, 0.f, 0.f, 0.f};
         if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(z + off), zz);
@@ -106,7 +106,7 @@ struct EpiResidualSsq {
               pack4_bf16(hv[0] * gam[tn][0], hv[1] * gam[tn][1], hv[2] * gam[tn][2], hv[3] * gam[tn][3]);
         }
       }
-      // the 4 lanes l % 16 == li hold the rest of row i's 128 columns
+      // the 4 lanes l % 16 == li hold the rest of row i's 64 columns
       ssq += shfl_xor(ssq, 16);
       ssq += shfl_xor(ssq, 32);
       if (lane < 16 && ok) P[i * pcols + nb / kWaveTileN] = ssq;
@@ -120,15 +120,15 @@ struct EpiRowScale {
   const float* r;
   void* y;
   int64_t M, N;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm) {
+    for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
       if (i >= M) continue;
       const float ri = r[i];
 #pragma unroll
-      for (int tn = 0; tn < 8; ++tn) {
+      for (int tn = 0; tn < kTN; ++tn) {
         const int64_t off = i * N + nb + 16 * tn + lj;
         const f32x4_t v = acc[tm][tn];
         if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(ri * v[0], ri * v[1], ri * v[2], ri * v[3]);
@@ -149,24 +149,24 @@ struct EpiRmsNormBwd {
   void* da;
   float* Pg;
   int64_t M, D;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[8][8], int64_t mb, int64_t nb, int lane) const {
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
     const float invD = 1.0f / float(D);
-    float rr[8], c2[8];
+    float rr[kTM], c2[kTM];
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm) {
+    for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
       const bool ok = i < M;
       rr[tm] = ok ? r[i] : 0.f;
       c2[tm] = ok ? s[i] * rr[tm] * rr[tm] * invD : 0.f;
     }
 #pragma unroll
-    for (int tn = 0; tn < 8; ++tn) {
+    for (int tn = 0; tn < kTN; ++tn) {
       const int64_t j = nb + 16 * tn + lj;
       float gam[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
       unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gam);
 #pragma unroll
-      for (int tm = 0; tm < 8; ++tm) {
+      for (int tm = 0; tm < kTM; ++tm) {
         const int64_t i = mb + 16 * tm + li;
         const bool ok = i < M;
         const int64_t off = i * D + j;
@@ -200,6 +200,9 @@ struct EpiRmsNormBwd {
   }
 };
 
+// The two wave groups run the loop one phase apart (see gemm_mainloop.hpp), so
+// each has its own copy of loop and epilogue; group 0's epilogue overlaps group
+// 1's last MFMAs.
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
@@ -207,10 +210,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const
   int tile_m, tile_n;
   map_tile(p.M, p.N, tile_m, tile_n);
   const int64_t m0 = int64_t(tile_m) * kBM, n0 = int64_t(tile_n) * kBN;
-  f32x4_t acc[8][8];
-  mainloop<A_K, B_K>(p, m0, n0, smem, acc);
-  const int wave = threadIdx.x >> 6;
-  epi(acc, m0 + (wave >> 1) * kWaveTileM, n0 + (wave & 1) * kWaveTileN, threadIdx.x & 63);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nb = n0 + (wave & 3) * kWaveTileN;
+  f32x4_t acc[kTM][kTN];
+  if (wave < 4) {
+    mainloop<A_K, B_K, 0>(p, m0, n0, smem, acc);
+    epi(acc, m0, nb, threadIdx.x & 63);
+  } else {
+    mainloop<A_K, B_K, 1>(p, m0, n0, smem, acc);
+    epi(acc, m0 + kWaveTileM, nb, threadIdx.x & 63);
+  }
 }
 
 // ------------------------------------------------------- small kernels

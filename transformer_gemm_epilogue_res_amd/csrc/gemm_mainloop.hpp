@@ -1,8 +1,28 @@
 // The bf16 MFMA GEMM mainloop shared by every kernel of the chain (gfx950).
 //
-// Block tile 256 x 256, K step 64, 256 threads = 4 waves in a 2 x 2 grid; each
-// wave owns a 128 x 128 sub-tile = 8 x 8 tiles of v_mfma_f32_16x16x32_bf16,
-// i.e. 64 fp32x4 accumulators per lane, kept in AGPRs.
+// Block tile 256 x 256, K step 64, 512 threads = 8 waves in two groups of 4;
+// every SIMD hosts one wave of each group. Group G owns rows 128 G .. 128 G +
+// 127 of the block tile and wave p of a group columns 64 p .. 64 p + 63: a
+// 128 x 64 sub-tile = 8 x 4 tiles of v_mfma_f32_16x16x32_bf16, i.e. 32 fp32x4
+// accumulators per lane, kept in AGPRs.
+//
+// Ping-pong schedule. The loop runs in phases separated by block barriers; in
+// every phase one group multiplies while the other loads:
+//
+//   phase      0      1      2      3     ...   2 KT-1    2 KT
+//   group 0   L(0)   C(0)   L(1)   C(1)   ...   C(KT-1)  (epilogue)
+//   group 1    -     L(0)   C(0)   L(1)   ...   L(KT-1)   C(KT-1)
+//
+// L(k) reads K step k's fragments (both 32-wide k slabs) from LDS into
+// registers; C(k) is the wave's 64 MFMAs on them. Each SIMD thus always has
+// one wave feeding the MFMA pipe while the other one's LDS reads are in flight,
+// and no wave waits on memory while it owns the pipe.
+//
+// Global -> LDS: in phase 2j all 8 waves issue the DMA of K step j+1 into the
+// other LDS stage (group 0 inside L(j), group 1 spread over C(j-1)), 8
+// instructions each; each wave waits for its own DMA before the barrier that
+// ends phase 2j+1. So step j+1 is complete in LDS before phase 2j+2 reads it,
+// and the stage it overwrites was last read in phases 2j-2 and 2j-1.
 //
 // Data path:
 //   * global -> LDS with buffer_load_dwordx4 ... lds (no VGPR round trip), two
@@ -14,18 +34,10 @@
 //     tiles, e.g. the [in, out] weights), XOR-swizzled layouts so each read hits
 //     every one of the 64 banks once per pass.
 //
-// Schedule of one K step (one wave; the MFMA pipe is the bottleneck, 64 MFMAs
-// per 32-wide k slab):
-//   slab 0: 64 MFMAs on fragments already in registers, interleaved with the 16
-//           DMA loads of the next stage and the 24 LDS reads of slab 1;
-//   slab 1: 64 MFMAs; after the first kBarrierAt of them every wave waits for
-//           its own DMA and meets the block barrier (the next stage is then
-//           complete in LDS and every read of the stage about to be refilled
-//           is done), and the remaining MFMAs hide the reads of the next
-//           step's slab-0 fragments.
-// LDS reads are issued from inline asm with their waits written out (so the
-// compiler does not serialise the DMA against them), and scheduling fences
-// after every MFMA keep the interleave in program order.
+// LDS reads, MFMAs, waits and barriers are inline asm, so the compiler can
+// neither serialise the DMA against the reads nor move work across phases; it
+// also knows none of their hazards, which check_lds_waits.py verifies on the
+// generated assembly (LDS waits, MFMA result latency).
 //
 // Operand swap: the N-side fragment is the MFMA's src0 and the M-side fragment
 // src1, so the 16x16 result tile is C^T and lane l, register e of tile (tm, tn)
@@ -50,24 +62,19 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 #define LDS_AS __attribute__((address_space(3)))
 typedef LDS_AS char lds_char_t;
 
+constexpr int kWaves = kThreads / 64;
+constexpr int kTM = kWaveTileM / 16;                // MFMA row tiles per wave
+constexpr int kTN = kWaveTileN / 16;                // MFMA column tiles per wave
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 64 KB: A tile then B tile
 constexpr int kTileBytes = kBM * kBK * 2;           // 32 KB
 constexpr int kSmemBytes = 2 * kStageBytes;
-#ifndef CODA_BARRIER_AT
-#define CODA_BARRIER_AT 28
-#endif
-#ifndef CODA_DMA_EVERY
-#define CODA_DMA_EVERY 2
-#endif
-#ifndef CODA_READ_EVERY
-#define CODA_READ_EVERY 2
-#endif
+constexpr int kSegs = kTileBytes / 1024 / kWaves;   // 1 KB DMA segments per wave per tile
+static_assert(kWaves == 8 && kTM == 8 && kTN == 4, "two groups of four 128 x 64 wave tiles");
+static_assert(2 * kWaveTileM == kBM && 4 * kWaveTileN == kBN, "the two groups cover the block tile");
+
 #ifndef CODA_GROUP_M
 #define CODA_GROUP_M 4
 #endif
-constexpr int kBarrierAt = CODA_BARRIER_AT;  // slab-1 MFMA index of the block barrier
-constexpr int kDmaEvery = CODA_DMA_EVERY;    // slab-0 MFMAs per DMA instruction
-constexpr int kReadEvery = CODA_READ_EVERY;  // slab-0 MFMAs per LDS read of slab 1
 
 // ------------------------------------------------------------ utilities
 
@@ -107,10 +114,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ int swz_krows(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_kcols(int k) { return ((k & 3) << 1) | (k & 8); }
 
-// One operand of the GEMM as the mainloop sees it.
-//   KROWS: tensor [nrows, ld] with k contiguous; the tile is rows r0 .. r0+255.
+// One operand of the GEMM as the mainloop sees it, and this wave's share of
+// its DMA: kSegs of the tile's 32 one-KB segments, segment q * 8 + wave.
+//   KROWS: tensor [nrows, ld] with k contiguous; the tile is rows r0 .. r0+255;
+//          segment s holds rows 8 s .. 8 s + 7.
 //   else : tensor [nk, ld] with the M/N index contiguous; the tile is columns
-//          c0 .. c0+255 of k-rows k0 .. k0+63.
+//          c0 .. c0+255 of k-rows k0 .. k0+63; segment s holds k-rows 2 s, 2 s + 1.
+// Segment q of a wave lies 64 q rows (16 q k-rows) past segment 0 and has the
+// same swizzle, so its per-lane byte offset is voff0 + q * seg_step.
 template <bool KROWS>
 struct Operand {
   const char* base;
@@ -118,7 +129,7 @@ struct Operand {
   int64_t extent; // KROWS: nrows; else nk
   int64_t pos0;   // KROWS: r0; else c0
   int64_t K;      // contraction length
-  uint32_t voff[8];
+  uint32_t voff0, seg_step;
 
   __device__ __forceinline__ void init(const void* b, int64_t ld_, int64_t extent_, int64_t pos0_, int64_t K_,
                                        int wave, int lane) {
@@ -127,18 +138,16 @@ struct Operand {
     extent = extent_;
     pos0 = pos0_;
     K = K_;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int seg = q * 4 + wave;  // this wave's q-th 1 KB segment of the 32 KB tile
-      if constexpr (KROWS) {
-        const int row = seg * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz_krows(row);
-        voff[q] = uint32_t((int64_t(row) * ld + chunk * 8) * 2);
-      } else {
-        const int k = seg * 2 + (lane >> 5);
-        const int chunk = (lane & 31) ^ swz_kcols(k);
-        voff[q] = uint32_t((int64_t(k) * ld + chunk * 8) * 2);
-      }
+    if constexpr (KROWS) {
+      const int row = wave * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz_krows(row);
+      voff0 = uint32_t((int64_t(row) * ld + chunk * 8) * 2);
+      seg_step = uint32_t(kWaves * 8 * ld * 2);
+    } else {
+      const int k = wave * 2 + (lane >> 5);
+      const int chunk = (lane & 31) ^ swz_kcols(k);
+      voff0 = uint32_t((int64_t(k) * ld + chunk * 8) * 2);
+      seg_step = uint32_t(kWaves * 2 * ld * 2);
     }
   }
 
@@ -153,38 +162,10 @@ struct Operand {
     }
   }
 
-  // DMA instruction q (0..7) of this wave into the tile at LDS address dst.
+  // DMA instruction q (0 .. kSegs-1) of this wave into the tile at LDS address dst.
   __device__ __forceinline__ void dma(const __amdgpu_buffer_rsrc_t& rs, lds_char_t* dst, int q, int wave) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (q * 4 + wave) * 1024), 16, voff[q], 0, 0, 0);
-  }
-};
-
-// Per-lane LDS byte addresses of one operand's fragments (both stages).
-//   KROWS: addr[s][kk] for rows wo + l % 16 (tile t adds t * 2048);
-//   else : addr[s][t]  for columns wo + 16 t, k-slab 0 low half (slab kk adds
-//          kk * 16384, the high half adds 2048).
-template <bool KROWS>
-struct FragAddr {
-  uint32_t addr[2][KROWS ? 2 : 8];
-  __device__ __forceinline__ void init(uint32_t tile0, int wo, int lane) {
-    const int s = lane & 15, b = lane >> 4;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const uint32_t tb = tile0 + uint32_t(st * kStageBytes);
-      if constexpr (KROWS) {
-        const int row = wo + s;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          addr[st][kk] = tb + uint32_t(row * 128 + (((kk * 4 + b) ^ swz_krows(row)) * 16));
-      } else {
-        const int k = b * 8 + (s >> 2);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int col = wo + 16 * t + 4 * (s & 3);
-          addr[st][t] = tb + uint32_t(k * 512 + (((col >> 3) ^ swz_kcols(k)) * 16) + (col & 7) * 2);
-        }
-      }
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (q * kWaves + wave) * 1024), 16,
+                                             voff0 + uint32_t(q) * seg_step, 0, 0, 0);
   }
 };
 
@@ -192,6 +173,12 @@ struct FragAddr {
 struct Frag {
   bf16x4_t lo, hi;
 };
+
+// Per-lane LDS byte addresses of one operand's fragments in stage 0 (stage 1
+// is kStageBytes further): NT tiles of 16 rows or columns starting at wo (a
+// multiple of 16 NT).
+template <bool KROWS, int NT>
+struct FragAddr;
 
 template <int OFF>
 __device__ __forceinline__ void ds_read_b128_to(Frag& f, uint32_t addr) {
@@ -206,80 +193,85 @@ __device__ __forceinline__ void ds_read_tr_to(bf16x4_t& d, uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
 }
 
-// The MFMA is inline asm: the "+a" constraint keeps every accumulator in an
-// AGPR for the whole loop and the asm order fixes the interleave. The compiler
-// therefore knows nothing of its hazards; the ones that can arise are handled
-// where they occur: the first k slab writes the accumulators with srcC = 0 (no
-// zeroing for the allocator to merge and move), and the mainloop ends with
-// padding that the last accumulators pass through (no read of an MFMA result
-// before it has landed). check_lds_waits.py verifies this and every LDS wait on
-// the generated assembly.
+// K-rows: addr[kk] for row wo + l % 16; tile t adds t * 2048 bytes.
+template <int NT>
+struct FragAddr<true, NT> {
+  uint32_t addr[2];
+  __device__ __forceinline__ void init(uint32_t tile0, int wo, int lane) {
+    const int s = lane & 15, b = lane >> 4;
+    const int row = wo + s;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) addr[kk] = tile0 + uint32_t(row * 128 + (((kk * 4 + b) ^ swz_krows(row)) * 16));
+  }
+  // Fragment tile T of k slab KK in the stage at byte offset soff.
+  template <int KK, int T>
+  __device__ __forceinline__ void read(Frag& f, uint32_t soff) const {
+    ds_read_b128_to<T * 2048>(f, addr[KK] + soff);
+  }
+};
+
+// K-cols: lane (s, b) = (l % 16, l / 16) reads k-row k = 8 b + s / 4 (low
+// half; the high half is 4 k-rows on, slab 1 is 32 on, both with the same
+// swizzle) at column wo + 16 t + 4 (s % 4): chunk wo / 8 + 2 t + (s % 4) / 2,
+// byte 8 (s % 2) within it. With W = 2 NT chunks per wave span and wo / 8 a
+// multiple of W, the stored chunk is
+//   ((wo / 8) ^ (swz & ~(W-1))) + ((2 t) ^ c),  c = (swz & (W-1)) | (s % 4) / 2.
+template <int NT>
+struct FragAddr<false, NT> {
+  uint32_t addr[NT];
+  __device__ __forceinline__ void init(uint32_t tile0, int wo, int lane) {
+    constexpr int W = 2 * NT;
+    const int s = lane & 15, b = lane >> 4;
+    const int k = b * 8 + (s >> 2);
+    const int swz = swz_kcols(k);
+    const int c = (swz & (W - 1)) | ((s & 3) >> 1);
+    const uint32_t base = tile0 + uint32_t(k * 512 + ((wo >> 3) ^ (swz & ~(W - 1))) * 16 + (s & 1) * 8);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) addr[t] = base + uint32_t(((2 * t) ^ c) * 16);
+  }
+  template <int KK, int T>
+  __device__ __forceinline__ void read(Frag& f, uint32_t soff) const {
+    const uint32_t a = addr[T] + soff;
+    ds_read_tr_to<KK * 16384>(f.lo, a);
+    ds_read_tr_to<KK * 16384 + 2048>(f.hi, a);
+  }
+};
+
+// MFMA as inline asm: "+a" keeps the accumulator in one AGPR for the whole
+// loop and the asm order fixes the schedule. The first K step's first slab
+// writes the accumulators with srcC = 0 (no zeroing for the allocator to merge
+// and move), and the mainloop ends with padding that the last accumulators pass
+// through (no read of an MFMA result before it has landed).
+template <bool FIRST>
 __device__ __forceinline__ void mfma_16x16x32(f32x4_t& c, const Frag& n_side, const Frag& m_side) {
   const bf16x8_t a = __builtin_shufflevector(n_side.lo, n_side.hi, 0, 1, 2, 3, 4, 5, 6, 7);
   const bf16x8_t b = __builtin_shufflevector(m_side.lo, m_side.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  if constexpr (FIRST) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
-// The first k slab: c = A B (accumulator input 0), so the accumulators are
-// defined by MFMAs alone and no zeroing is ever merged with them.
-__device__ __forceinline__ void mfma_16x16x32_first(f32x4_t& c, const Frag& n_side, const Frag& m_side) {
-  const bf16x8_t a = __builtin_shufflevector(n_side.lo, n_side.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  const bf16x8_t b = __builtin_shufflevector(m_side.lo, m_side.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+// Pad past the MFMA result latency. The accumulators of the final 16 MFMAs pass
+// through the padding asm and all the others through an empty asm after it
+// (volatile asm keeps its order), so no read of any accumulator can be placed
+// ahead of the padding.
+__device__ __forceinline__ void mfma_drain(f32x4_t (&acc)[kTM][kTN]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[4][0]), "+a"(acc[4][1]), "+a"(acc[4][2]), "+a"(acc[4][3]), "+a"(acc[5][0]),
+                 "+a"(acc[5][1]), "+a"(acc[5][2]), "+a"(acc[5][3]), "+a"(acc[6][0]), "+a"(acc[6][1]),
+                 "+a"(acc[6][2]), "+a"(acc[6][3]), "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]),
+                 "+a"(acc[7][3]));
+  asm volatile(""
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+                 "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+                 "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+                 "+a"(acc[3][3]));
 }
 
-// End of the mainloop: pad past the MFMA result latency; the accumulators of
-// the final 16 MFMAs pass through the asm, so no read of them can be placed
-// ahead of it.
-__device__ __forceinline__ void mfma_drain(f32x4_t (&acc)[8][8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3]), "+a"(acc[6][4]),
-                 "+a"(acc[6][5]), "+a"(acc[6][6]), "+a"(acc[6][7]), "+a"(acc[7][0]), "+a"(acc[7][1]),
-                 "+a"(acc[7][2]), "+a"(acc[7][3]), "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]),
-                 "+a"(acc[7][7]));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
-}
-
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Number of LDS instructions that read one fragment.
-template <bool KROWS>
-constexpr int reads_per_frag() {
-  return KROWS ? 1 : 2;
-}
-
-// Issue LDS read number R (0 .. 8 * reads_per_frag - 1) of slab KK of stage ST
-// for fragment tile R / reads_per_frag into dst[].
-template <bool KROWS, int ST, int KK, int R>
-__device__ __forceinline__ void frag_read(Frag (&dst)[8], const FragAddr<KROWS>& fa) {
-  if constexpr (KROWS) {
-    ds_read_b128_to<R * 2048>(dst[R], fa.addr[ST][KK]);
-  } else {
-    constexpr int t = R / 2;
-    if constexpr (R % 2 == 0) ds_read_tr_to<KK * 16384>(dst[t].lo, fa.addr[ST][t]);
-    else ds_read_tr_to<KK * 16384 + 2048>(dst[t].hi, fa.addr[ST][t]);
-  }
-}
-
-// The i-th read of a slab: first the N-side fragments, then the M-side ones.
-template <bool A_K, bool B_K, int ST, int KK, int I>
-__device__ __forceinline__ void slab_read(Frag (&a)[8], Frag (&b)[8], const FragAddr<A_K>& fa,
-                                          const FragAddr<B_K>& fb) {
-  constexpr int nb = 8 * reads_per_frag<B_K>();
-  if constexpr (I < nb) frag_read<B_K, ST, KK, I>(b, fb);
-  else frag_read<A_K, ST, KK, I - nb>(a, fa);
-}
-
-template <bool A_K, bool B_K>
-constexpr int slab_reads() {
-  return 8 * reads_per_frag<A_K>() + 8 * reads_per_frag<B_K>();
-}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void prio_high() { asm volatile("s_setprio 1" ::: "memory"); }
+__device__ __forceinline__ void prio_low() { asm volatile("s_setprio 0" ::: "memory"); }
 
 // Block -> output tile. Consecutive logical tiles go to one XCD (the
 // dispatcher deals blocks round-robin over the 8 XCDs); logical tiles are
@@ -307,94 +299,131 @@ struct GemmShape {
   int64_t ldb;
 };
 
-// One K step on stage ST: see the schedule in the header comment. NEXT says
-// whether another K step follows (DMA, barrier and next reads are skipped on
-// the last one).
-template <bool A_K, bool B_K, int ST, bool NEXT, bool FIRST = false>
-__device__ __forceinline__ void kstep(f32x4_t (&acc)[8][8], Frag (&a0)[8], Frag (&b0)[8], Frag (&a1)[8],
-                                      Frag (&b1)[8], const FragAddr<A_K>& fa, const FragAddr<B_K>& fb,
-                                      const Operand<A_K>& opa, const Operand<B_K>& opb, lds_char_t* smem,
-                                      int kt, int wave) {
-  constexpr int NR = slab_reads<A_K, B_K>();
-  lds_char_t* nxt = smem + (ST ^ 1) * kStageBytes;
-  __amdgpu_buffer_rsrc_t ra, rb;
-  if constexpr (NEXT) {
-    ra = opa.rsrc(kt + 1);
-    rb = opb.rsrc(kt + 1);
-  }
-  // ---- slab 0: MFMAs on (a0, b0) (complete: waited for at the end of the
-  // previous step or of the prologue); DMA of the next stage; reads of slab 1
-  sfor<64>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    if constexpr (FIRST) mfma_16x16x32_first(acc[i / 8][i % 8], b0[i % 8], a0[i / 8]);
-    else mfma_16x16x32(acc[i / 8][i % 8], b0[i % 8], a0[i / 8]);
-    if constexpr (NEXT && i % kDmaEvery == 0 && i / kDmaEvery < 16) {
-      constexpr int q = i / kDmaEvery;  // 0..15: 8 A-tile then 8 B-tile instructions
-      if constexpr (q < 8) opa.dma(ra, nxt, q, wave);
-      else opb.dma(rb, nxt + kTileBytes, q - 8, wave);
-    }
-    if constexpr (i % kReadEvery == kReadEvery - 1 && i / kReadEvery < NR)
-      slab_read<A_K, B_K, ST, 1, i / kReadEvery>(a1, b1, fa, fb);
-  });
-  // ---- slab 1: MFMAs on (a1, b1); barrier; reads of the next step's slab 0
-  wait_lgkm<0>();
-  sfor<64>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    mfma_16x16x32(acc[i / 8][i % 8], b1[i % 8], a1[i / 8]);
-    if constexpr (NEXT && i == kBarrierAt) wait_vm_barrier();
-    if constexpr (NEXT && i > kBarrierAt && i - kBarrierAt - 1 < NR)
-      slab_read<A_K, B_K, ST ^ 1, 0, i - kBarrierAt - 1>(a0, b0, fa, fb);
-  });
-  // the next step's slab-0 fragments (issued 20+ MFMAs ago): nothing stays in
-  // flight across the loop back edge or its exit
-  wait_lgkm<0>();
-}
-
-// acc[tm][tn] (lane l, reg e) = C[m0 + 128 wm + 16 tm + l % 16][n0 + 128 wn + 16 tn + 4 (l / 16) + e]
+// One wave's view of the loop.
 template <bool A_K, bool B_K>
-__device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
-                                         f32x4_t (&acc)[8][8]) {
-  static_assert(slab_reads<A_K, B_K>() <= 64 - kBarrierAt - 1, "slab-0 reads must fit after the barrier");
-  static_assert(slab_reads<A_K, B_K>() * kReadEvery <= 64, "slab-1 reads must fit in slab 0");
-  static_assert(16 * kDmaEvery <= 64, "the DMA must fit in slab 0");
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+struct Loop {
   Operand<A_K> opa;
   Operand<B_K> opb;
-  if constexpr (A_K) opa.init(p.A, p.lda, p.M, m0, p.K, wave, lane);
-  else opa.init(p.A, p.lda, p.K, m0, p.K, wave, lane);
-  if constexpr (B_K) opb.init(p.B, p.ldb, p.N, n0, p.K, wave, lane);
-  else opb.init(p.B, p.ldb, p.K, n0, p.K, wave, lane);
-  FragAddr<A_K> fa;
-  FragAddr<B_K> fb;
-  fa.init(lds_u32(smem), wm * 128, lane);
-  fb.init(lds_u32(smem) + kTileBytes, wn * 128, lane);
+  FragAddr<A_K, kTM> fa;
+  FragAddr<B_K, kTN> fb;
+  lds_char_t* smem;
+  int wave;
 
-  // An even number of K steps; a step past K reads zeros (rows past the end of
-  // the operand tensors are out of the descriptors' range) and adds nothing.
-  const int KT = 2 * int(dceil_div(p.K, 2 * kBK));
-  {  // prologue: stage 0 -> LDS, slab-0 fragments -> registers
-    const __amdgpu_buffer_rsrc_t ra = opa.rsrc(0), rb = opb.rsrc(0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      opa.dma(ra, smem, q, wave);
-      opb.dma(rb, smem + kTileBytes, q, wave);
-    }
+  __device__ __forceinline__ void rsrc(int kt, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) const {
+    ra = opa.rsrc(kt);
+    rb = opb.rsrc(kt);
   }
-  wait_vm_barrier();
-  Frag a0[8], b0[8], a1[8], b1[8];
-  sfor<slab_reads<A_K, B_K>()>([&](auto I) { slab_read<A_K, B_K, 0, 0, decltype(I)::value>(a0, b0, fa, fb); });
-  wait_lgkm<0>();
+  // DMA instruction i (0 .. 2 kSegs - 1: the A tile's, then the B tile's) of K step kt.
+  __device__ __forceinline__ void dma(int i, int kt, const __amdgpu_buffer_rsrc_t& ra,
+                                      const __amdgpu_buffer_rsrc_t& rb) const {
+    lds_char_t* dst = smem + (kt & 1) * kStageBytes;
+    if (i < kSegs) opa.dma(ra, dst, i, wave);
+    else opb.dma(rb, dst + kTileBytes, i - kSegs, wave);
+  }
+  __device__ __forceinline__ void dma_all(int kt) const {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    rsrc(kt, ra, rb);
+#pragma unroll
+    for (int i = 0; i < 2 * kSegs; ++i) dma(i, kt, ra, rb);
+  }
+  // L(kt): this wave's fragments of K step kt; N-side first.
+  __device__ __forceinline__ void load(int kt, Frag (&a)[2][kTM], Frag (&b)[2][kTN]) const {
+    const uint32_t st = uint32_t(kt & 1) * kStageBytes;
+    sfor<2>([&](auto KK) {
+      constexpr int kk = decltype(KK)::value;
+      sfor<kTN>([&](auto T) { fb.template read<kk, decltype(T)::value>(b[kk][T], st); });
+      sfor<kTM>([&](auto T) { fa.template read<kk, decltype(T)::value>(a[kk][T], st); });
+    });
+  }
+};
 
-  // Every step has the same body: on the last one the "next stage" DMA lies
-  // past the end of K (its descriptors have no records, it loads zeros) and the
-  // fragments it reads are never used. The first step starts the accumulators.
-  kstep<A_K, B_K, 0, true, true>(acc, a0, b0, a1, b1, fa, fb, opa, opb, smem, 0, wave);
-  kstep<A_K, B_K, 1, true>(acc, a0, b0, a1, b1, fa, fb, opa, opb, smem, 1, wave);
-  for (int kt = 2; kt < KT; kt += 2) {
-    kstep<A_K, B_K, 0, true>(acc, a0, b0, a1, b1, fa, fb, opa, opb, smem, kt, wave);
-    kstep<A_K, B_K, 1, true>(acc, a0, b0, a1, b1, fa, fb, opa, opb, smem, kt + 1, wave);
+// C(k): 64 MFMAs, slab 0 then slab 1, row-tile major; after(I) runs after MFMA I.
+template <bool FIRST, class F>
+__device__ __forceinline__ void compute(f32x4_t (&acc)[kTM][kTN], const Frag (&a)[2][kTM], const Frag (&b)[2][kTN],
+                                        F&& after) {
+  sfor<2 * kTM * kTN>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    constexpr int kk = i / (kTM * kTN), tm = (i / kTN) % kTM, tn = i % kTN;
+    mfma_16x16x32<FIRST && kk == 0>(acc[tm][tn], b[kk][tn], a[kk][tm]);
+    after(I);
+  });
+}
+
+// Group G's side of the loop, for wave 4 G + p:
+//   acc[tm][tn] (lane l, reg e) = C[m0 + 128 G + 16 tm + l % 16][n0 + 64 p + 16 tn + 4 (l / 16) + e].
+// Both groups pass the same number of barriers (1 + 2 KT).
+template <bool A_K, bool B_K, int G>
+__device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
+                                         f32x4_t (&acc)[kTM][kTN]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Loop<A_K, B_K> L;
+  L.smem = smem;
+  L.wave = wave;
+  if constexpr (A_K) L.opa.init(p.A, p.lda, p.M, m0, p.K, wave, lane);
+  else L.opa.init(p.A, p.lda, p.K, m0, p.K, wave, lane);
+  if constexpr (B_K) L.opb.init(p.B, p.ldb, p.N, n0, p.K, wave, lane);
+  else L.opb.init(p.B, p.ldb, p.K, n0, p.K, wave, lane);
+  L.fa.init(lds_u32(smem), G * kWaveTileM, lane);
+  L.fb.init(lds_u32(smem) + kTileBytes, (wave & 3) * kWaveTileN, lane);
+  const int KT = int(dceil_div(p.K, kBK));
+
+  L.dma_all(0);  // prologue: K step 0 -> stage 0, all 8 waves
+  wait_vm0();
+  block_barrier();
+
+  Frag a[2][kTM], b[2][kTN];
+  auto none = [](auto) {};
+  if constexpr (G == 0) {
+    // phase 2k: L(k) and the DMA of step k+1; phase 2k+1: C(k), then wait for that DMA
+    if (1 < KT) L.dma_all(1);
+    L.load(0, a, b);
+    wait_lgkm0();
+    block_barrier();
+    prio_high();
+    compute<true>(acc, a, b, none);
+    prio_low();
+    wait_vm0();
+    block_barrier();
+    for (int k = 1; k < KT; ++k) {
+      if (k + 1 < KT) L.dma_all(k + 1);
+      L.load(k, a, b);
+      wait_lgkm0();
+      block_barrier();
+      prio_high();
+      compute<false>(acc, a, b, none);
+      prio_low();
+      wait_vm0();
+      block_barrier();
+    }
+  } else {
+    // phase 0: DMA of step 1; phase 2k+1: L(k), then wait for the DMA of step
+    // k+1; phase 2k+2: C(k) with the DMA of step k+2 spread over it. That DMA
+    // is issued unconditionally: past the end of K its descriptors have no
+    // records and it writes zeros into the stage L(k) has just finished with
+    // (a branch here would split the accumulators' live ranges).
+    L.dma_all(1);
+    block_barrier();
+    auto step = [&](int k, auto first) {
+      constexpr bool FIRST = decltype(first)::value;
+      L.load(k, a, b);
+      wait_vm0();
+      wait_lgkm0();
+      block_barrier();
+      prio_high();
+      __amdgpu_buffer_rsrc_t ra, rb;
+      L.rsrc(k + 2, ra, rb);
+      compute<FIRST>(acc, a, b, [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int every = 2 * kTM * kTN / (2 * kSegs);
+        if constexpr (i % every == every / 2) L.dma(i / every, k + 2, ra, rb);
+      });
+      prio_low();
+      if (k + 1 < KT) block_barrier();
+    };
+    step(0, std::true_type{});
+    for (int k = 1; k < KT; ++k) step(k, std::false_type{});
+    wait_vm0();  // the last zero-fill DMA lands before the block can end
   }
   mfma_drain(acc);
 }
