@@ -7,8 +7,9 @@ reports:
 
 1. any instruction that reads (or non-LDS-writes) a VGPR/AGPR whose LDS load is
    still outstanding, i.e. not yet retired by an `s_waitcnt lgkmcnt(N)` (LDS
-   loads of one wave return in order; SMEM loads also count in lgkmcnt and are
-   tracked the same way);
+   operations of one wave complete in order and every one of them, writes
+   included, counts; SMEM loads also count in lgkmcnt and are tracked the same
+   way);
 2. any non-MFMA instruction that touches a register an MFMA wrote fewer than
    MFMA_RESULT_STATES wait states earlier (s_nop N counts N+1, every other
    instruction 1), and any MFMA that reads as accumulator input a register a
@@ -130,6 +131,8 @@ def check_function(name: str, body: str):
                 bad = used & pending
                 if bad:
                     problems.append((i, ins, "use of a register with a pending LDS/SMEM load", sorted(bad)))
+                if op.startswith("ds_"):  # LDS writes count in lgkmcnt too (no register returns)
+                    state = state + (frozenset(),)
             if op.startswith("v_mfma"):
                 srcc = regs_of(ops[3]) if len(ops) > 3 else set()
                 hot = {r for r in srcc if va.get(r, 99) < VALU_TO_MFMA_STATES}

@@ -42,30 +42,80 @@ __device__ __forceinline__ void unpack8_bf16(uint4 v, float* o) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// ------------------------------------------------------ coalesced stores
+//
+// In the MFMA layout a lane holds four adjacent columns of one row per tile, so
+// a direct bf16 store writes 16 rows x 32 bytes per instruction. Instead each
+// wave stages its 128 x 64 bf16 block in its own 16 KB of LDS (the mainloop's
+// stages are free once the last barrier is passed) and then stores whole
+// 128-byte rows, eight lanes x 16 bytes each. The 16-byte chunks of a staged
+// row are XOR-swizzled by the row index, so both passes spread over all 64
+// banks. fp32 outputs are stored directly (16 bytes per lane).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct StageBf16 {
+  lds_char_t* base;
+  int lane;
+  // The four values of tile (tm, tn) of this lane.
+  __device__ __forceinline__ void put(int tm, int tn, const f32x4_t& v) const {
+    const int li = lane & 15, lg = lane >> 4;
+    const int row = 16 * tm + li, c = 2 * tn + (lg >> 1);
+    const uint2 p = pack4_bf16(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<LDS_AS u32x2_t*>(base + row * 128 + ((c ^ (row & 7)) << 4) + (lg & 1) * 8) = u32x2_t{p.x, p.y};
+  }
+  // Rows mb .. mb+127 (those below M), columns nb .. nb+63 of out[., ldc].
+  __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
+    const int c = lane & 7;
+#pragma unroll
+    for (int q = 0; q < kWaveTileM / 8; ++q) {
+      const int row = 8 * q + (lane >> 3);
+      const u32x4_t v = *reinterpret_cast<const LDS_AS u32x4_t*>(base + row * 128 + ((c ^ (row & 7)) << 4));
+      const int64_t i = mb + row;
+      if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldc + nb + 8 * c) = v;
+    }
+  }
+};
+
+// out[rows of tile tm, columns of tile tn] for this lane, fp32 (16 bytes per lane).
+__device__ __forceinline__ void store_f32(float* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M, int lane,
+                                          int tm, int tn, const f32x4_t& v) {
+  const int64_t i = mb + 16 * tm + (lane & 15);
+  if (i < M) *reinterpret_cast<float4*>(out + i * ldc + nb + 16 * tn + 4 * (lane >> 4)) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Writes the wave's block val(tm, tn) as bf16 (staged) or fp32 (direct).
+template <bool F32, class V>
+__device__ __forceinline__ void store_block(lds_char_t* stage, int lane, void* out, int64_t ldc, int64_t mb,
+                                            int64_t nb, int64_t M, V&& val) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn) store_f32(static_cast<float*>(out), ldc, mb, nb, M, lane, tm, tn, val(tm, tn));
+  } else {
+    const StageBf16 st{stage, lane};
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn) st.put(tm, tn, val(tm, tn));
+    st.flush(static_cast<uint16_t*>(out), ldc, mb, nb, M);
+  }
+}
+
 // ------------------------------------------------------------ epilogues
 // Each epilogue gets the wave's 128 x 64 accumulator block whose first row is
-// mb and first column nb. Lane l owns rows mb + 16 tm + l % 16 and columns
-// nb + 16 tn + 4 (l / 16) + {0..3}.
+// mb and first column nb, and the wave's LDS staging area. Lane l owns rows
+// mb + 16 tm + l % 16 and columns nb + 16 tn + 4 (l / 16) + {0..3}.
 
 // Plain store C = acc (bf16 or fp32).
 template <bool F32>
 struct EpiStore {
   void* C;
   int64_t ldc, M;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
-    const int li = lane & 15, lj = 4 * (lane >> 4);
-#pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      if (i >= M) continue;
-#pragma unroll
-      for (int tn = 0; tn < kTN; ++tn) {
-        const int64_t j = nb + 16 * tn + lj;
-        const f32x4_t v = acc[tm][tn];
-        if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(C) + i * ldc + j) = make_float4(v[0], v[1], v[2], v[3]);
-        else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + i * ldc + j) = pack4_bf16(v[0], v[1], v[2], v[3]);
-      }
-    }
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
+    store_block<F32>(stage, lane, C, ldc, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
   }
 };
 
@@ -79,11 +129,13 @@ struct EpiResidualSsq {
   uint16_t* g;
   float* P;
   int64_t M, D, pcols;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
     float gam[kTN][4];
 #pragma unroll
     for (int tn = 0; tn < kTN; ++tn) unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
+    // h = acc + z in place, and the row sums of squares
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
@@ -91,19 +143,12 @@ struct EpiResidualSsq {
       float ssq = 0.f;
 #pragma unroll
       for (int tn = 0; tn < kTN; ++tn) {
-        const int64_t off = i * D + nb + 16 * tn + lj;
         float zz[4] = {0.f, 0.f, 0.f, 0.f};
-        if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(z + off), zz);
-        float hv[4];
+        if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(z + i * D + nb + 16 * tn + lj), zz);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hv[e] = acc[tm][tn][e] + zz[e];
-          ssq += hv[e] * hv[e];
-        }
-        if (ok) {
-          *reinterpret_cast<uint2*>(h + off) = pack4_bf16(hv[0], hv[1], hv[2], hv[3]);
-          *reinterpret_cast<uint2*>(g + off) =
-              pack4_bf16(hv[0] * gam[tn][0], hv[1] * gam[tn][1], hv[2] * gam[tn][2], hv[3] * gam[tn][3]);
+          acc[tm][tn][e] += zz[e];
+          ssq += acc[tm][tn][e] * acc[tm][tn][e];
         }
       }
       // the 4 lanes l % 16 == li hold the rest of row i's 64 columns
@@ -111,6 +156,13 @@ struct EpiResidualSsq {
       ssq += shfl_xor(ssq, 32);
       if (lane < 16 && ok) P[i * pcols + nb / kWaveTileN] = ssq;
     }
+    store_block<false>(stage, lane, h, D, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
+    store_block<false>(stage, lane, g, D, mb, nb, M, [&](int tm, int tn) {
+      f32x4_t v = acc[tm][tn];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= gam[tn][e];
+      return v;
+    });
   }
 };
 
@@ -120,21 +172,21 @@ struct EpiRowScale {
   const float* r;
   void* y;
   int64_t M, N;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
-    const int li = lane & 15, lj = 4 * (lane >> 4);
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
+    const int li = lane & 15;
+    float rr[kTM];
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
-      if (i >= M) continue;
-      const float ri = r[i];
-#pragma unroll
-      for (int tn = 0; tn < kTN; ++tn) {
-        const int64_t off = i * N + nb + 16 * tn + lj;
-        const f32x4_t v = acc[tm][tn];
-        if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(ri * v[0], ri * v[1], ri * v[2], ri * v[3]);
-        else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) = pack4_bf16(ri * v[0], ri * v[1], ri * v[2], ri * v[3]);
-      }
+      rr[tm] = i < M ? r[i] : 0.f;
     }
+    store_block<F32>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
+      f32x4_t v = acc[tm][tn];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= rr[tm];
+      return v;
+    });
   }
 };
 
@@ -149,7 +201,8 @@ struct EpiRmsNormBwd {
   void* da;
   float* Pg;
   int64_t M, D;
-  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane) const {
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
     const float invD = 1.0f / float(D);
     float rr[kTM], c2[kTM];
@@ -160,6 +213,8 @@ struct EpiRmsNormBwd {
       rr[tm] = ok ? r[i] : 0.f;
       c2[tm] = ok ? s[i] * rr[tm] * rr[tm] * invD : 0.f;
     }
+    const StageBf16 st{stage, lane};
+    // da tile by tile, and the dgamma column partials
 #pragma unroll
     for (int tn = 0; tn < kTN; ++tn) {
       const int64_t j = nb + 16 * tn + lj;
@@ -168,21 +223,17 @@ struct EpiRmsNormBwd {
 #pragma unroll
       for (int tm = 0; tm < kTM; ++tm) {
         const int64_t i = mb + 16 * tm + li;
-        const bool ok = i < M;
-        const int64_t off = i * D + j;
         float hv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(h + off), hv);
-        float d[4];
+        if (i < M) unpack4_bf16(*reinterpret_cast<const uint2*>(h + i * D + j), hv);
+        f32x4_t d;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float G = acc[tm][tn][e];
-          d[e] = rr[tm] * gam[e] * G - c2[tm] * hv[e];
           cs[e] += G * rr[tm] * hv[e];
+          d[e] = rr[tm] * gam[e] * G - c2[tm] * hv[e];
         }
-        if (ok) {
-          if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(da) + off) = make_float4(d[0], d[1], d[2], d[3]);
-          else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(da) + off) = pack4_bf16(d[0], d[1], d[2], d[3]);
-        }
+        if constexpr (F32) store_f32(static_cast<float*>(da), D, mb, nb, M, lane, tm, tn, d);
+        else st.put(tm, tn, d);
       }
       // column sums over the 16 lanes sharing l / 16 (they hold the 16 rows of each tile)
 #pragma unroll
@@ -197,12 +248,10 @@ struct EpiRmsNormBwd {
       if (li == 0 && mb < M)  // a wave whose rows all lie past M has no Pg row
         *reinterpret_cast<float4*>(Pg + (mb / kWaveTileM) * D + j) = make_float4(cs[0], cs[1], cs[2], cs[3]);
     }
+    if constexpr (!F32) st.flush(static_cast<uint16_t*>(da), D, mb, nb, M);
   }
 };
 
-// The two wave groups run the loop one phase apart (see gemm_mainloop.hpp), so
-// each has its own copy of loop and epilogue; group 0's epilogue overlaps group
-// 1's last MFMAs.
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
@@ -215,10 +264,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const
   f32x4_t acc[kTM][kTN];
   if (wave < 4) {
     mainloop<A_K, B_K, 0>(p, m0, n0, smem, acc);
-    epi(acc, m0, nb, threadIdx.x & 63);
+    epi(acc, m0, nb, threadIdx.x & 63, smem + wave * kEpiWaveBytes);
   } else {
     mainloop<A_K, B_K, 1>(p, m0, n0, smem, acc);
-    epi(acc, m0 + kWaveTileM, nb, threadIdx.x & 63);
+    epi(acc, m0 + kWaveTileM, nb, threadIdx.x & 63, smem + wave * kEpiWaveBytes);
   }
 }
 

@@ -68,6 +68,7 @@ constexpr int kTN = kWaveTileN / 16;                // MFMA column tiles per wav
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 64 KB: A tile then B tile
 constexpr int kTileBytes = kBM * kBK * 2;           // 32 KB
 constexpr int kSmemBytes = 2 * kStageBytes;
+constexpr int kEpiWaveBytes = kSmemBytes / kWaves;  // per-wave LDS staging of the epilogue (reuses the stages)
 constexpr int kSegs = kTileBytes / 1024 / kWaves;   // 1 KB DMA segments per wave per tile
 static_assert(kWaves == 8 && kTM == 8 && kTN == 4, "two groups of four 128 x 64 wave tiles");
 static_assert(2 * kWaveTileM == kBM && 4 * kWaveTileN == kBN, "the two groups cover the block tile");
@@ -398,11 +399,11 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
     }
   } else {
     // phase 0: DMA of step 1; phase 2k+1: L(k), then wait for the DMA of step
-    // k+1; phase 2k+2: C(k) with the DMA of step k+2 spread over it. That DMA
-    // is issued unconditionally: past the end of K its descriptors have no
-    // records and it writes zeros into the stage L(k) has just finished with
-    // (a branch here would split the accumulators' live ranges).
-    L.dma_all(1);
+    // k+1; phase 2k+2: C(k) with the DMA of step k+2 spread over it (each
+    // instruction under its own uniform branch, so the MFMA sequence is not
+    // duplicated). After the last barrier no wave touches the LDS stages
+    // again, so the epilogues may reuse them.
+    if (1 < KT) L.dma_all(1);
     block_barrier();
     auto step = [&](int k, auto first) {
       constexpr bool FIRST = decltype(first)::value;
@@ -411,19 +412,21 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
       wait_lgkm0();
       block_barrier();
       prio_high();
+      const bool more = k + 2 < KT;
       __amdgpu_buffer_rsrc_t ra, rb;
       L.rsrc(k + 2, ra, rb);
       compute<FIRST>(acc, a, b, [&](auto I) {
         constexpr int i = decltype(I)::value;
         constexpr int every = 2 * kTM * kTN / (2 * kSegs);
-        if constexpr (i % every == every / 2) L.dma(i / every, k + 2, ra, rb);
+        if constexpr (i % every == every / 2) {
+          if (more) L.dma(i / every, k + 2, ra, rb);
+        }
       });
       prio_low();
       if (k + 1 < KT) block_barrier();
     };
     step(0, std::true_type{});
     for (int k = 1; k < KT; ++k) step(k, std::false_type{});
-    wait_vm0();  // the last zero-fill DMA lands before the block can end
   }
   mfma_drain(acc);
 }
