@@ -18,15 +18,21 @@
 // one wave feeding the MFMA pipe while the other one's LDS reads are in flight,
 // and no wave waits on memory while it owns the pipe.
 //
-// Global -> LDS: in phase 2j all 8 waves issue the DMA of K step j+1 into the
-// other LDS stage (group 0 inside L(j), group 1 spread over C(j-1)), 8
-// instructions each; each wave waits for its own DMA before the barrier that
-// ends phase 2j+1. So step j+1 is complete in LDS before phase 2j+2 reads it,
-// and the stage it overwrites was last read in phases 2j-2 and 2j-1.
+// Global -> LDS. The A tiles of the K steps rotate through 3 LDS slots and the
+// B tiles through 2 (5 x 32 KB = all 160 KB of a CU's LDS). Group 0 loads the B
+// tiles and group 1 the A tiles, each only in its L phases, so no DMA
+// instruction ever waits for a memory queue in the middle of an MFMA phase:
+//   * B(j+1) is issued at the start of phase 2j (group 0's L(j)) into the slot
+//     B(j-1) left, and group 0 waits for it at the end of phase 2j+1;
+//   * A(j+2) is issued in phase 2j+1 (group 1's L(j)) into the slot A(j-1)
+//     left, and group 1 waits for it at the end of phase 2j+3.
+// Each wait precedes a barrier, so a tile is complete in LDS before the phase
+// that first reads it, and a slot is refilled only after both groups' reads of
+// its previous tile (A(j-1) and B(j-1) are last read in phase 2j-1).
 //
 // Data path:
-//   * global -> LDS with buffer_load_dwordx4 ... lds (no VGPR round trip), two
-//     64 KB stages; the buffer descriptor is rebased on every K step and its
+//   * global -> LDS with buffer_load_dwordx4 ... lds (no VGPR round trip); the
+//     buffer descriptor is rebased on every K step and its
 //     record count is the tensor's remaining bytes, so rows past the end (the
 //     ragged last row tile, or a ragged K = M in the weight gradient) read as 0;
 //   * LDS -> VGPR: ds_read_b128 for operands whose k is contiguous ("K-rows"
@@ -63,15 +69,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef LDS_AS char lds_char_t;
 
 constexpr int kWaves = kThreads / 64;
-constexpr int kTM = kWaveTileM / 16;                // MFMA row tiles per wave
-constexpr int kTN = kWaveTileN / 16;                // MFMA column tiles per wave
-constexpr int kStageBytes = (kBM + kBN) * kBK * 2;  // 64 KB: A tile then B tile
-constexpr int kTileBytes = kBM * kBK * 2;           // 32 KB
-constexpr int kSmemBytes = 2 * kStageBytes;
-constexpr int kEpiWaveBytes = kSmemBytes / kWaves;  // per-wave LDS staging of the epilogue (reuses the stages)
-constexpr int kSegs = kTileBytes / 1024 / kWaves;   // 1 KB DMA segments per wave per tile
+constexpr int kTM = kWaveTileM / 16;               // MFMA row tiles per wave
+constexpr int kTN = kWaveTileN / 16;               // MFMA column tiles per wave
+constexpr int kTileBytes = kBM * kBK * 2;          // 32 KB: one operand tile of one K step
+constexpr int kASlots = 3, kBSlots = 2;            // LDS ring slots of the A and B tiles
+constexpr int kBBase = kASlots * kTileBytes;       // B slots follow the A slots
+constexpr int kSmemBytes = (kASlots + kBSlots) * kTileBytes;  // 160 KB, all of a CU's LDS
+constexpr int kEpiWaveBytes = 16384;               // per-wave LDS staging of the epilogue (reuses the slots)
+constexpr int kDmaWaves = 4;                       // one wave group loads each operand
+constexpr int kSegs = kTileBytes / 1024 / kDmaWaves;  // 1 KB DMA segments per wave per tile
 static_assert(kWaves == 8 && kTM == 8 && kTN == 4, "two groups of four 128 x 64 wave tiles");
 static_assert(2 * kWaveTileM == kBM && 4 * kWaveTileN == kBN, "the two groups cover the block tile");
+static_assert(kWaves * kEpiWaveBytes <= kSmemBytes, "epilogue staging fits in the slots");
 
 #ifndef CODA_GROUP_M
 #define CODA_GROUP_M 4
@@ -115,14 +124,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ int swz_krows(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_kcols(int k) { return ((k & 3) << 1) | (k & 8); }
 
-// One operand of the GEMM as the mainloop sees it, and this wave's share of
-// its DMA: kSegs of the tile's 32 one-KB segments, segment q * 8 + wave.
+// One operand of the GEMM as the mainloop sees it, and a loading wave's share
+// of its DMA: kSegs of the tile's 32 one-KB segments, segment q * 4 + w for
+// wave w of the group that loads this operand.
 //   KROWS: tensor [nrows, ld] with k contiguous; the tile is rows r0 .. r0+255;
 //          segment s holds rows 8 s .. 8 s + 7.
 //   else : tensor [nk, ld] with the M/N index contiguous; the tile is columns
 //          c0 .. c0+255 of k-rows k0 .. k0+63; segment s holds k-rows 2 s, 2 s + 1.
-// Segment q of a wave lies 64 q rows (16 q k-rows) past segment 0 and has the
-// same swizzle, so its per-lane byte offset is voff0 + q * seg_step.
+// Segment q of a wave lies 32 q rows (8 q k-rows) past segment 0. A K-rows
+// segment has the same swizzle for every q; a K-cols segment's swizzle has bit
+// 3 = (k & 8) = (q & 1) << 3, so odd and even q keep their own base offset:
+// the per-lane byte offset is voff[q & 1] + (q >> 1) * pair_step.
 template <bool KROWS>
 struct Operand {
   const char* base;
@@ -130,7 +142,7 @@ struct Operand {
   int64_t extent; // KROWS: nrows; else nk
   int64_t pos0;   // KROWS: r0; else c0
   int64_t K;      // contraction length
-  uint32_t voff0, seg_step;
+  uint32_t voff[2], pair_step;
 
   __device__ __forceinline__ void init(const void* b, int64_t ld_, int64_t extent_, int64_t pos0_, int64_t K_,
                                        int wave, int lane) {
@@ -139,17 +151,19 @@ struct Operand {
     extent = extent_;
     pos0 = pos0_;
     K = K_;
-    if constexpr (KROWS) {
-      const int row = wave * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ swz_krows(row);
-      voff0 = uint32_t((int64_t(row) * ld + chunk * 8) * 2);
-      seg_step = uint32_t(kWaves * 8 * ld * 2);
-    } else {
-      const int k = wave * 2 + (lane >> 5);
-      const int chunk = (lane & 31) ^ swz_kcols(k);
-      voff0 = uint32_t((int64_t(k) * ld + chunk * 8) * 2);
-      seg_step = uint32_t(kWaves * 2 * ld * 2);
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      if constexpr (KROWS) {
+        const int row = odd * kDmaWaves * 8 + wave * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz_krows(row);
+        voff[odd] = uint32_t((int64_t(row) * ld + chunk * 8) * 2);
+      } else {
+        const int k = odd * kDmaWaves * 2 + wave * 2 + (lane >> 5);
+        const int chunk = (lane & 31) ^ swz_kcols(k);
+        voff[odd] = uint32_t((int64_t(k) * ld + chunk * 8) * 2);
+      }
     }
+    pair_step = uint32_t((KROWS ? 2 * kDmaWaves * 8 : 2 * kDmaWaves * 2) * ld * 2);
   }
 
   // Descriptor of K step kt's tile. A K-rows step at or past K gets no records
@@ -163,10 +177,10 @@ struct Operand {
     }
   }
 
-  // DMA instruction q (0 .. kSegs-1) of this wave into the tile at LDS address dst.
-  __device__ __forceinline__ void dma(const __amdgpu_buffer_rsrc_t& rs, lds_char_t* dst, int q, int wave) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (q * kWaves + wave) * 1024), 16,
-                                             voff0 + uint32_t(q) * seg_step, 0, 0, 0);
+  // DMA instruction q (0 .. kSegs-1) of loading wave w into the tile at LDS address dst.
+  __device__ __forceinline__ void dma(const __amdgpu_buffer_rsrc_t& rs, lds_char_t* dst, int q, int w) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (q * kDmaWaves + w) * 1024), 16,
+                                             voff[q & 1] + uint32_t(q >> 1) * pair_step, 0, 0, 0);
   }
 };
 
@@ -175,9 +189,9 @@ struct Frag {
   bf16x4_t lo, hi;
 };
 
-// Per-lane LDS byte addresses of one operand's fragments in stage 0 (stage 1
-// is kStageBytes further): NT tiles of 16 rows or columns starting at wo (a
-// multiple of 16 NT).
+// Per-lane LDS byte addresses of one operand's fragments in its first ring
+// slot (the others are whole tiles further): NT tiles of 16 rows or columns
+// starting at wo (a multiple of 16 NT).
 template <bool KROWS, int NT>
 struct FragAddr;
 
@@ -270,6 +284,8 @@ __device__ __forceinline__ void mfma_drain(f32x4_t (&acc)[kTM][kTN]) {
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void prio_high() { asm volatile("s_setprio 1" ::: "memory"); }
 __device__ __forceinline__ void prio_low() { asm volatile("s_setprio 0" ::: "memory"); }
@@ -300,7 +316,8 @@ struct GemmShape {
   int64_t ldb;
 };
 
-// One wave's view of the loop.
+// One wave's view of the loop. The A tile of K step s lives in A slot s % 3,
+// the B tile in B slot s % 2.
 template <bool A_K, bool B_K>
 struct Loop {
   Operand<A_K> opa;
@@ -308,32 +325,28 @@ struct Loop {
   FragAddr<A_K, kTM> fa;
   FragAddr<B_K, kTN> fb;
   lds_char_t* smem;
-  int wave;
+  int w4;  // wave index within its group
 
-  __device__ __forceinline__ void rsrc(int kt, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) const {
-    ra = opa.rsrc(kt);
-    rb = opb.rsrc(kt);
-  }
-  // DMA instruction i (0 .. 2 kSegs - 1: the A tile's, then the B tile's) of K step kt.
-  __device__ __forceinline__ void dma(int i, int kt, const __amdgpu_buffer_rsrc_t& ra,
-                                      const __amdgpu_buffer_rsrc_t& rb) const {
-    lds_char_t* dst = smem + (kt & 1) * kStageBytes;
-    if (i < kSegs) opa.dma(ra, dst, i, wave);
-    else opb.dma(rb, dst + kTileBytes, i - kSegs, wave);
-  }
-  __device__ __forceinline__ void dma_all(int kt) const {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    rsrc(kt, ra, rb);
+  // All of this wave's DMA of the A (group 1) or B (group 0) tile of K step s.
+  __device__ __forceinline__ void dma_a(int s) const {
+    const __amdgpu_buffer_rsrc_t r = opa.rsrc(s);
+    lds_char_t* dst = smem + (s % kASlots) * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 2 * kSegs; ++i) dma(i, kt, ra, rb);
+    for (int q = 0; q < kSegs; ++q) opa.dma(r, dst, q, w4);
   }
-  // L(kt): this wave's fragments of K step kt; N-side first.
-  __device__ __forceinline__ void load(int kt, Frag (&a)[2][kTM], Frag (&b)[2][kTN]) const {
-    const uint32_t st = uint32_t(kt & 1) * kStageBytes;
+  __device__ __forceinline__ void dma_b(int s) const {
+    const __amdgpu_buffer_rsrc_t r = opb.rsrc(s);
+    lds_char_t* dst = smem + kBBase + (s & 1) * kTileBytes;
+#pragma unroll
+    for (int q = 0; q < kSegs; ++q) opb.dma(r, dst, q, w4);
+  }
+  // L(s): this wave's fragments of K step s; N-side first.
+  __device__ __forceinline__ void load(int s, Frag (&a)[2][kTM], Frag (&b)[2][kTN]) const {
+    const uint32_t sa = uint32_t(s % kASlots) * kTileBytes, sb = uint32_t(s & 1) * kTileBytes;
     sfor<2>([&](auto KK) {
       constexpr int kk = decltype(KK)::value;
-      sfor<kTN>([&](auto T) { fb.template read<kk, decltype(T)::value>(b[kk][T], st); });
-      sfor<kTM>([&](auto T) { fa.template read<kk, decltype(T)::value>(a[kk][T], st); });
+      sfor<kTN>([&](auto T) { fb.template read<kk, decltype(T)::value>(b[kk][T], sb); });
+      sfor<kTM>([&](auto T) { fa.template read<kk, decltype(T)::value>(a[kk][T], sa); });
     });
   }
 };
@@ -360,68 +373,54 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Loop<A_K, B_K> L;
   L.smem = smem;
-  L.wave = wave;
-  if constexpr (A_K) L.opa.init(p.A, p.lda, p.M, m0, p.K, wave, lane);
-  else L.opa.init(p.A, p.lda, p.K, m0, p.K, wave, lane);
-  if constexpr (B_K) L.opb.init(p.B, p.ldb, p.N, n0, p.K, wave, lane);
-  else L.opb.init(p.B, p.ldb, p.K, n0, p.K, wave, lane);
+  L.w4 = wave & 3;
+  if constexpr (A_K) L.opa.init(p.A, p.lda, p.M, m0, p.K, L.w4, lane);
+  else L.opa.init(p.A, p.lda, p.K, m0, p.K, L.w4, lane);
+  if constexpr (B_K) L.opb.init(p.B, p.ldb, p.N, n0, p.K, L.w4, lane);
+  else L.opb.init(p.B, p.ldb, p.K, n0, p.K, L.w4, lane);
   L.fa.init(lds_u32(smem), G * kWaveTileM, lane);
-  L.fb.init(lds_u32(smem) + kTileBytes, (wave & 3) * kWaveTileN, lane);
+  L.fb.init(lds_u32(smem) + kBBase, L.w4 * kWaveTileN, lane);
   const int KT = int(dceil_div(p.K, kBK));
-
-  L.dma_all(0);  // prologue: K step 0 -> stage 0, all 8 waves
-  wait_vm0();
-  block_barrier();
 
   Frag a[2][kTM], b[2][kTN];
   auto none = [](auto) {};
   if constexpr (G == 0) {
-    // phase 2k: L(k) and the DMA of step k+1; phase 2k+1: C(k), then wait for that DMA
-    if (1 < KT) L.dma_all(1);
-    L.load(0, a, b);
-    wait_lgkm0();
-    block_barrier();
-    prio_high();
-    compute<true>(acc, a, b, none);
-    prio_low();
+    // prologue: B(0). Phase 2k: the DMA of B(k+1), then L(k); phase 2k+1:
+    // C(k), then wait for B(k+1).
+    L.dma_b(0);
     wait_vm0();
     block_barrier();
-    for (int k = 1; k < KT; ++k) {
-      if (k + 1 < KT) L.dma_all(k + 1);
+    auto step = [&](int k, auto first) {
+      if (k + 1 < KT) L.dma_b(k + 1);
       L.load(k, a, b);
       wait_lgkm0();
       block_barrier();
       prio_high();
-      compute<false>(acc, a, b, none);
+      compute<decltype(first)::value>(acc, a, b, none);
       prio_low();
       wait_vm0();
       block_barrier();
-    }
+    };
+    step(0, std::true_type{});
+    for (int k = 1; k < KT; ++k) step(k, std::false_type{});
   } else {
-    // phase 0: DMA of step 1; phase 2k+1: L(k), then wait for the DMA of step
-    // k+1; phase 2k+2: C(k) with the DMA of step k+2 spread over it (each
-    // instruction under its own uniform branch, so the MFMA sequence is not
-    // duplicated). After the last barrier no wave touches the LDS stages
-    // again, so the epilogues may reuse them.
-    if (1 < KT) L.dma_all(1);
+    // prologue: A(0) and A(1). Phase 0: nothing; phase 2k+1: the DMA of
+    // A(k+2), then L(k), then wait for A(k+1); phase 2k+2: C(k).
+    L.dma_a(0);
+    if (1 < KT) L.dma_a(1);
+    wait_vm0();
+    block_barrier();
     block_barrier();
     auto step = [&](int k, auto first) {
-      constexpr bool FIRST = decltype(first)::value;
+      const bool more = k + 2 < KT;
+      if (more) L.dma_a(k + 2);
       L.load(k, a, b);
-      wait_vm0();
+      if (more) wait_vm<kSegs>();
+      else wait_vm0();
       wait_lgkm0();
       block_barrier();
       prio_high();
-      const bool more = k + 2 < KT;
-      __amdgpu_buffer_rsrc_t ra, rb;
-      L.rsrc(k + 2, ra, rb);
-      compute<FIRST>(acc, a, b, [&](auto I) {
-        constexpr int i = decltype(I)::value;
-        constexpr int every = 2 * kTM * kTN / (2 * kSegs);
-        if constexpr (i % every == every / 2) {
-          if (more) L.dma(i / every, k + 2, ra, rb);
-        }
-      });
+      compute<decltype(first)::value>(acc, a, b, none);
       prio_low();
       if (k + 1 < KT) block_barrier();
     };
