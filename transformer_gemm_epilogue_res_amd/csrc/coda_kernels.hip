@@ -273,14 +273,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const
 
 // ------------------------------------------------------- small kernels
 
-// r_i = 1 / sqrt(sum_t P[i, t] / D + eps), fixed summation order.
+// r_i = 1 / sqrt(sum_t P[i, t] / D + eps). Sixteen lanes per row, each summing
+// a strided quarter of the row's partials as float4 loads, then a fixed
+// butterfly over the 16 lanes: the summation order depends only on pcols.
+constexpr int kCombineRows = 16;  // rows per 256-thread block
 __global__ __launch_bounds__(256) void rms_combine_kernel(const float* P, float* r, int64_t M, int64_t pcols,
                                                           float D, float eps) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= M) return;
+  const int64_t i = int64_t(blockIdx.x) * kCombineRows + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
   float acc = 0.f;
-  for (int64_t t = 0; t < pcols; ++t) acc += P[i * pcols + t];
-  r[i] = 1.0f / sqrtf(acc / D + eps);
+  if (i < M) {
+    const float4* row = reinterpret_cast<const float4*>(P + i * pcols);
+    for (int64_t t = l; t < pcols / 4; t += 16) {
+      const float4 v = row[t];
+      acc += (v.x + v.y) + (v.z + v.w);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) acc += shfl_xor(acc, m);
+  if (l == 0 && i < M) r[i] = 1.0f / sqrtf(acc / D + eps);
 }
 
 // Block-wide sum over 256 threads, fixed order (wave shuffles, then LDS).
@@ -295,28 +306,56 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return t;
 }
 
-// One block per row i: s_i = sum_n dY_in y_in (fp32) and gr_i = bf16(r_i g_i).
-__global__ __launch_bounds__(256) void rowstat_kernel(const uint16_t* dY, const uint16_t* y, const uint16_t* g,
-                                                      const float* r, float* s, uint16_t* gr, int64_t N,
-                                                      int64_t D) {
-  __shared__ float red[4];
+// Block-wide sum over 512 threads, fixed order (wave shuffles, then LDS).
+__device__ __forceinline__ float block_sum512(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  const float t = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+  __syncthreads();
+  return t;
+}
+
+// One 512-thread block per row i: s_i = sum_n dY_in y_in (fp32) and
+// gr_i = bf16(r_i g_i). The row is read in rounds of kRowUnroll x 16 bytes per
+// thread of each input, all loads of a round issued before any is used (7
+// rounds cover an N = 28672 row in one pass).
+constexpr int kRowThreads = 512;
+constexpr int kRowUnroll = 7;
+__global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY, const uint16_t* y,
+                                                              const uint16_t* g, const float* r, float* s,
+                                                              uint16_t* gr, int64_t N, int64_t D) {
+  __shared__ float red[kRowThreads / 64];
   const int64_t i = blockIdx.x;
   const uint4* a = reinterpret_cast<const uint4*>(dY + i * N);
   const uint4* b = reinterpret_cast<const uint4*>(y + i * N);
+  const int64_t n8 = N / 8;
   float acc = 0.f;
-  for (int64_t v = threadIdx.x; v < N / 8; v += 256) {
-    float fa[8], fb[8];
-    unpack8_bf16(a[v], fa);
-    unpack8_bf16(b[v], fb);
+  for (int64_t base = threadIdx.x; base < n8; base += kRowThreads * kRowUnroll) {
+    uint4 va[kRowUnroll], vb[kRowUnroll];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += fa[e] * fb[e];
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int64_t v = base + u * kRowThreads;
+      va[u] = v < n8 ? a[v] : make_uint4(0, 0, 0, 0);
+      vb[u] = v < n8 ? b[v] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      float fa[8], fb[8];
+      unpack8_bf16(va[u], fa);
+      unpack8_bf16(vb[u], fb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += fa[e] * fb[e];
+    }
   }
-  const float tot = block_sum256(acc, red);
+  const float tot = block_sum512(acc, red);
   if (threadIdx.x == 0) s[i] = tot;
   const float ri = r[i];
   const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
   uint4* go = reinterpret_cast<uint4*>(gr + i * D);
-  for (int64_t v = threadIdx.x; v < D / 8; v += 256) {
+  for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
     float f[8];
     unpack8_bf16(gs[v], f);
     const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
@@ -325,14 +364,26 @@ __global__ __launch_bounds__(256) void rowstat_kernel(const uint16_t* dY, const 
   }
 }
 
-// dgamma_j = sum_t Pg[t, j], fixed order.
+// dgamma_j = sum_t Pg[t, j]. A 256-thread block covers 32 columns; its 8 row
+// groups each sum every 8th partial row, then the 8 group sums are added in a
+// fixed order.
+constexpr int kDgCols = 32, kDgGroups = 8;
 __global__ __launch_bounds__(256) void dgamma_combine_kernel(const float* Pg, float* dgamma, int64_t rows,
                                                              int64_t D) {
-  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (j >= D) return;
+  __shared__ float part[kDgGroups][kDgCols];
+  const int c = threadIdx.x % kDgCols, q = threadIdx.x / kDgCols;
+  const int64_t j = int64_t(blockIdx.x) * kDgCols + c;
   float acc = 0.f;
-  for (int64_t t = 0; t < rows; ++t) acc += Pg[t * D + j];
-  dgamma[j] = acc;
+  if (j < D)
+    for (int64_t t = q; t < rows; t += kDgGroups) acc += Pg[t * D + j];
+  part[q][c] = acc;
+  __syncthreads();
+  if (q == 0 && j < D) {
+    float tot = 0.f;
+#pragma unroll
+    for (int g = 0; g < kDgGroups; ++g) tot += part[g][c];
+    dgamma[j] = tot;
+  }
 }
 
 // Unfused: one block per row. h = t + z (fp32, stored bf16), r from the fp32 h,
@@ -438,7 +489,7 @@ char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // s and bf16(r * g), then the weight gradient dW1 = bf16(r g)^T @ dY.
 hipError_t bwd_rowstat(const coda_bwd_args_t* a, uint16_t* gr, hipStream_t st) {
-  hipLaunchKernelGGL(rowstat_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, (const uint16_t*)a->dY,
+  hipLaunchKernelGGL(rowstat_kernel, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)a->dY,
                      (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, a->s, gr, a->N, a->D);
   return hipGetLastError();
 }
@@ -450,7 +501,7 @@ hipError_t bwd_wgrad(const coda_bwd_args_t* a, const uint16_t* gr, hipStream_t s
 }
 
 hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, hipStream_t st) {
-  hipLaunchKernelGGL(dgamma_combine_kernel, dim3(unsigned(ceil_div(a->D, 256))), dim3(256), 0, st, Pg, a->dgamma,
+  hipLaunchKernelGGL(dgamma_combine_kernel, dim3(unsigned(ceil_div(a->D, kDgCols))), dim3(256), 0, st, Pg, a->dgamma,
                      rows, a->D);
   return hipGetLastError();
 }
@@ -476,7 +527,7 @@ coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size
         p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st));
   }
   if (stage == 1) {  // partial sums of squares -> r
-    hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, 256))), dim3(256), 0, st, P, a->r, a->M,
+    hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, kCombineRows))), dim3(256), 0, st, P, a->r, a->M,
                        pcols, float(a->D), a->eps);
     return to_status(hipGetLastError());
   }

@@ -404,11 +404,16 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
     step(0, std::true_type{});
     for (int k = 1; k < KT; ++k) step(k, std::false_type{});
   } else {
-    // prologue: A(0) and A(1). Phase 0: nothing; phase 2k+1: the DMA of
-    // A(k+2), then L(k), then wait for A(k+1); phase 2k+2: C(k).
+    // prologue: A(0), and A(1) left in flight (it is first read in phase 2).
+    // Phase 0: nothing; phase 2k+1: the DMA of A(k+2), then L(k), then wait
+    // for A(k+1); phase 2k+2: C(k).
     L.dma_a(0);
-    if (1 < KT) L.dma_a(1);
-    wait_vm0();
+    if (1 < KT) {
+      L.dma_a(1);
+      wait_vm<kSegs>();
+    } else {
+      wait_vm0();
+    }
     block_barrier();
     block_barrier();
     auto step = [&](int k, auto first) {
