@@ -39,6 +39,14 @@ The da formula is the exact gradient of the definition above (d r_i / d h_ij =
 sum_k G_ik n_ik = sum_n dY_in y_in); the pages print only s. It is pinned
 against torch autograd and finite differences in the tests.
 
+Backward through the first GEMM and the residual (the rest of the chain's
+backward, h = x @ W0 + z), for an upstream gradient dh of h (da above, plus any
+gradient the residual stream brings, which this chain does not model):
+
+    dz  = dh
+    dx  = dh @ W0^T
+    dW0 = x^T @ dh
+
 Matrix products use numpy's float64 matmul as a library primitive. Row subsets
 (``rows``) and column subsets are supported because rows of the forward are
 independent and the large configurations are checked on seeded samples.
@@ -143,4 +151,25 @@ def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=No
         gr = _take(g, blk) * rd[blk, None]
         dW1 += gr.T @ _take(dY, blk, nc)
     out["dW1"] = dW1
+    return out
+
+
+def backward_gemm0(dh, x, W0, rows=None, dw0_cols=None) -> dict:
+    """Backward through h = x @ W0 + z for the upstream gradient dh [M, D].
+
+    * ``rows``: rows i of dx (and dz) returned (all when None);
+    * ``dw0_cols``: columns j of dW0 (sums over *all* M rows; all when None).
+    """
+    W0d = f64(W0)
+    M, D = dh.shape
+    K0 = W0d.shape[0]
+    ridx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    dhr = _take(dh, ridx)
+    out = {"dz": dhr, "dx": dhr @ W0d.T}
+    jc = np.arange(D) if dw0_cols is None else np.asarray(dw0_cols, dtype=np.int64)
+    dW0 = np.zeros((K0, len(jc)))
+    for c0 in range(0, M, 2048):
+        blk = np.arange(c0, min(M, c0 + 2048))
+        dW0 += _take(x, blk).T @ _take(dh, blk, jc)
+    out["dW0"] = dW0
     return out

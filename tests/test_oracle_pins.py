@@ -174,6 +174,53 @@ def test_backward_matches_torch_autograd():
     assert _relerr(b["dW1"], W.grad.numpy()) < 1e-10
 
 
+def test_backward_through_gemm0_matches_torch_autograd():
+    # the whole chain in float64 autograd: x, W0, z are leaves; the oracle composes
+    # backward (da) with backward_gemm0 (dx, dW0, dz = da)
+    x, W0, z, gamma, W1, dY, eps = _rand_problem(12, 24, 32, 40, 9)
+    xl, wl, zl = (t.clone().requires_grad_(True) for t in (x, W0, z))
+    h = xl @ wl + zl
+    y = torch.nn.functional.rms_norm(h, (h.shape[1],), gamma, eps) @ W1
+    (y * dY).sum().backward()
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    b = orc.backward(dY, f["y"], f["h"], f["h"] * gamma.numpy()[None, :], f["r"], gamma, W1)
+    b0 = orc.backward_gemm0(b["da"], x, W0)
+    assert _relerr(b0["dx"], xl.grad.numpy()) < 1e-10
+    assert _relerr(b0["dW0"], wl.grad.numpy()) < 1e-10
+    assert _relerr(b0["dz"], zl.grad.numpy()) < 1e-10
+
+
+def test_backward_through_gemm0_finite_differences_and_subsets():
+    M, K0, D, N = 6, 8, 16, 12
+    x, W0, z, gamma, W1, dY, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
+                                     for t in _rand_problem(M, K0, D, N, 10))
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    b = orc.backward(dY, f["y"], f["h"], f["h"] * gamma[None, :], f["r"], gamma, W1)
+    b0 = orc.backward_gemm0(b["da"], x, W0)
+
+    def L(xx, ww):
+        return float((orc.forward(xx, ww, z, gamma, W1, eps)["y"] * dY).sum())
+
+    step = 1e-6
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        i, k = rng.integers(M), rng.integers(K0)
+        xp, xm = x.copy(), x.copy()
+        xp[i, k] += step
+        xm[i, k] -= step
+        fd = (L(xp, W0) - L(xm, W0)) / (2 * step)
+        assert abs(fd - b0["dx"][i, k]) <= 1e-7 * max(1.0, abs(fd))
+        k, j = rng.integers(K0), rng.integers(D)
+        wp, wm = W0.copy(), W0.copy()
+        wp[k, j] += step
+        wm[k, j] -= step
+        fd = (L(x, wp) - L(x, wm)) / (2 * step)
+        assert abs(fd - b0["dW0"][k, j]) <= 1e-7 * max(1.0, abs(fd))
+    part = orc.backward_gemm0(b["da"], x, W0, rows=[1, 4], dw0_cols=[0, 9, 15])
+    assert np.allclose(part["dx"], b0["dx"][[1, 4]], rtol=0, atol=1e-13)
+    assert np.allclose(part["dW0"], b0["dW0"][:, [0, 9, 15]], rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------------ finite differences
 
 def test_backward_finite_differences():
