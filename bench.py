@@ -231,6 +231,24 @@ def main():
     for n in names:
         log(f"[bench]   {n:20s} {kernels[n]}")
 
+    # The backward through the first GEMM (dx, dW0 from the step's bf16 da): not part
+    # of the headline step (the chain's metric stops at da), reported beside it.
+    g0o = {"dx": torch.empty(M, K0, dtype=bf, device=dev), "dW0": torch.empty(K0, D, dtype=bf, device=dev)}
+    G0 = L.BoundGemm0(bo["da"], x, W0, g0o)
+    for _ in range(2):
+        G0.run(sp)
+    a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(args.steps):
+        G0.run(sp)
+    b0.record(stream)
+    torch.cuda.synchronize()
+    g0_ms = a0.elapsed_time(b0) / args.steps
+    g0_flop = 2 * 2 * M * K0 * D
+    bwd_gemm0 = {"ms": round(g0_ms, 4), "tflops": round(g0_flop / g0_ms / 1e9, 1),
+                 "pct_peak": round(100 * g0_flop / g0_ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    log(f"[bench] backward through GEMM0 (dx, dW0): {g0_ms:.3f} ms, {bwd_gemm0['tflops']} TFLOP/s")
+
     unfused = None
     if not args.no_unfused:
         log("[bench] timing the unfused baseline")
@@ -274,6 +292,7 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
                 "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
+        "bwd_gemm0": bwd_gemm0,
         "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

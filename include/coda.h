@@ -122,6 +122,29 @@ typedef struct {
   coda_dtype_t dW1_dtype;
 } coda_bwd_args_t;
 
+/* Backward through the chain's first GEMM and its residual, h = x @ W0 + z
+ * (hotdry blog, section "GEMM-Residual-RMSNorm-GEMM 重参数化", for the
+ * forward; kucoin page, section "実験結果", which evaluates the backward of the
+ * whole GEMM-Residual-RMSNorm-GEMM chain), for an upstream gradient dh of h
+ * (coda_bwd's da stored as bf16, plus whatever gradient the residual stream
+ * adds, which this chain does not model):
+ *     dz = dh            (nothing to compute: the caller uses dh itself)
+ *     dx = dh @ W0^T     dW0 = x^T @ dh
+ *   in : dh [M,D] bf16, x [M,K0] bf16, W0 [K0,D] bf16.
+ *   out: dx [M,K0] in dx_dtype, dW0 [K0,D] in dW0_dtype.
+ * Two launches of the shared mainloop with store-only epilogues; no workspace.
+ * Shapes as for coda_fwd (K0 and D multiples of 256, any M >= 1). */
+typedef struct {
+  int64_t M, K0, D;
+  const void* dh;
+  const void* x;
+  const void* W0;
+  void* dx;
+  void* dW0;
+  coda_dtype_t dx_dtype;
+  coda_dtype_t dW0_dtype;
+} coda_bwd_gemm0_args_t;
+
 /* Operand layouts for coda_gemm. */
 typedef enum {
   CODA_ROW = 0, /* A: element (m,k) at A[m*lda + k];  B: element (k,n) at B[k*ldb + n] */
@@ -156,6 +179,7 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N);
 coda_status_t coda_validate_fwd(const coda_fwd_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_bwd(const coda_bwd_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_gemm(const coda_gemm_args_t* a);
+coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a);
 /* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD or CODA_OP_BWD). */
 coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
 
@@ -191,6 +215,9 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
  *     G = dY@W1^T stored as bf16 in the workspace -> RMSNorm-backward row kernel
  *     (da, dgamma partials) -> dgamma combine -> same dW1 GEMM. */
 coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward through the first GEMM (see coda_bwd_gemm0_args_t): dx, then dW0. */
+coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream);
 
 /* Plain GEMM (see coda_gemm_args_t); needs no workspace. */
 coda_status_t coda_gemm(const coda_gemm_args_t* a, void* stream);

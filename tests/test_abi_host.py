@@ -35,10 +35,13 @@ def test_struct_layout_matches_c_header():
 #include "coda.h"
 #define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
 int main(void) {
-  printf("fwd %zu bwd %zu gemm %zu\n", sizeof(coda_fwd_args_t), sizeof(coda_bwd_args_t), sizeof(coda_gemm_args_t));
+  printf("fwd %zu bwd %zu gemm %zu bwd0 %zu\n", sizeof(coda_fwd_args_t), sizeof(coda_bwd_args_t), sizeof(coda_gemm_args_t),
+         sizeof(coda_bwd_gemm0_args_t));
   O(coda_fwd_args_t, eps); O(coda_fwd_args_t, x); O(coda_fwd_args_t, y); O(coda_fwd_args_t, y_dtype);
   O(coda_bwd_args_t, dY); O(coda_bwd_args_t, s); O(coda_bwd_args_t, da_dtype); O(coda_bwd_args_t, dW1_dtype);
   O(coda_gemm_args_t, a_layout); O(coda_gemm_args_t, B); O(coda_gemm_args_t, b_layout); O(coda_gemm_args_t, c_dtype);
+  O(coda_bwd_gemm0_args_t, dh); O(coda_bwd_gemm0_args_t, dW0); O(coda_bwd_gemm0_args_t, dx_dtype);
+  O(coda_bwd_gemm0_args_t, dW0_dtype);
   return 0;
 }
 """
@@ -52,7 +55,9 @@ int main(void) {
     assert int(head[1]) == ctypes.sizeof(L.FwdArgs)
     assert int(head[3]) == ctypes.sizeof(L.BwdArgs)
     assert int(head[5]) == ctypes.sizeof(L.GemmArgs)
-    types = {"coda_fwd_args_t": L.FwdArgs, "coda_bwd_args_t": L.BwdArgs, "coda_gemm_args_t": L.GemmArgs}
+    assert int(head[7]) == ctypes.sizeof(L.BwdGemm0Args)
+    types = {"coda_fwd_args_t": L.FwdArgs, "coda_bwd_args_t": L.BwdArgs, "coda_gemm_args_t": L.GemmArgs,
+             "coda_bwd_gemm0_args_t": L.BwdGemm0Args}
     for line in out[1:]:
         if not line:
             continue
@@ -148,6 +153,20 @@ def test_validate_unfused_and_gemm():
         g2 = L.GemmArgs.from_buffer_copy(g)
         setattr(g2, k, v)
         assert lib.coda_validate_gemm(ctypes.byref(g2)) == want, k
+
+
+def test_validate_bwd_gemm0():
+    lib = L.lib()
+    a = L.BwdGemm0Args(300, 512, 256, fake(1), fake(2), fake(3), fake(4), fake(5), L.CODA_BF16, L.CODA_F32)
+    assert lib.coda_validate_bwd_gemm0(ctypes.byref(a)) == L.CODA_OK
+    for k, v, want in (("M", 0, L.CODA_ERR_SHAPE), ("K0", 300, L.CODA_ERR_SHAPE), ("D", 0, L.CODA_ERR_SHAPE),
+                       ("dh", None, L.CODA_ERR_NULL), ("dW0", ctypes.c_void_p(A + 8), L.CODA_ERR_ALIGN),
+                       ("dx_dtype", 7, L.CODA_ERR_ARG)):
+        b = L.BwdGemm0Args.from_buffer_copy(a)
+        setattr(b, k, v)
+        assert lib.coda_validate_bwd_gemm0(ctypes.byref(b)) == want, k
+        assert lib.coda_bwd_gemm0(ctypes.byref(b), None) == want, k  # rejected before any launch
+    assert lib.coda_validate_bwd_gemm0(None) == L.CODA_ERR_NULL
 
 
 def test_entry_points_reject_without_launching():

@@ -225,6 +225,80 @@ def test_bwd_llama3_8b_sampled():
     check_bwd(o32, o16, host, rows=rows, jcols=jcols, ncols=ncols)
 
 
+# --------------------------------------------- backward through the first GEMM
+
+BWD0_SMALL = {
+    "tiny": dict(M=64, K0=256, D=256),
+    "ragged": dict(M=300, K0=512, D=256),
+    "one_row": dict(M=1, K0=256, D=512),
+}
+
+
+def check_bwd_gemm0(o32, o16, ref, rows=None, cols=None):
+    def rsel(t):
+        return t.cpu() if rows is None else t.index_select(0, torch.as_tensor(rows, device=t.device)).cpu()
+
+    def csel(t):
+        return t.cpu() if cols is None else t.index_select(1, torch.as_tensor(cols, device=t.device)).cpu()
+
+    dx, dW0 = rsel(o32["dx"]), csel(o32["dW0"])
+    e = {"dx": mt.normwise(dx, ref["dx"]), "dW0": mt.normwise(dW0, ref["dW0"])}
+    print("  " + "  ".join(f"{k} max|d|/rms={v:.3e}" for k, v in e.items()))
+    assert torch.equal(mt.rne_bf16(dx).view(torch.int16), rsel(o16["dx"]).view(torch.int16))
+    assert torch.equal(mt.rne_bf16(dW0).view(torch.int16), csel(o16["dW0"]).view(torch.int16))
+    return e
+
+
+@pytest.mark.parametrize("name", list(BWD0_SMALL))
+def test_bwd_gemm0_small_full(name):
+    # a plain pair of products of bf16 operands with fp32 accumulation: fp32-level agreement
+    c = BWD0_SMALL[name]
+    announce(f"coda_bwd_gemm0 {name} {c} seed=0 (dh random)")
+    inp = inputs.forward_inputs(M=c["M"], K0=c["K0"], D=c["D"], N=256, seed=0)
+    dh = inputs.upstream_grad(c["M"], c["D"], seed=0)
+    d = to_dev({"dh": dh, "x": inp["x"], "W0": inp["W0"]})
+    o32 = L.bwd_gemm0(d["dh"], d["x"], d["W0"], dx_dtype=torch.float32, dW0_dtype=torch.float32)
+    o16 = L.bwd_gemm0(d["dh"], d["x"], d["W0"])
+    torch.cuda.synchronize()
+    e = check_bwd_gemm0(o32, o16, orc.backward_gemm0(dh, inp["x"], inp["W0"]))
+    assert e["dx"] <= 1e-4 and e["dW0"] <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_bwd_gemm0_after_chain_backward(name):
+    # the whole chain's backward on the GPU (da stored as bf16 and fed on) against
+    # the oracle's composition: the error is the bf16 rounding of da
+    c = BWD_SMALL[name]
+    announce(f"coda_bwd -> coda_bwd_gemm0 {name} {c} seed=0")
+    inp = inputs.forward_inputs(**c, seed=0)
+    host = dict(saved_set(inp), dY=inputs.output_grad(c["M"], c["N"], seed=0), gamma=inp["gamma"], W1=inp["W1"])
+    dev = to_dev(dict(host, x=inp["x"], W0=inp["W0"]))
+    b = L.bwd(dev["dY"], dev["y"], dev["h"], dev["g"], dev["r"], dev["gamma"], dev["W1"])
+    o32 = L.bwd_gemm0(b["da"], dev["x"], dev["W0"], dx_dtype=torch.float32, dW0_dtype=torch.float32)
+    o16 = L.bwd_gemm0(b["da"], dev["x"], dev["W0"])
+    torch.cuda.synchronize()
+    ref_b = orc.backward(host["dY"], host["y"], host["h"], host["g"], host["r"], host["gamma"], host["W1"])
+    e = check_bwd_gemm0(o32, o16, orc.backward_gemm0(ref_b["da"], inp["x"], inp["W0"]))
+    assert e["dx"] <= mt.Y_TOL and e["dW0"] <= mt.Y_TOL
+
+
+@pytest.mark.slow
+def test_bwd_gemm0_llama3_8b_sampled():
+    c = inputs.CONFIGS["llama3_8b"]
+    announce(f"coda_bwd_gemm0 llama3_8b M={c['M']} K0={c['K0']} D={c['D']} seed=0 (dh random), sampled")
+    inp = inputs.forward_inputs(**c, seed=0)
+    dh = inputs.upstream_grad(c["M"], c["D"], seed=0)
+    rows = inputs.sample(c["M"], 256, 0, "rows").numpy()
+    cols = inputs.sample(c["D"], 256, 0, "dw0_cols").numpy()
+    d = to_dev({"dh": dh, "x": inp["x"], "W0": inp["W0"]})
+    o32 = L.bwd_gemm0(d["dh"], d["x"], d["W0"], dx_dtype=torch.float32, dW0_dtype=torch.float32)
+    o16 = L.bwd_gemm0(d["dh"], d["x"], d["W0"])
+    torch.cuda.synchronize()
+    e = check_bwd_gemm0(o32, o16, orc.backward_gemm0(dh, inp["x"], inp["W0"], rows=rows, dw0_cols=cols),
+                        rows=rows, cols=cols)
+    assert e["dx"] <= 1e-4 and e["dW0"] <= 1e-4
+
+
 # ------------------------------------------------------ determinism, canaries
 
 def test_run_to_run_bitwise_determinism():

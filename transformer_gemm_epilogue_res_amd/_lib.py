@@ -48,6 +48,12 @@ class GemmArgs(ctypes.Structure):
                 ("C", c_void_p), ("ldc", c_int64), ("c_dtype", c_int)]
 
 
+class BwdGemm0Args(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("K0", c_int64), ("D", c_int64),
+                ("dh", c_void_p), ("x", c_void_p), ("W0", c_void_p), ("dx", c_void_p), ("dW0", c_void_p),
+                ("dx_dtype", c_int), ("dW0_dtype", c_int)]
+
+
 class CodaError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: status {status} ({status_string(status)})")
@@ -75,7 +81,9 @@ def lib() -> ctypes.CDLL:
                            ("coda_unfused_ref", [c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
                            ("coda_fwd_stage", [c_int, POINTER(FwdArgs), c_void_p, c_size_t, c_void_p]),
                            ("coda_bwd_stage", [c_int, POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
-                           ("coda_gemm", [POINTER(GemmArgs), c_void_p])):
+                           ("coda_gemm", [POINTER(GemmArgs), c_void_p]),
+                           ("coda_validate_bwd_gemm0", [POINTER(BwdGemm0Args)]),
+                           ("coda_bwd_gemm0", [POINTER(BwdGemm0Args), c_void_p])):
             fn = getattr(L, name)
             fn.restype = c_int
             fn.argtypes = argt
@@ -88,7 +96,7 @@ def lib() -> ctypes.CDLL:
 def declared_functions() -> list:
     """Names of the functions include/coda.h declares."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\**(coda_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\**(coda_[a-z0-9_]+)\s*\(", text, re.M)))
 
 
 def status_string(s: int) -> str:
@@ -201,6 +209,38 @@ def bwd(dY, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_dtype=torch.bflo
         st = lib().coda_bwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "coda_unfused_ref(bwd)" if unfused else "coda_bwd")
     return out
+
+
+def _bwd_gemm0_args(dh, x, W0, dx, dW0):
+    M, D = dh.shape
+    K0 = x.shape[1]
+    _want(dh, "dh", torch.bfloat16, (M, D))
+    _want(x, "x", torch.bfloat16, (M, K0))
+    _want(W0, "W0", torch.bfloat16, (K0, D))
+    return BwdGemm0Args(M, K0, D, _ptr(dh), _ptr(x), _ptr(W0), _ptr(dx), _ptr(dW0), _dt(dx.dtype), _dt(dW0.dtype))
+
+
+def bwd_gemm0(dh, x, W0, dx_dtype=torch.bfloat16, dW0_dtype=torch.bfloat16, out=None):
+    """Backward through h = x @ W0 + z for the upstream gradient dh: dict(dx, dW0) (dz is dh)."""
+    M, D = dh.shape
+    K0 = x.shape[1]
+    dev = dh.device
+    if out is None:
+        out = {"dx": torch.empty(M, K0, dtype=dx_dtype, device=dev),
+               "dW0": torch.empty(K0, D, dtype=dW0_dtype, device=dev)}
+    a = _bwd_gemm0_args(dh, x, W0, out["dx"], out["dW0"])
+    _check(lib().coda_bwd_gemm0(ctypes.byref(a), _stream(dev)), "coda_bwd_gemm0")
+    return out
+
+
+class BoundGemm0:
+    """coda_bwd_gemm0 with its arguments marshalled once (benchmarks)."""
+
+    def __init__(self, dh, x, W0, out):
+        self.args, self._keep = _bwd_gemm0_args(dh, x, W0, out["dx"], out["dW0"]), (dh, x, W0, out)
+
+    def run(self, stream):
+        _check(lib().coda_bwd_gemm0(ctypes.byref(self.args), stream), "coda_bwd_gemm0")
 
 
 class Bound:

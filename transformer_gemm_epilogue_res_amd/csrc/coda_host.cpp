@@ -131,6 +131,16 @@ coda_status_t coda_validate_gemm(const coda_gemm_args_t* a) {
   return CODA_OK;
 }
 
+coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->dh, a->x, a->W0, a->dx, a->dW0};
+  coda_status_t st = check_ptrs(ps, 5);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->K0) || !dim_ok(a->D)) return CODA_ERR_SHAPE;
+  if (!dtype_ok(a->dx_dtype) || !dtype_ok(a->dW0_dtype)) return CODA_ERR_ARG;
+  return CODA_OK;
+}
+
 const char* coda_status_string(coda_status_t s) {
   switch (s) {
     case CODA_OK: return "ok";

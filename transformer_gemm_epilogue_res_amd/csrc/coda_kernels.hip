@@ -611,6 +611,19 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
   return to_status(bwd_wgrad(a, gr, st));
 }
 
+coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream) {
+  coda_status_t v = coda_validate_bwd_gemm0(a);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // dx [M,K0] = dh @ W0^T: A = dh [M,D] (k contiguous), B(k=j, n=k0) = W0[k0, j] (k contiguous)
+  const GemmShape px{a->M, a->K0, a->D, a->dh, a->D, a->W0, a->D};
+  hipError_t e = gemm_plain(px, true, true, a->dx, a->K0, a->dx_dtype == CODA_F32, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  // dW0 [K0,D] = x^T @ dh: A(m=k0, k=i) = x[i, k0] (m contiguous), B(k=i, n=j) = dh[i, j] (n contiguous), K = M
+  const GemmShape pw{a->K0, a->D, a->M, a->x, a->K0, a->dh, a->D};
+  return to_status(gemm_plain(pw, false, false, a->dW0, a->D, a->dW0_dtype == CODA_F32, st));
+}
+
 coda_status_t coda_gemm(const coda_gemm_args_t* a, void* stream) {
   coda_status_t v = coda_validate_gemm(a);
   if (v != CODA_OK) return v;

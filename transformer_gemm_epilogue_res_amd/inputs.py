@@ -9,9 +9,10 @@ expectations" paragraph, and the kucoin article, "experimental results"):
 
 * every tensor has its own CPU ``torch.Generator`` seeded ``seed*100 + id``
   with ids x=1, W0=2, z=3, gamma=4, W1=5, dY=6 (row sample 7, dgamma column
-  sample 8, dW1 column sample 9);
+  sample 8, dW1 column sample 9), and for the backward through the first GEMM
+  dh=10 (dW0 column sample 11);
 * each draw is fp32 ``randn`` scaled and then cast to bfloat16 (round to
-  nearest even): x, z, dY ~ N(0, 1); W0 ~ N(0, 1/K0); W1 ~ N(0, 1/D)
+  nearest even): x, z, dY, dh ~ N(0, 1); W0 ~ N(0, 1/K0); W1 ~ N(0, 1/D)
   (fan-in = rows of the ``[in, out]`` weight); gamma = 1 + 0.1 N(0, 1);
 * eps = 1e-5.
 
@@ -27,7 +28,7 @@ import torch
 EPS = 1e-5
 
 IDS = {"x": 1, "W0": 2, "z": 3, "gamma": 4, "W1": 5, "dY": 6,
-       "rows": 7, "dgamma_cols": 8, "dw1_cols": 9}
+       "rows": 7, "dgamma_cols": 8, "dw1_cols": 9, "dh": 10, "dw0_cols": 11}
 
 # name -> (M tokens, K0, D, N = 2 * ffn)
 CONFIGS = {
@@ -67,6 +68,11 @@ def forward_inputs(M: int, K0: int, D: int, N: int, seed: int = 0) -> dict:
 def output_grad(M: int, N: int, seed: int = 0) -> torch.Tensor:
     """dY [M,N] bf16 ~ N(0,1)."""
     return _randn_bf16((M, N), seed, "dY")
+
+
+def upstream_grad(M: int, D: int, seed: int = 0) -> torch.Tensor:
+    """dh [M,D] bf16 ~ N(0,1): a gradient of h for the backward through the first GEMM."""
+    return _randn_bf16((M, D), seed, "dh")
 
 
 def sample(n: int, count: int, seed: int, name: str) -> torch.Tensor:
