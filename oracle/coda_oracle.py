@@ -47,6 +47,24 @@ gradient the residual stream brings, which this chain does not model):
     dx  = dh @ W0^T
     dW0 = x^T @ dh
 
+SwiGLU on the second GEMM's output (blog, section "成对激活的寄存器级融合":
+paired features sit in adjacent output columns, so the gated activation is
+applied where the pair is produced; the backward of such a pairwise epilogue is
+a dimension-expanding one). Column 2f of y is gate f and column 2f+1 is up f:
+
+    o_if   = silu(y_i,2f) * y_i,2f+1,      silu(v) = v / (1 + exp(-v))
+
+and for an output projection out = o @ W2 (W2 [F, E]) with L = <dOut, out>:
+
+    dO       = dOut @ W2^T                 (the down projection's data gradient)
+    dY_i,2f  = dO_if * y_i,2f+1 * silu'(y_i,2f),   silu'(v) = sig(v) (1 + v (1 - sig(v)))
+    dY_i,2f+1 = dO_if * silu(y_i,2f)
+    s_i      = sum_n dY_in * y_in          (the same row statistic, now taken where
+                                            dY is produced)
+    dW2      = o^T @ dOut
+
+after which the chain's backward above continues with this dY.
+
 Matrix products use numpy's float64 matmul as a library primitive. Row subsets
 (``rows``) and column subsets are supported because rows of the forward are
 independent and the large configurations are checked on seeded samples.
@@ -172,4 +190,46 @@ def backward_gemm0(dh, x, W0, rows=None, dw0_cols=None) -> dict:
         blk = np.arange(c0, min(M, c0 + 2048))
         dW0 += _take(x, blk).T @ _take(dh, blk, jc)
     out["dW0"] = dW0
+    return out
+
+
+def _sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def silu(v) -> np.ndarray:
+    """silu(v) = v * sigmoid(v)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v * _sigmoid(v)
+
+
+def swiglu(y) -> np.ndarray:
+    """o[:, f] = silu(y[:, 2f]) * y[:, 2f+1] (gate/up interleaved along the columns)."""
+    yd = f64(y)
+    return silu(yd[:, 0::2]) * yd[:, 1::2]
+
+
+def swiglu_backward(dOut, W2, y, o, rows=None, dw2_cols=None) -> dict:
+    """Backward of o = swiglu(y), out = o @ W2 for L = <dOut, out>, for the saved y (and o).
+
+    * ``rows``: rows i of dO, dY and s returned (all when None);
+    * ``dw2_cols``: columns e of dW2 = o^T @ dOut (sums over all M rows; all when None).
+    """
+    W2d = f64(W2)
+    M = dOut.shape[0]
+    ridx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    dO = _take(dOut, ridx) @ W2d.T
+    yr = _take(y, ridx)
+    gate, up = yr[:, 0::2], yr[:, 1::2]
+    sg = _sigmoid(gate)
+    dY = np.empty_like(yr)
+    dY[:, 0::2] = dO * up * (sg * (1.0 + gate * (1.0 - sg)))
+    dY[:, 1::2] = dO * gate * sg
+    out = {"dO": dO, "dY": dY, "s": (dY * yr).sum(axis=1)}
+    ec = np.arange(W2d.shape[1]) if dw2_cols is None else np.asarray(dw2_cols, dtype=np.int64)
+    dW2 = np.zeros((W2d.shape[0], len(ec)))
+    for c0 in range(0, M, 2048):
+        blk = np.arange(c0, min(M, c0 + 2048))
+        dW2 += _take(o, blk).T @ _take(dOut, blk, ec)
+    out["dW2"] = dW2
     return out

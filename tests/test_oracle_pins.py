@@ -221,6 +221,84 @@ def test_backward_through_gemm0_finite_differences_and_subsets():
     assert np.allclose(part["dW0"], b0["dW0"][:, [0, 9, 15]], rtol=0, atol=1e-13)
 
 
+# --------------------------------------------------------------------- SwiGLU
+
+def test_silu_closed_forms_and_torch():
+    # silu(0) = 0, silu(1) = e / (1 + e), silu(v) -> v and silu(-v) -> 0 for large v; torch's silu in fp64
+    assert orc.silu(0.0) == 0.0
+    e = float(mpmath.e)
+    assert abs(orc.silu(1.0) - e / (1 + e)) < 1e-15
+    assert abs(orc.silu(40.0) - 40.0) < 1e-12 and abs(orc.silu(-40.0)) < 1e-15
+    v = torch.linspace(-12, 12, 2001, dtype=torch.float64)
+    assert _relerr(orc.silu(v.numpy()), torch.nn.functional.silu(v).numpy()) < 1e-15
+
+
+def test_swiglu_pairs_interleaved_columns():
+    # column 2f is the gate and 2f+1 the up value of feature f
+    y = np.array([[1.0, 2.0, 0.0, 5.0, -3.0, 0.5]])
+    e = float(mpmath.e)
+    want = [e / (1 + e) * 2.0, 0.0, orc.silu(-3.0) * 0.5]
+    assert np.allclose(orc.swiglu(y)[0], want, rtol=0, atol=1e-15)
+    # hand-derived backward of one pair (gate 1, up 2) for dO = 1: d/dgate = up silu'(1), d/dup = silu(1),
+    # silu'(1) = sig(1) (1 + 1 - sig(1)) with sig(1) = e / (1 + e)
+    sg = e / (1 + e)
+    W2 = np.array([[1.0]])
+    b = orc.swiglu_backward(np.array([[1.0]]), W2, y[:, :2], orc.swiglu(y[:, :2]))
+    assert abs(b["dY"][0, 0] - 2.0 * sg * (2.0 - sg)) < 1e-15
+    assert abs(b["dY"][0, 1] - sg) < 1e-15
+
+
+def test_swiglu_block_backward_matches_torch_autograd():
+    # the whole block in float64 autograd: h -> rms_norm -> @W1 -> swiglu -> @W2, L = <dOut, out>;
+    # the oracle composes swiglu_backward (dY, s, dW2) with the chain's backward (da, dgamma, dW1)
+    x, W0, z, gamma, W1, _, eps = _rand_problem(12, 24, 32, 40, 11)
+    g = torch.Generator().manual_seed(11)
+    W2 = torch.randn(20, 28, generator=g, dtype=torch.float64) / np.sqrt(20)
+    dOut = torch.randn(12, 28, generator=g, dtype=torch.float64)
+    h = (x @ W0 + z).requires_grad_(True)
+    gam, w1, w2 = (t.clone().requires_grad_(True) for t in (gamma, W1, W2))
+    y = torch.nn.functional.rms_norm(h, (h.shape[1],), gam, eps) @ w1
+    y.retain_grad()
+    o = torch.nn.functional.silu(y[:, 0::2]) * y[:, 1::2]
+    ((o @ w2) * dOut).sum().backward()
+    f = orc.forward(x, W0, z, gamma, W1, eps)
+    of = orc.swiglu(f["y"])
+    assert _relerr(of, o.detach().numpy()) < 1e-13
+    sb = orc.swiglu_backward(dOut, W2, f["y"], of)
+    assert _relerr(sb["dY"], y.grad.numpy()) < 1e-10
+    assert _relerr(sb["dW2"], w2.grad.numpy()) < 1e-10
+    b = orc.backward(sb["dY"], f["y"], f["h"], f["h"] * gamma.numpy()[None, :], f["r"], gamma, W1)
+    assert _relerr(b["s"], sb["s"]) < 1e-13
+    assert _relerr(b["da"], h.grad.numpy()) < 1e-10
+    assert _relerr(b["dgamma"], gam.grad.numpy()) < 1e-10
+    assert _relerr(b["dW1"], w1.grad.numpy()) < 1e-10
+
+
+def test_swiglu_backward_finite_differences_and_subsets():
+    rng = np.random.default_rng(3)
+    M, F, E = 5, 6, 7
+    y = rng.standard_normal((M, 2 * F)) * 2
+    W2 = rng.standard_normal((F, E))
+    dOut = rng.standard_normal((M, E))
+    b = orc.swiglu_backward(dOut, W2, y, orc.swiglu(y))
+
+    def L(yy):
+        return float(((orc.swiglu(yy) @ W2) * dOut).sum())
+
+    step = 1e-6
+    for _ in range(30):
+        i, n = rng.integers(M), rng.integers(2 * F)
+        yp, ym = y.copy(), y.copy()
+        yp[i, n] += step
+        ym[i, n] -= step
+        fd = (L(yp) - L(ym)) / (2 * step)
+        assert abs(fd - b["dY"][i, n]) <= 1e-7 * max(1.0, abs(fd))
+    part = orc.swiglu_backward(dOut, W2, y, orc.swiglu(y), rows=[0, 3], dw2_cols=[1, 6])
+    for k in ("dO", "dY", "s"):
+        assert np.allclose(part[k], b[k][[0, 3]], rtol=0, atol=1e-13)
+    assert np.allclose(part["dW2"], b["dW2"][:, [1, 6]], rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------------ finite differences
 
 def test_backward_finite_differences():
