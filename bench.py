@@ -123,6 +123,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows in the oracle's timed sample (0 = skip)")
     ap.add_argument("--cpu-cols", type=int, default=64)
     ap.add_argument("--no-unfused", action="store_true", help="skip timing the unfused baseline")
+    ap.add_argument("--no-swiglu", action="store_true", help="skip timing the SwiGLU block")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many bytes (a reference kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -249,6 +250,37 @@ def main():
                  "pct_peak": round(100 * g0_flop / g0_ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
     log(f"[bench] backward through GEMM0 (dx, dW0): {g0_ms:.3f} ms, {bwd_gemm0['tflops']} TFLOP/s")
 
+    # The SwiGLU block on the chain (coda_fwd_swiglu / coda_bwd_swiglu with the
+    # output projection W2 [N/2, D]): reported beside the headline step.
+    swiglu = None
+    if not args.no_swiglu:
+        Fh, E = N // 2, D
+        W2, dOut = rnd(Fh, E, scale=Fh ** -0.5), rnd(M, E)
+        so = dict(fo, o=torch.empty(M, Fh, dtype=bf, device=dev))
+        sbo = dict(bo, dY=torch.empty(M, N, dtype=bf, device=dev), dW2=torch.empty(Fh, E, dtype=bf, device=dev))
+        SF = L.bind_fwd_swiglu(x, W0, z, gamma, W1, inputs.EPS, so, fws)
+        SB = L.bind_bwd_swiglu(dOut, W2, so["o"], so["y"], so["h"], so["g"], so["r"], gamma, W1, sbo,
+                               L.workspace(L.CODA_OP_BWD_SWIGLU, M, D, N, dev))
+        t = {}
+        for name, obj in (("fwd", SF), ("bwd", SB)):
+            for _ in range(2):
+                obj.run(sp)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                obj.run(sp)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t[name] = a.elapsed_time(b) / args.steps
+        s_bwd_flop = bwd_flop + 2 * 2 * M * Fh * E   # + dO = dOut W2^T and dW2 = o^T dOut
+        swiglu = {"E": E, "fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
+                  "fwd_tflops": round(fwd_flop / t["fwd"] / 1e9, 1),
+                  "bwd_tflops": round(s_bwd_flop / t["bwd"] / 1e9, 1),
+                  "tflops": round((fwd_flop + s_bwd_flop) / (t["fwd"] + t["bwd"]) / 1e9, 1)}
+        swiglu["pct_peak"] = round(100 * swiglu["tflops"] / PEAK_BF16_TFLOPS, 2)
+        log(f"[bench] SwiGLU block: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {swiglu['tflops']} TFLOP/s")
+        del W2, dOut, so, sbo, SF, SB
+
     unfused = None
     if not args.no_unfused:
         log("[bench] timing the unfused baseline")
@@ -292,7 +324,7 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
                 "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
-        "bwd_gemm0": bwd_gemm0,
+        "bwd_gemm0": bwd_gemm0, "swiglu": swiglu,
         "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

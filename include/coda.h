@@ -74,7 +74,9 @@ typedef enum {
   CODA_OP_FWD = 0,          /* coda_fwd                      */
   CODA_OP_BWD = 1,          /* coda_bwd                      */
   CODA_OP_UNFUSED_FWD = 2,  /* coda_unfused_ref(CODA_OP_FWD)  */
-  CODA_OP_UNFUSED_BWD = 3   /* coda_unfused_ref(CODA_OP_BWD)  */
+  CODA_OP_UNFUSED_BWD = 3,  /* coda_unfused_ref(CODA_OP_BWD)  */
+  CODA_OP_FWD_SWIGLU = 4,   /* coda_fwd_swiglu */
+  CODA_OP_BWD_SWIGLU = 5    /* coda_bwd_swiglu */
 } coda_op_t;
 
 /* Forward arguments.
@@ -145,6 +147,59 @@ typedef struct {
   coda_dtype_t dW0_dtype;
 } coda_bwd_gemm0_args_t;
 
+/* SwiGLU on the chain's output (hotdry blog, section "成对激活的寄存器级融合":
+ * paired features sit in adjacent output columns, so the gated activation is
+ * applied in the epilogue that produces the pair). Column 2f of y is gate f and
+ * column 2f+1 is up f; F = N/2 features:
+ *     o_if = silu(y_i,2f) * y_i,2f+1,   silu(v) = v / (1 + exp(-v)).
+ * The forward is coda_fwd with GEMM1's epilogue also emitting o (from the fp32
+ * y; y itself is still stored, in bf16 as the backward takes it: chain.y_dtype
+ * must be CODA_BF16). N must be a multiple of 512. Workspace: as coda_fwd
+ * (coda_workspace_bytes(CODA_OP_FWD_SWIGLU, ...)). */
+typedef struct {
+  coda_fwd_args_t chain; /* as for coda_fwd */
+  void* o;               /* out: [M, N/2] in o_dtype */
+  coda_dtype_t o_dtype;
+} coda_fwd_swiglu_args_t;
+
+/* Backward of the SwiGLU block for an output projection out = o @ W2 and
+ * L = <dOut, out> (same page, sections on pairwise activations — their backward
+ * is a dimension-expanding epilogue — and on the backward's GEMM-epilogue form,
+ * where the row statistic s is accumulated by the GEMM epilogue that produces
+ * the gradient of y):
+ *     dO  = dOut @ W2^T, its epilogue expanding each feature to its pair:
+ *           dY_i,2f = dO_if y_i,2f+1 silu'(y_i,2f),  dY_i,2f+1 = dO_if silu(y_i,2f)
+ *           and the partial sums of s_i = sum_n dY_in y_in (fp32 dY, saved bf16 y);
+ *     then the chain's backward on this dY: da, dgamma, dW1 (as coda_bwd), and
+ *     dW2 = o^T @ dOut.
+ *   in : dOut [M,E] bf16; W2 [F,E] bf16 (F = N/2); the forward's saved
+ *        o [M,F] bf16, y [M,N] bf16, h [M,D] bf16, g [M,D] bf16, r [M] f32;
+ *        gamma [D] bf16; W1 [D,N] bf16.
+ *   out: dY [M,N] bf16, da [M,D] in da_dtype, dgamma [D] f32, dW1 [D,N] in
+ *        dW1_dtype, dW2 [F,E] in dW2_dtype, s [M] f32.
+ * N a multiple of 512, E a multiple of 256 in [256, 2^20]. */
+typedef struct {
+  int64_t M, D, N, E;
+  const void* dOut;
+  const void* W2;
+  const void* o;
+  const void* y;
+  const void* h;
+  const void* g;
+  const float* r;
+  const void* gamma;
+  const void* W1;
+  void* dY;
+  void* da;
+  float* dgamma;
+  void* dW1;
+  void* dW2;
+  float* s;
+  coda_dtype_t da_dtype;
+  coda_dtype_t dW1_dtype;
+  coda_dtype_t dW2_dtype;
+} coda_bwd_swiglu_args_t;
+
 /* Operand layouts for coda_gemm. */
 typedef enum {
   CODA_ROW = 0, /* A: element (m,k) at A[m*lda + k];  B: element (k,n) at B[k*ldb + n] */
@@ -171,8 +226,9 @@ typedef struct {
 
 /* Bytes of device workspace `op` needs for these sizes (0 when none). The
  * workspace of the fused forward holds the partial sums of squares; the
- * fused backward holds bf16(r*g) [M,D] and the dgamma column partials; the
- * unfused baseline also holds its materialised intermediates. */
+ * fused backward holds bf16(r*g) [M,D] and the dgamma column partials (the
+ * SwiGLU backward also the partial sums of s); the unfused baseline also holds
+ * its materialised intermediates. */
 size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N);
 
 /* Host-only argument checks (no HIP call). Return CODA_OK or the first error. */
@@ -180,6 +236,8 @@ coda_status_t coda_validate_fwd(const coda_fwd_args_t* a, const void* ws, size_t
 coda_status_t coda_validate_bwd(const coda_bwd_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_gemm(const coda_gemm_args_t* a);
 coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a);
+coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const void* ws, size_t ws_bytes);
+coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const void* ws, size_t ws_bytes);
 /* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD or CODA_OP_BWD). */
 coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
 
@@ -215,6 +273,10 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
  *     G = dY@W1^T stored as bf16 in the workspace -> RMSNorm-backward row kernel
  *     (da, dgamma partials) -> dgamma combine -> same dW1 GEMM. */
 coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream);
+
+/* SwiGLU forward and backward (see coda_fwd_swiglu_args_t, coda_bwd_swiglu_args_t). */
+coda_status_t coda_fwd_swiglu(const coda_fwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream);
+coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward through the first GEMM (see coda_bwd_gemm0_args_t): dx, then dW0. */
 coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream);

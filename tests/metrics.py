@@ -10,7 +10,18 @@ Tolerances (fp32 accumulate, bf16 storage):
   index, so its bf16 operand r*g is rounded once before the MFMA. The bound is
   |x - ref| <= 1e-2 rms(ref) + sum_i ulp(r_i g_ij)/2 |dY_in| (the exact
   first-order effect of that one rounding); at M = 1 (a rank-1 product) nothing
-  averages it and it alone exceeds 1e-2 rms.
+  averages it and it alone exceeds 1e-2 rms. Where dY is itself produced in fp32
+  and rounded to bf16 before the product (the SwiGLU backward), the bound adds
+  sum_i |r_i g_ij| ulp(dY_in)/2.
+* SwiGLU o = silu(gate) up, computed from the fp32 y: with |y - y_ref| <= d =
+  1e-2 rms(y_ref) elementwise, |silu'| <= 1.1 and |silu''| <= 0.5 (Taylor with
+  remainder), |o - o_ref| <= d (1.1 |up| + |silu(gate)|) + d^2 (1.1 + 0.25 |up|)
+  + 0.25 d^3, plus 1e-5 |o_ref| for the fp32 evaluation itself.
+* dY of the SwiGLU backward and dW2 (plain products of bf16 operands with fp32
+  accumulation, rounded once): within 1e-4 rms plus half a bf16 ulp.
+* da and dgamma of the SwiGLU backward: dY is produced in fp32 and rounded to
+  bf16 before G = dY @ W1^T, so |dG_ij| <= A_ij = sum_n ulp(dY_in)/2 |W1_jn| and
+  the bounds add r_i |gamma_j| A_ij (da) and sum_i r_i |h_ij| A_ij (dgamma).
 """
 from __future__ import annotations
 
@@ -64,17 +75,45 @@ def bf16_one_ulp(x, ref) -> float:
     return float(np.max(np.abs(x - ref) / (bf16_ulp(ref) + 1e-6 * rms(ref))))
 
 
-def operand_rounding_allowance(g, r, dY, cols=None) -> np.ndarray:
-    """[D, C] bound sum_i ulp(r_i g_ij)/2 |dY_in| for the sampled columns n."""
-    a = 0.5 * bf16_ulp(f64(g) * f64(r)[:, None])
-    d = np.abs(f64(dY if cols is None else dY.index_select(1, torch.as_tensor(cols))))
-    return a.T @ d
+def operand_rounding_allowance(g, r, dY, cols=None, dY_rounded=False) -> np.ndarray:
+    """[D, C] bound sum_i ulp(r_i g_ij)/2 |dY_in| for the sampled columns n; with
+    dY_rounded (dY itself rounded to bf16 before the product, from an exact value)
+    also sum_i |r_i g_ij| ulp(dY_in)/2."""
+    rg = f64(g) * f64(r)[:, None]
+    d = f64(dY)
+    if cols is not None:
+        d = d[:, np.asarray(cols)]
+    allow = (0.5 * bf16_ulp(rg)).T @ np.abs(d)
+    if dY_rounded:
+        allow += np.abs(rg).T @ (0.5 * bf16_ulp(d))
+    return allow
+
+
+def dgrad_rounding_allowance(dY, W1, r, gamma, h, rows=None, cols=None) -> tuple:
+    """(da [R, D], dgamma [C]) first-order bounds of the bf16 rounding of dY in G = dY @ W1^T."""
+    u = 0.5 * bf16_ulp(dY)
+    aw = np.abs(f64(W1))
+    rd = f64(r)
+    ridx = np.arange(u.shape[0]) if rows is None else np.asarray(rows)
+    da = rd[ridx, None] * np.abs(f64(gamma))[None, :] * (u[ridx] @ aw.T)
+    jc = np.arange(aw.shape[0]) if cols is None else np.asarray(cols)
+    hd = f64(h)[:, jc]
+    dg = ((u @ aw[jc].T) * rd[:, None] * np.abs(hd)).sum(axis=0)
+    return da, dg
 
 
 def within_allowance(x, ref, allow, tol=Y_TOL) -> float:
     """Largest |x - ref| / (tol rms(ref) + allow); <= 1 passes."""
     x, ref = f64(x), f64(ref)
     return float(np.max(np.abs(x - ref) / (tol * rms(ref) + allow)))
+
+
+def swiglu_o_bound(y_ref, silu_gate, tol=Y_TOL) -> np.ndarray:
+    """Per-element bound on o's error given y's elementwise error tol rms(y_ref)."""
+    y = f64(y_ref)
+    d = tol * rms(y)
+    up, sg = np.abs(y[:, 1::2]), np.abs(f64(silu_gate))
+    return d * (1.1 * up + sg) + d * d * (1.1 + 0.25 * up) + 0.25 * d ** 3 + 1e-5 * sg * up
 
 
 def rne_bf16(t: torch.Tensor) -> torch.Tensor:

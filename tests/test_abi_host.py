@@ -35,13 +35,18 @@ def test_struct_layout_matches_c_header():
 #include "coda.h"
 #define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
 int main(void) {
-  printf("fwd %zu bwd %zu gemm %zu bwd0 %zu\n", sizeof(coda_fwd_args_t), sizeof(coda_bwd_args_t), sizeof(coda_gemm_args_t),
-         sizeof(coda_bwd_gemm0_args_t));
+  printf("fwd %zu bwd %zu gemm %zu bwd0 %zu fsw %zu bsw %zu\n", sizeof(coda_fwd_args_t), sizeof(coda_bwd_args_t),
+         sizeof(coda_gemm_args_t), sizeof(coda_bwd_gemm0_args_t), sizeof(coda_fwd_swiglu_args_t),
+         sizeof(coda_bwd_swiglu_args_t));
   O(coda_fwd_args_t, eps); O(coda_fwd_args_t, x); O(coda_fwd_args_t, y); O(coda_fwd_args_t, y_dtype);
   O(coda_bwd_args_t, dY); O(coda_bwd_args_t, s); O(coda_bwd_args_t, da_dtype); O(coda_bwd_args_t, dW1_dtype);
   O(coda_gemm_args_t, a_layout); O(coda_gemm_args_t, B); O(coda_gemm_args_t, b_layout); O(coda_gemm_args_t, c_dtype);
   O(coda_bwd_gemm0_args_t, dh); O(coda_bwd_gemm0_args_t, dW0); O(coda_bwd_gemm0_args_t, dx_dtype);
   O(coda_bwd_gemm0_args_t, dW0_dtype);
+  O(coda_fwd_swiglu_args_t, o); O(coda_fwd_swiglu_args_t, o_dtype);
+  O(coda_bwd_swiglu_args_t, E); O(coda_bwd_swiglu_args_t, dOut); O(coda_bwd_swiglu_args_t, W1);
+  O(coda_bwd_swiglu_args_t, dY); O(coda_bwd_swiglu_args_t, dW2); O(coda_bwd_swiglu_args_t, s);
+  O(coda_bwd_swiglu_args_t, da_dtype); O(coda_bwd_swiglu_args_t, dW2_dtype);
   return 0;
 }
 """
@@ -56,8 +61,11 @@ int main(void) {
     assert int(head[3]) == ctypes.sizeof(L.BwdArgs)
     assert int(head[5]) == ctypes.sizeof(L.GemmArgs)
     assert int(head[7]) == ctypes.sizeof(L.BwdGemm0Args)
+    assert int(head[9]) == ctypes.sizeof(L.FwdSwigluArgs)
+    assert int(head[11]) == ctypes.sizeof(L.BwdSwigluArgs)
     types = {"coda_fwd_args_t": L.FwdArgs, "coda_bwd_args_t": L.BwdArgs, "coda_gemm_args_t": L.GemmArgs,
-             "coda_bwd_gemm0_args_t": L.BwdGemm0Args}
+             "coda_bwd_gemm0_args_t": L.BwdGemm0Args, "coda_fwd_swiglu_args_t": L.FwdSwigluArgs,
+             "coda_bwd_swiglu_args_t": L.BwdSwigluArgs}
     for line in out[1:]:
         if not line:
             continue
@@ -76,6 +84,12 @@ def test_workspace_sizes():
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD, 0, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_FWD, M, 100, N) == 0
+    N2 = 1024  # SwiGLU needs N % 512 == 0; its backward adds the s partials Ps[M, (N/2)/64]
+    assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N2) == a256(M * (D // 64) * 4)
+    assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == (
+        a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4) + a256(M * (N2 // 2 // 64) * 4))
+    assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
+    assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0
 
 
 def _fwd(**kw):
@@ -167,6 +181,57 @@ def test_validate_bwd_gemm0():
         assert lib.coda_validate_bwd_gemm0(ctypes.byref(b)) == want, k
         assert lib.coda_bwd_gemm0(ctypes.byref(b), None) == want, k  # rejected before any launch
     assert lib.coda_validate_bwd_gemm0(None) == L.CODA_ERR_NULL
+
+
+def _fsw(**kw):
+    a = L.FwdSwigluArgs(_fwd(N=1024), fake(20), L.CODA_F32)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _bsw(**kw):
+    a = L.BwdSwigluArgs(300, 256, 1024, 512, *[fake(i) for i in range(15)], L.CODA_BF16, L.CODA_F32, L.CODA_BF16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_validate_swiglu():
+    lib = L.lib()
+
+    def vf(a, ws=WS, n=1 << 30):
+        return lib.coda_validate_fwd_swiglu(ctypes.byref(a), ws, n)
+
+    def vb(a, ws=WS, n=1 << 30):
+        return lib.coda_validate_bwd_swiglu(ctypes.byref(a), ws, n)
+
+    assert vf(_fsw()) == L.CODA_OK
+    assert vf(_fsw(o=None)) == L.CODA_ERR_NULL
+    assert vf(_fsw(o=ctypes.c_void_p(A + 4))) == L.CODA_ERR_ALIGN
+    assert vf(_fsw(o_dtype=5)) == L.CODA_ERR_ARG
+    assert vf(_fsw(chain=_fwd(N=768))) == L.CODA_ERR_SHAPE        # N not a multiple of 512
+    assert vf(_fsw(chain=_fwd(N=1024, y_dtype=L.CODA_F32))) == L.CODA_ERR_ARG  # y is saved in bf16
+    assert vf(_fsw(chain=_fwd(N=1024, eps=0.0))) == L.CODA_ERR_ARG
+    need = L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, 64, 256, 1024)
+    assert vf(_fsw(), WS, need - 1) == L.CODA_ERR_WORKSPACE
+    assert vf(_fsw(), WS, need) == L.CODA_OK
+    assert lib.coda_validate_fwd_swiglu(None, WS, need) == L.CODA_ERR_NULL
+
+    assert vb(_bsw()) == L.CODA_OK
+    for f in ("dOut", "W2", "o", "y", "h", "g", "r", "gamma", "W1", "dY", "da", "dgamma", "dW1", "dW2", "s"):
+        assert vb(_bsw(**{f: None})) == L.CODA_ERR_NULL, f
+        assert vb(_bsw(**{f: ctypes.c_void_p(A + 8)})) == L.CODA_ERR_ALIGN, f
+    for k, v in (("M", 0), ("N", 768), ("N", 256), ("E", 300), ("E", 0), ("D", 128)):
+        assert vb(_bsw(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
+    for k in ("da_dtype", "dW1_dtype", "dW2_dtype"):
+        assert vb(_bsw(**{k: 4})) == L.CODA_ERR_ARG, k
+    need = L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, 300, 256, 1024)
+    assert vb(_bsw(), WS, need - 1) == L.CODA_ERR_WORKSPACE
+    assert vb(_bsw(), WS, need) == L.CODA_OK
+    # rejected before any launch
+    assert lib.coda_fwd_swiglu(ctypes.byref(_fsw(o_dtype=9)), WS, need, None) == L.CODA_ERR_ARG
+    assert lib.coda_bwd_swiglu(ctypes.byref(_bsw(E=100)), WS, need, None) == L.CODA_ERR_SHAPE
 
 
 def test_entry_points_reject_without_launching():

@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "coda.h")
 
 CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA_ERR_ARG, CODA_ERR_HIP = range(7)
 CODA_BF16, CODA_F32 = 0, 1
-CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD = range(4)
+CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD, CODA_OP_FWD_SWIGLU, CODA_OP_BWD_SWIGLU = range(6)
 CODA_ROW, CODA_COL = 0, 1
 CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 4
 FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
@@ -54,6 +54,19 @@ class BwdGemm0Args(ctypes.Structure):
                 ("dx_dtype", c_int), ("dW0_dtype", c_int)]
 
 
+class FwdSwigluArgs(ctypes.Structure):
+    _fields_ = [("chain", FwdArgs), ("o", c_void_p), ("o_dtype", c_int)]
+
+
+class BwdSwigluArgs(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("D", c_int64), ("N", c_int64), ("E", c_int64),
+                ("dOut", c_void_p), ("W2", c_void_p), ("o", c_void_p),
+                ("y", c_void_p), ("h", c_void_p), ("g", c_void_p), ("r", c_void_p),
+                ("gamma", c_void_p), ("W1", c_void_p),
+                ("dY", c_void_p), ("da", c_void_p), ("dgamma", c_void_p), ("dW1", c_void_p), ("dW2", c_void_p),
+                ("s", c_void_p), ("da_dtype", c_int), ("dW1_dtype", c_int), ("dW2_dtype", c_int)]
+
+
 class CodaError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: status {status} ({status_string(status)})")
@@ -83,7 +96,11 @@ def lib() -> ctypes.CDLL:
                            ("coda_bwd_stage", [c_int, POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
                            ("coda_gemm", [POINTER(GemmArgs), c_void_p]),
                            ("coda_validate_bwd_gemm0", [POINTER(BwdGemm0Args)]),
-                           ("coda_bwd_gemm0", [POINTER(BwdGemm0Args), c_void_p])):
+                           ("coda_bwd_gemm0", [POINTER(BwdGemm0Args), c_void_p]),
+                           ("coda_validate_fwd_swiglu", [POINTER(FwdSwigluArgs), c_void_p, c_size_t]),
+                           ("coda_validate_bwd_swiglu", [POINTER(BwdSwigluArgs), c_void_p, c_size_t]),
+                           ("coda_fwd_swiglu", [POINTER(FwdSwigluArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_bwd_swiglu", [POINTER(BwdSwigluArgs), c_void_p, c_size_t, c_void_p])):
             fn = getattr(L, name)
             fn.restype = c_int
             fn.argtypes = argt
@@ -231,6 +248,89 @@ def bwd_gemm0(dh, x, W0, dx_dtype=torch.bfloat16, dW0_dtype=torch.bfloat16, out=
     a = _bwd_gemm0_args(dh, x, W0, out["dx"], out["dW0"])
     _check(lib().coda_bwd_gemm0(ctypes.byref(a), _stream(dev)), "coda_bwd_gemm0")
     return out
+
+
+def _fwd_swiglu_args(x, W0, z, gamma, W1, eps, out):
+    return FwdSwigluArgs(_fwd_args(x, W0, z, gamma, W1, eps, out["h"], out["g"], out["r"], out["y"]),
+                         _ptr(out["o"]), _dt(out["o"].dtype))
+
+
+def fwd_swiglu(x, W0, z, gamma, W1, eps, o_dtype=torch.bfloat16, ws=None, out=None):
+    """Forward of the chain followed by SwiGLU on y's interleaved (gate, up) columns.
+    Returns dict(h, g, r, y, o); y is bf16, o is [M, N/2] in o_dtype."""
+    M, D, N = x.shape[0], W1.shape[0], W1.shape[1]
+    dev = x.device
+    if out is None:
+        out = {"h": torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+               "g": torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+               "r": torch.empty(M, dtype=torch.float32, device=dev),
+               "y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+               "o": torch.empty(M, N // 2, dtype=o_dtype, device=dev)}
+    a = _fwd_swiglu_args(x, W0, z, gamma, W1, eps, out)
+    if ws is None:
+        ws = workspace(CODA_OP_FWD_SWIGLU, M, D, N, dev)
+    _check(lib().coda_fwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_fwd_swiglu")
+    return out
+
+
+def _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out):
+    M, E = dOut.shape
+    D, N = W1.shape
+    F = W2.shape[0]
+    _want(dOut, "dOut", torch.bfloat16, (M, E))
+    _want(W2, "W2", torch.bfloat16, (N // 2, E))
+    _want(o, "o", torch.bfloat16, (M, F))
+    _want(y, "y", torch.bfloat16, (M, N))
+    _want(h, "h", torch.bfloat16, (M, D))
+    _want(g, "g", torch.bfloat16, (M, D))
+    _want(r, "r", torch.float32, (M,))
+    _want(gamma, "gamma", torch.bfloat16, (D,))
+    _want(W1, "W1", torch.bfloat16, (D, N))
+    return BwdSwigluArgs(M, D, N, E, _ptr(dOut), _ptr(W2), _ptr(o), _ptr(y), _ptr(h), _ptr(g), _ptr(r),
+                         _ptr(gamma), _ptr(W1), _ptr(out["dY"]), _ptr(out["da"]), _ptr(out["dgamma"]),
+                         _ptr(out["dW1"]), _ptr(out["dW2"]), _ptr(out["s"]),
+                         _dt(out["da"].dtype), _dt(out["dW1"].dtype), _dt(out["dW2"].dtype))
+
+
+def bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_dtype=torch.bfloat16,
+               dW2_dtype=torch.bfloat16, ws=None, out=None):
+    """Backward of SwiGLU + output projection out = o @ W2 and of the chain under it.
+    Returns dict(dY, da, dgamma, dW1, dW2, s)."""
+    M, E = dOut.shape
+    D, N = W1.shape
+    dev = dOut.device
+    if out is None:
+        out = {"dY": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+               "da": torch.empty(M, D, dtype=da_dtype, device=dev),
+               "dgamma": torch.empty(D, dtype=torch.float32, device=dev),
+               "dW1": torch.empty(D, N, dtype=dW1_dtype, device=dev),
+               "dW2": torch.empty(N // 2, E, dtype=dW2_dtype, device=dev),
+               "s": torch.empty(M, dtype=torch.float32, device=dev)}
+    a = _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out)
+    if ws is None:
+        ws = workspace(CODA_OP_BWD_SWIGLU, M, D, N, dev)
+    _check(lib().coda_bwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_bwd_swiglu")
+    return out
+
+
+class BoundSwiglu:
+    """coda_fwd_swiglu / coda_bwd_swiglu with arguments marshalled once (benchmarks)."""
+
+    def __init__(self, kind, args, ws, keep):
+        self.kind, self.args, self.ws, self._keep = kind, args, ws, keep
+
+    def run(self, stream):
+        fn = lib().coda_fwd_swiglu if self.kind == "fwd" else lib().coda_bwd_swiglu
+        _check(fn(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}_swiglu")
+
+
+def bind_fwd_swiglu(x, W0, z, gamma, W1, eps, out, ws):
+    return BoundSwiglu("fwd", _fwd_swiglu_args(x, W0, z, gamma, W1, eps, out), ws, (x, W0, z, gamma, W1, out))
+
+
+def bind_bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, out, ws):
+    return BoundSwiglu("bwd", _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out), ws,
+                       (dOut, W2, o, y, h, g, r, gamma, W1, out))
 
 
 class BoundGemm0:

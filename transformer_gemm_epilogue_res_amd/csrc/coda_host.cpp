@@ -35,10 +35,6 @@ coda_status_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 size_t fwd_ws(int64_t M, int64_t D) { return align256(size_t(M) * size_t(ssq_cols(D)) * 4); }
 
-size_t bwd_ws(int64_t M, int64_t D) {
-  return align256(size_t(M) * size_t(D) * 2) + align256(size_t(dgamma_rows(M)) * size_t(D) * 4);
-}
-
 size_t unfused_fwd_ws(int64_t M, int64_t D) { return 2 * align256(size_t(M) * size_t(D) * 2); }
 
 size_t unfused_bwd_ws(int64_t M, int64_t D) {
@@ -80,6 +76,8 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_BWD: return bwd_ws(M, D);
     case CODA_OP_UNFUSED_FWD: return unfused_fwd_ws(M, D);
     case CODA_OP_UNFUSED_BWD: return unfused_bwd_ws(M, D);
+    case CODA_OP_FWD_SWIGLU: return N % 512 == 0 ? fwd_ws(M, D) : 0;
+    case CODA_OP_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? bwd_swiglu_ws(M, D, N) : 0;
   }
   return 0;
 }
@@ -129,6 +127,28 @@ coda_status_t coda_validate_gemm(const coda_gemm_args_t* a) {
   if (a->lda % 8 || a->ldb % 8 || a->ldc % 8) return CODA_ERR_ALIGN;
   if (a->lda > kMaxDim || a->ldb > kMaxDim || a->ldc > kMaxDim) return CODA_ERR_SHAPE;
   return CODA_OK;
+}
+
+coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const void* ws, size_t ws_bytes) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  coda_status_t st = coda_validate_fwd(&a->chain, ws, ws_bytes);
+  if (st != CODA_OK) return st;
+  const void* ps[] = {a->o};
+  if ((st = check_ptrs(ps, 1)) != CODA_OK) return st;
+  if (a->chain.N % 512) return CODA_ERR_SHAPE;
+  if (a->chain.y_dtype != CODA_BF16 || !dtype_ok(a->o_dtype)) return CODA_ERR_ARG;
+  return CODA_OK;
+}
+
+coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const void* ws, size_t ws_bytes) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->dOut, a->W2, a->o, a->y, a->h, a->g, a->r, a->gamma, a->W1, a->dY, a->da, a->dgamma,
+                      a->dW1, a->dW2, a->s};
+  coda_status_t st = check_ptrs(ps, 15);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 512) return CODA_ERR_SHAPE;
+  if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype) || !dtype_ok(a->dW2_dtype)) return CODA_ERR_ARG;
+  return check_ws(ws, ws_bytes, bwd_swiglu_ws(a->M, a->D, a->N));
 }
 
 coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a) {

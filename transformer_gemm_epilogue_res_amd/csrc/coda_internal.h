@@ -30,8 +30,19 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Column count of the forward's sum-of-squares partials P[M, D / kWaveTileN].
 inline int64_t ssq_cols(int64_t D) { return D / kWaveTileN; }
+// Column count of the SwiGLU backward's s partials Ps[M, (N / 2) / kWaveTileN].
+inline int64_t swiglu_s_cols(int64_t N) { return (N / 2) / kWaveTileN; }
 // Row count of the fused backward's dgamma partials Pg[ceil(M / kWaveTileM), D].
 inline int64_t dgamma_rows(int64_t M) { return ceil_div(M, kWaveTileM); }
+
+// Fused backward workspace: bf16(r g) [M, D], then Pg.
+inline size_t bwd_ws(int64_t M, int64_t D) {
+  return align256(size_t(M) * size_t(D) * 2) + align256(size_t(dgamma_rows(M)) * size_t(D) * 4);
+}
+// SwiGLU backward workspace: the fused backward's, then the s partials Ps.
+inline size_t bwd_swiglu_ws(int64_t M, int64_t D, int64_t N) {
+  return bwd_ws(M, D) + align256(size_t(M) * size_t(swiglu_s_cols(N)) * 4);
+}
 
 }  // namespace coda
 

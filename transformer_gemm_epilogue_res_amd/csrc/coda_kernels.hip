@@ -57,23 +57,32 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 struct StageBf16 {
   lds_char_t* base;
   int lane;
-  // The four values of tile (tm, tn) of this lane.
-  __device__ __forceinline__ void put(int tm, int tn, const f32x4_t& v) const {
+  // Eight bytes of row 16 tm + l % 16 at byte 8 (4 tn + l / 16) of the staged row.
+  __device__ __forceinline__ void put_raw(int tm, int tn, u32x2_t p) const {
     const int li = lane & 15, lg = lane >> 4;
     const int row = 16 * tm + li, c = 2 * tn + (lg >> 1);
-    const uint2 p = pack4_bf16(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<LDS_AS u32x2_t*>(base + row * 128 + ((c ^ (row & 7)) << 4) + (lg & 1) * 8) = u32x2_t{p.x, p.y};
+    *reinterpret_cast<LDS_AS u32x2_t*>(base + row * 128 + ((c ^ (row & 7)) << 4) + (lg & 1) * 8) = p;
   }
-  // Rows mb .. mb+127 (those below M), columns nb .. nb+63 of out[., ldc].
-  __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
+  // The four values of tile (tm, tn) of this lane.
+  __device__ __forceinline__ void put(int tm, int tn, const f32x4_t& v) const {
+    const uint2 p = pack4_bf16(v[0], v[1], v[2], v[3]);
+    put_raw(tm, tn, u32x2_t{p.x, p.y});
+  }
+  // Staged rows to rows mb .. mb+127 (those below M) of out, row stride ldb
+  // bytes, starting at byte column cb.
+  __device__ __forceinline__ void flush_raw(char* out, int64_t ldb, int64_t mb, int64_t cb, int64_t M) const {
     const int c = lane & 7;
 #pragma unroll
     for (int q = 0; q < kWaveTileM / 8; ++q) {
       const int row = 8 * q + (lane >> 3);
       const u32x4_t v = *reinterpret_cast<const LDS_AS u32x4_t*>(base + row * 128 + ((c ^ (row & 7)) << 4));
       const int64_t i = mb + row;
-      if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldc + nb + 8 * c) = v;
+      if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldb + cb + 16 * c) = v;
     }
+  }
+  // Rows mb .. mb+127 (those below M), columns nb .. nb+63 of out[., ldc].
+  __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
+    flush_raw(reinterpret_cast<char*>(out), 2 * ldc, mb, 2 * nb, M);
   }
 };
 
@@ -187,6 +196,129 @@ struct EpiRowScale {
       for (int e = 0; e < 4; ++e) v[e] *= rr[tm];
       return v;
     });
+  }
+};
+
+// ---------------------------------------------------------------- SwiGLU
+// Column 2f of y is gate f and 2f+1 up f (blog, section "成对激活的寄存器级融合":
+// paired features in adjacent output columns). In the MFMA layout a lane holds
+// four adjacent columns 16 tn + 4 (l / 16) + {0..3} of a row, i.e. two whole
+// pairs, so the activation and its backward are lane-local.
+
+__device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+// Staging of a 128 x 32 bf16 block (64-byte rows; 16-byte chunk c of row r at
+// c ^ ((r >> 2) & 3), which spreads both passes over all 64 banks). put() takes
+// the two values of columns 8 tn + 2 (l / 16) + {0, 1} of row 16 tm + l % 16.
+struct StageBf16Half {
+  lds_char_t* base;
+  int lane;
+  __device__ __forceinline__ void put(int tm, int tn, float a, float b) const {
+    const int li = lane & 15, lg = lane >> 4;
+    const int row = 16 * tm + li;
+    *reinterpret_cast<LDS_AS uint32_t*>(base + row * 64 + ((tn ^ ((row >> 2) & 3)) << 4) + 4 * lg) = pack2_bf16(a, b);
+  }
+  __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
+    const int c = lane & 3;
+#pragma unroll
+    for (int q = 0; q < kWaveTileM / 16; ++q) {
+      const int row = 16 * q + (lane >> 2);
+      const u32x4_t v = *reinterpret_cast<const LDS_AS u32x4_t*>(base + row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+      const int64_t i = mb + row;
+      if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldc + nb + 8 * c) = v;
+    }
+  }
+};
+
+// GEMM1 epilogue with SwiGLU: y = r_i * acc (stored in bf16: the backward needs
+// the gate and up values) and o_if = silu(y_i,2f) * y_i,2f+1 from the fp32 y,
+// stored in fp32 (F32) or bf16.
+template <bool F32>
+struct EpiRowScaleSwiglu {
+  const float* r;
+  void* y;
+  void* o;
+  int64_t M, N;  // o has N / 2 columns
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
+    const int li = lane & 15;
+    float rr[kTM];
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      rr[tm] = i < M ? r[i] : 0.f;
+    }
+    store_block<false>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
+      f32x4_t v = acc[tm][tn];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= rr[tm];
+      return v;
+    });
+    const int64_t F = N / 2, ob = nb / 2;  // the wave's 32 columns of o start at nb / 2
+    const StageBf16Half st{stage, lane};
+    const StageBf16 sf{stage, lane};
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = rr[tm] * acc[tm][tn][e];
+        const float o0 = v[0] * sigmoidf_(v[0]) * v[1], o1 = v[2] * sigmoidf_(v[2]) * v[3];
+        if constexpr (F32) sf.put_raw(tm, tn, u32x2_t{__float_as_uint(o0), __float_as_uint(o1)});
+        else st.put(tm, tn, o0, o1);
+      }
+    }
+    // the wave's 128 x 32 block of o: fp32 rows are 128 bytes, as the bf16 y rows
+    if constexpr (F32) sf.flush_raw(static_cast<char*>(o), 4 * F, mb, 4 * ob, M);
+    else st.flush(static_cast<uint16_t*>(o), F, mb, ob, M);
+  }
+};
+
+// Epilogue of the output projection's data gradient dO = dOut @ W2^T with the
+// SwiGLU backward (the dimension-expanding step): for the four features
+// f = nb + 16 tn + 4 (l / 16) + {0..3} of a lane it reads the saved gate/up pairs
+// y[i, 2f], y[i, 2f+1] (16 contiguous bytes), writes
+//   dY[i, 2f] = dO up silu'(gate),  dY[i, 2f+1] = dO silu(gate)   (bf16)
+// and the row statistic's partial sum over the wave's 64 features,
+//   Ps[i, nb / 64] = sum over its 128 columns of dY y   (fp32 dY, bf16 y).
+struct EpiSwigluBwd {
+  const uint16_t* y;
+  uint16_t* dY;
+  float* Ps;
+  int64_t M, F, pcols;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t*) const {
+    const int li = lane & 15, lj = 4 * (lane >> 4);
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      const bool ok = i < M;
+      float part = 0.f;
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn) {
+        const int64_t c = i * (2 * F) + 2 * (nb + 16 * tn + lj);
+        float yv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (ok) unpack8_bf16(*reinterpret_cast<const uint4*>(y + c), yv);
+        float d[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gate = yv[2 * e], up = yv[2 * e + 1], dO = acc[tm][tn][e];
+          const float sg = sigmoidf_(gate);
+          d[2 * e] = dO * up * (sg * (1.0f + gate * (1.0f - sg)));
+          d[2 * e + 1] = dO * (gate * sg);
+          part += d[2 * e] * gate + d[2 * e + 1] * up;
+        }
+        if (ok) {
+          const uint2 lo = pack4_bf16(d[0], d[1], d[2], d[3]), hi = pack4_bf16(d[4], d[5], d[6], d[7]);
+          *reinterpret_cast<uint4*>(dY + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      }
+      // the 4 lanes l % 16 == li hold the rest of row i's 64 features
+      part += shfl_xor(part, 16);
+      part += shfl_xor(part, 32);
+      if (lane < 16 && ok) Ps[i * pcols + nb / kWaveTileN] = part;
+    }
   }
 };
 
@@ -386,6 +518,28 @@ __global__ __launch_bounds__(256) void dgamma_combine_kernel(const float* Pg, fl
   }
 }
 
+// SwiGLU backward: one 256-thread block per row i: s_i = sum_t Ps[i, t] (fixed
+// order) and gr_i = bf16(r_i g_i).
+__global__ __launch_bounds__(256) void scombine_gr_kernel(const float* Ps, const uint16_t* g, const float* r,
+                                                          float* s, uint16_t* gr, int64_t pcols, int64_t D) {
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  float acc = 0.f;
+  for (int64_t t = threadIdx.x; t < pcols; t += 256) acc += Ps[i * pcols + t];
+  const float tot = block_sum256(acc, red);
+  if (threadIdx.x == 0) s[i] = tot;
+  const float ri = r[i];
+  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
+  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
+  for (int64_t v = threadIdx.x; v < D / 8; v += 256) {
+    float f[8];
+    unpack8_bf16(gs[v], f);
+    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
+    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
+    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
 // Unfused: one block per row. h = t + z (fp32, stored bf16), r from the fp32 h,
 // n = bf16(r h gamma) for the second GEMM.
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* t, const uint16_t* z,
@@ -506,6 +660,14 @@ hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, h
   return hipGetLastError();
 }
 
+hipError_t bwd_dgrad(const coda_bwd_args_t* a, float* Pg, hipStream_t st) {
+  // G = dY @ W1^T: A = dY [M, N] (k contiguous), B(k=n, j) = W1[j, n] (k contiguous)
+  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
+  if (a->da_dtype == CODA_F32)
+    return launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
+  return launch_gemm<true, true>(pd, EpiRmsNormBwd<false>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
+}
+
 coda_status_t to_status(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
 
 }  // namespace coda
@@ -553,13 +715,7 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
   uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
   float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
   if (stage == 0) return to_status(bwd_rowstat(a, gr, st));
-  if (stage == 1) {
-    // G = dY @ W1^T: A = dY [M, N] (k contiguous), B(k=n, j) = W1[j, n] (k contiguous)
-    const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
-    if (a->da_dtype == CODA_F32)
-      return to_status(launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st));
-    return to_status(launch_gemm<true, true>(pd, EpiRmsNormBwd<false>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st));
-  }
+  if (stage == 1) return to_status(bwd_dgrad(a, Pg, st));
   if (stage == 2) return to_status(bwd_dgamma(Pg, dgamma_rows(a->M), a, st));
   return to_status(bwd_wgrad(a, gr, st));
 }
@@ -609,6 +765,45 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
   if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
   if ((e = bwd_dgamma(Pg, ceil_div(a->M, kUnfusedBwdRows), a, st)) != hipSuccess) return CODA_ERR_HIP;
   return to_status(bwd_wgrad(a, gr, st));
+}
+
+coda_status_t coda_fwd_swiglu(const coda_fwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  coda_status_t v = coda_validate_fwd_swiglu(a, ws, ws_bytes);
+  if (v != CODA_OK) return v;
+  const coda_fwd_args_t* c = &a->chain;
+  for (int s = 0; s < 2; ++s)  // GEMM0 with its epilogue, then r
+    if ((v = coda_fwd_stage(s, c, ws, ws_bytes, stream)) != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const GemmShape p1{c->M, c->N, c->D, c->g, c->D, c->W1, c->N};
+  if (a->o_dtype == CODA_F32)
+    return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<true>{c->r, c->y, a->o, c->M, c->N}, st));
+  return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<false>{c->r, c->y, a->o, c->M, c->N}, st));
+}
+
+coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  coda_status_t v = coda_validate_bwd_swiglu(a, ws, ws_bytes);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t F = a->N / 2, pcols = swiglu_s_cols(a->N);
+  uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
+  float* Ps = reinterpret_cast<float*>(ws_at(ws, bwd_ws(a->M, a->D)));
+  // dO = dOut @ W2^T with the SwiGLU-backward epilogue: A = dOut [M, E], B(k=e, f) = W2[f, e] (both k contiguous)
+  const GemmShape po{a->M, F, a->E, a->dOut, a->E, a->W2, a->E};
+  hipError_t e = launch_gemm<true, true>(po, EpiSwigluBwd{(const uint16_t*)a->y, (uint16_t*)a->dY, Ps, a->M, F, pcols}, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  hipLaunchKernelGGL(scombine_gr_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, Ps, (const uint16_t*)a->g, a->r, a->s,
+                     gr, pcols, a->D);
+  if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+  // the chain's backward on dY, with s and bf16(r g) already in place
+  const coda_bwd_args_t c{a->M, a->D, a->N, a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1,
+                          a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
+  float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
+  if ((e = bwd_dgrad(&c, Pg, st)) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_dgamma(Pg, dgamma_rows(a->M), &c, st)) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_wgrad(&c, gr, st)) != hipSuccess) return CODA_ERR_HIP;
+  // dW2 [F, E] = o^T @ dOut: A(m=f, k=i) = o[i, f] (m contiguous), B(k=i, n=e) = dOut[i, e] (n contiguous), K = M
+  const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
+  return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));
 }
 
 coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream) {

@@ -10,10 +10,11 @@ expectations" paragraph, and the kucoin article, "experimental results"):
 * every tensor has its own CPU ``torch.Generator`` seeded ``seed*100 + id``
   with ids x=1, W0=2, z=3, gamma=4, W1=5, dY=6 (row sample 7, dgamma column
   sample 8, dW1 column sample 9), and for the backward through the first GEMM
-  dh=10 (dW0 column sample 11);
+  dh=10 (dW0 column sample 11), and for the SwiGLU block's output projection
+  W2=12, dOut=13 (dW2 column sample 14);
 * each draw is fp32 ``randn`` scaled and then cast to bfloat16 (round to
-  nearest even): x, z, dY, dh ~ N(0, 1); W0 ~ N(0, 1/K0); W1 ~ N(0, 1/D)
-  (fan-in = rows of the ``[in, out]`` weight); gamma = 1 + 0.1 N(0, 1);
+  nearest even): x, z, dY, dh, dOut ~ N(0, 1); W0 ~ N(0, 1/K0); W1 ~ N(0, 1/D);
+  W2 ~ N(0, 1/F) (fan-in = rows of the ``[in, out]`` weight); gamma = 1 + 0.1 N(0, 1);
 * eps = 1e-5.
 
 W1's columns are read as interleaved gate/up pairs (column 2f = gate f,
@@ -28,7 +29,8 @@ import torch
 EPS = 1e-5
 
 IDS = {"x": 1, "W0": 2, "z": 3, "gamma": 4, "W1": 5, "dY": 6,
-       "rows": 7, "dgamma_cols": 8, "dw1_cols": 9, "dh": 10, "dw0_cols": 11}
+       "rows": 7, "dgamma_cols": 8, "dw1_cols": 9, "dh": 10, "dw0_cols": 11,
+       "W2": 12, "dOut": 13, "dw2_cols": 14}
 
 # name -> (M tokens, K0, D, N = 2 * ffn)
 CONFIGS = {
@@ -73,6 +75,14 @@ def output_grad(M: int, N: int, seed: int = 0) -> torch.Tensor:
 def upstream_grad(M: int, D: int, seed: int = 0) -> torch.Tensor:
     """dh [M,D] bf16 ~ N(0,1): a gradient of h for the backward through the first GEMM."""
     return _randn_bf16((M, D), seed, "dh")
+
+
+def swiglu_inputs(M: int, N: int, E: int, seed: int = 0) -> dict:
+    """Output projection of the SwiGLU block: W2 [N/2, E] bf16 ~ N(0, 2/N) and its
+    upstream gradient dOut [M, E] bf16 ~ N(0, 1)."""
+    F = N // 2
+    return {"W2": _randn_bf16((F, E), seed, "W2", scale=1.0 / math.sqrt(F)),
+            "dOut": _randn_bf16((M, E), seed, "dOut")}
 
 
 def sample(n: int, count: int, seed: int, name: str) -> torch.Tensor:
