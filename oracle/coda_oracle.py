@@ -65,6 +65,27 @@ and for an output projection out = o @ W2 (W2 [F, E]) with L = <dOut, out>:
 
 after which the chain's backward above continues with this dY.
 
+Cross-entropy on an LM-head GEMM (blog, section "五类 Epilogue 原语", the
+stateful-transform primitive: tile-level online log-sum-exp and cross-entropy
+statistics; kucoin, section "五つの「ブロック」": block log-sum-exp and the
+running max / sum-exp statistics, and section "CODAの機能": cross-entropy loss
+and its gradient are in scope). For hidden states h [M, D], an output weight
+W [V, D] (one row per vocabulary entry) and targets t [M]:
+
+    logits_iv = sum_d h_id W_vd                     (logits = h @ W^T)
+    lse_i     = m_i + log sum_v exp(logits_iv - m_i),  m_i = max_v logits_iv
+    loss_i    = lse_i - logits_i,t_i                (0 for a row whose target lies
+                                                     outside [0, V): an ignored row)
+
+and for L = sum_i dloss_i loss_i:
+
+    dlogits_iv = dloss_i (exp(logits_iv - lse_i) - [v = t_i])   (0 on ignored rows)
+    dh         = dlogits @ W
+    dW         = dlogits^T @ h
+
+The max shift is the textbook way to write log-sum-exp (exact in real
+arithmetic); the oracle takes it over the whole row, with no tiling.
+
 Matrix products use numpy's float64 matmul as a library primitive. Row subsets
 (``rows``) and column subsets are supported because rows of the forward are
 independent and the large configurations are checked on seeded samples.
@@ -232,4 +253,72 @@ def swiglu_backward(dOut, W2, y, o, rows=None, dw2_cols=None) -> dict:
         blk = np.arange(c0, min(M, c0 + 2048))
         dW2 += _take(o, blk).T @ _take(dOut, blk, ec)
     out["dW2"] = dW2
+    return out
+
+
+def log_sum_exp(L) -> np.ndarray:
+    """lse_i = m_i + log sum_v exp(L_iv - m_i) with m_i the row maximum (float64)."""
+    L = np.asarray(L, dtype=np.float64)
+    m = L.max(axis=1)
+    return m + np.log(np.exp(L - m[:, None]).sum(axis=1))
+
+
+def cross_entropy_logits(L, targets) -> dict:
+    """Per-row cross-entropy of logits L [R, V] against targets [R]: dict(lse, loss, valid);
+    rows with a target outside [0, V) are ignored (loss 0)."""
+    L = np.asarray(L, dtype=np.float64)
+    t = np.asarray(targets, dtype=np.int64)
+    V = L.shape[1]
+    valid = (t >= 0) & (t < V)
+    lse = log_sum_exp(L)
+    picked = np.where(valid, L[np.arange(L.shape[0]), np.where(valid, t, 0)], 0.0)
+    return {"lse": lse, "loss": np.where(valid, lse - picked, 0.0), "valid": valid}
+
+
+def lm_head_cross_entropy(h, W, targets, rows=None, chunk: int = 512) -> dict:
+    """Forward of loss_i = lse_i(h @ W^T) - (h @ W^T)_i,t_i for the given rows (all when None).
+    Returns float64 lse [R], loss [R], and the boolean valid [R]."""
+    Wd = f64(W)
+    t = np.asarray(targets, dtype=np.int64) if not hasattr(targets, "numpy") else targets.numpy().astype(np.int64)
+    M = len(t)
+    idx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = {"lse": [], "loss": [], "valid": []}
+    for c0 in range(0, len(idx), chunk):
+        sel = idx[c0:c0 + chunk]
+        r = cross_entropy_logits(_take(h, sel) @ Wd.T, t[sel])
+        for k in out:
+            out[k].append(r[k])
+    return {k: np.concatenate(v) for k, v in out.items()}
+
+
+def lm_head_cross_entropy_backward(h, W, targets, lse, dloss, rows=None, dw_rows=None, chunk: int = 512) -> dict:
+    """Backward of L = sum_i dloss_i loss_i for the saved lse [M]:
+
+    * ``rows``: rows i of dlogits [R, V] and dh [R, D] returned (all when None);
+    * ``dw_rows``: vocabulary rows v of dW [*, D] (sums over *all* M rows; all when None).
+    """
+    Wd = f64(W)
+    t = np.asarray(targets, dtype=np.int64) if not hasattr(targets, "numpy") else targets.numpy().astype(np.int64)
+    lse_d, dl = f64(lse), f64(dloss)
+    M, V = len(t), Wd.shape[0]
+
+    def dlogits(sel, vcols=None):
+        Wc = Wd if vcols is None else Wd[vcols]
+        L = _take(h, sel) @ Wc.T
+        P = np.exp(L - lse_d[sel, None])
+        tv = t[sel]
+        valid = (tv >= 0) & (tv < V)
+        cols = np.arange(V) if vcols is None else np.asarray(vcols)
+        onehot = (cols[None, :] == tv[:, None]).astype(np.float64)
+        return np.where(valid[:, None], dl[sel, None] * (P - onehot), 0.0)
+
+    idx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    dL = np.concatenate([dlogits(idx[c0:c0 + chunk]) for c0 in range(0, len(idx), chunk)])
+    out = {"dlogits": dL, "dh": dL @ Wd}
+    vc = np.arange(V) if dw_rows is None else np.asarray(dw_rows, dtype=np.int64)
+    dW = np.zeros((len(vc), Wd.shape[1]))
+    for c0 in range(0, M, chunk):
+        blk = np.arange(c0, min(M, c0 + chunk))
+        dW += dlogits(blk, vc).T @ _take(h, blk)
+    out["dW"] = dW
     return out

@@ -301,6 +301,108 @@ def test_swiglu_backward_finite_differences_and_subsets():
 
 # ------------------------------------------------------------ finite differences
 
+# ------------------------------------------------------- cross-entropy (LM head)
+
+def _ce_problem(M, D, V, seed, scale=2.0):
+    g = torch.Generator().manual_seed(seed)
+    h = torch.randn(M, D, generator=g).to(torch.bfloat16)
+    W = (torch.randn(V, D, generator=g) * (scale / D ** 0.5)).to(torch.bfloat16)
+    t = torch.randint(0, V, (M,), generator=g)
+    return h, W, t
+
+
+def test_cross_entropy_matches_torch():
+    h, W, t = _ce_problem(24, 64, 300, 1)
+    t[3] = -100                                    # torch's ignore index
+    ref = orc.lm_head_cross_entropy(h, W, t)
+    L = h.double() @ W.double().T
+    want = torch.nn.functional.cross_entropy(L, t, reduction="none", ignore_index=-100)
+    assert _relerr(ref["loss"], want.numpy()) < 1e-14
+    assert _relerr(ref["lse"], torch.logsumexp(L, dim=1).numpy()) < 1e-14
+    assert ref["loss"][3] == 0.0 and not ref["valid"][3]
+    # any target outside [0, V) is an ignored row
+    t2 = t.clone()
+    t2[5] = 300
+    assert orc.lm_head_cross_entropy(h, W, t2)["loss"][5] == 0.0
+
+
+def test_cross_entropy_brute_force_and_closed_forms():
+    # 50-digit log-sum-exp on small integer logits
+    rng = np.random.default_rng(3)
+    L = rng.integers(-30, 31, size=(4, 9)).astype(np.float64)
+    t = np.array([0, 8, 4, 2])
+    r = orc.cross_entropy_logits(L, t)
+    for i in range(4):
+        lse = mpmath.log(mpmath.fsum(mpmath.e ** mpmath.mpf(v) for v in L[i]))
+        assert abs(float(lse) - r["lse"][i]) <= 1e-14 * abs(float(lse))
+        assert abs(float(lse - mpmath.mpf(L[i, t[i]])) - r["loss"][i]) <= 1e-13
+    # uniform logits: loss = lse = log V
+    V = 1000
+    r = orc.cross_entropy_logits(np.full((2, V), 3.25), [7, 999])
+    assert np.allclose(r["loss"], np.log(V), rtol=0, atol=1e-13)
+    assert np.allclose(r["lse"], 3.25 + np.log(V), rtol=0, atol=1e-13)
+    # one dominant target logit: loss = log(1 + (V - 1) e^-s), to the rounding of lse (~ulp(s))
+    Ld = np.zeros((1, V))
+    for sh in (5.0, 50.0):
+        Ld[0, 17] = sh
+        got = orc.cross_entropy_logits(Ld, [17])["loss"][0]
+        assert abs(got - np.log1p((V - 1) * np.exp(-sh))) <= 4 * np.spacing(sh)
+    # shift invariance per row, no overflow at large logits
+    L = rng.standard_normal((3, 50)) * 4
+    a = orc.cross_entropy_logits(L, [1, 2, 3])
+    b = orc.cross_entropy_logits(L + np.array([[1000.0], [-1000.0], [0.5]]), [1, 2, 3])
+    assert np.all(np.isfinite(b["loss"])) and np.allclose(a["loss"], b["loss"], rtol=0, atol=1e-10)
+
+
+def test_cross_entropy_backward_matches_torch_autograd():
+    h, W, t = _ce_problem(20, 64, 260, 2)
+    t[0] = -100
+    dloss = torch.randn(20, generator=torch.Generator().manual_seed(5), dtype=torch.float64)
+    hd, Wd = h.double().requires_grad_(), W.double().requires_grad_()
+    loss = torch.nn.functional.cross_entropy(hd @ Wd.T, t, reduction="none", ignore_index=-100)
+    (loss * dloss).sum().backward()
+    f = orc.lm_head_cross_entropy(h, W, t)
+    b = orc.lm_head_cross_entropy_backward(h, W, t, f["lse"], dloss)
+    assert _relerr(b["dh"], hd.grad.numpy()) < 1e-12
+    assert _relerr(b["dW"], Wd.grad.numpy()) < 1e-12
+    # gradient rows of valid targets sum to zero; ignored rows are zero; dloss = 0 gives zero gradients
+    assert np.max(np.abs(b["dlogits"][1:].sum(axis=1))) < 1e-14
+    assert np.all(b["dlogits"][0] == 0)
+    z = orc.lm_head_cross_entropy_backward(h, W, t, f["lse"], np.zeros(20))
+    assert not np.any(z["dh"]) and not np.any(z["dW"])
+
+
+def test_cross_entropy_backward_finite_differences_and_subsets():
+    h, W, t = _ce_problem(6, 16, 40, 4)
+    dloss = np.random.default_rng(6).standard_normal(6)
+    hd, Wd = orc.f64(h), orc.f64(W)
+
+    def total(hh, WW):
+        return float((orc.cross_entropy_logits(hh @ WW.T, t.numpy())["loss"] * dloss).sum())
+
+    f = orc.lm_head_cross_entropy(h, W, t)
+    b = orc.lm_head_cross_entropy_backward(h, W, t, f["lse"], dloss)
+    e = 1e-6
+    for (i, j) in ((0, 0), (3, 7), (5, 15)):
+        hp, hm = hd.copy(), hd.copy()
+        hp[i, j] += e
+        hm[i, j] -= e
+        assert abs((total(hp, Wd) - total(hm, Wd)) / (2 * e) - b["dh"][i, j]) < 1e-7
+    for (v, j) in ((0, 0), (int(t[2]), 3), (39, 15)):
+        Wp, Wm = Wd.copy(), Wd.copy()
+        Wp[v, j] += e
+        Wm[v, j] -= e
+        assert abs((total(hd, Wp) - total(hd, Wm)) / (2 * e) - b["dW"][v, j]) < 1e-7
+    # row and vocabulary-row subsets equal the full computation
+    rows, vr = [1, 4], [0, 17, 39]
+    fs = orc.lm_head_cross_entropy(h, W, t, rows=rows)
+    assert np.array_equal(fs["loss"], f["loss"][rows]) and np.array_equal(fs["lse"], f["lse"][rows])
+    bs = orc.lm_head_cross_entropy_backward(h, W, t, f["lse"], dloss, rows=rows, dw_rows=vr)
+    assert np.allclose(bs["dh"], b["dh"][rows], rtol=0, atol=1e-15)
+    assert np.allclose(bs["dlogits"], b["dlogits"][rows], rtol=0, atol=1e-15)
+    assert np.allclose(bs["dW"], b["dW"][vr], rtol=0, atol=1e-14)
+
+
 def test_backward_finite_differences():
     M, K0, D, N = 6, 8, 16, 12
     x, W0, z, gamma, W1, dY, eps = (t.numpy() if isinstance(t, torch.Tensor) else t
@@ -454,3 +556,9 @@ def test_inputs_are_seeded_and_distributed_as_stated():
     rows = inputs.sample(8192, 256, 0, "rows")
     assert rows.tolist() == sorted(set(rows.tolist())) and len(rows) == 256
     assert inputs.sample(64, 256, 0, "rows").tolist() == list(range(64))
+    lm = inputs.lm_head_inputs(4096, 256, 512, seed=0)
+    assert torch.equal(lm["targets"], inputs.lm_head_inputs(4096, 256, 512, seed=0)["targets"])
+    assert lm["W"].shape == (512, 256) and abs(lm["W"].float().std().item() * 8 - 1) < 0.05   # 2/sqrt(D)
+    ign = (lm["targets"] == -100).float().mean().item()
+    assert 0.02 < ign < 0.04 and int(lm["targets"].max()) < 512
+    assert len(set(inputs.IDS.values())) == len(inputs.IDS)

@@ -11,10 +11,14 @@ expectations" paragraph, and the kucoin article, "experimental results"):
   with ids x=1, W0=2, z=3, gamma=4, W1=5, dY=6 (row sample 7, dgamma column
   sample 8, dW1 column sample 9), and for the backward through the first GEMM
   dh=10 (dW0 column sample 11), and for the SwiGLU block's output projection
-  W2=12, dOut=13 (dW2 column sample 14);
+  W2=12, dOut=13 (dW2 column sample 14), and for the cross-entropy LM head
+  h=15, W=16, targets=17, dloss=18, ignored rows=19 (dW row sample 20);
 * each draw is fp32 ``randn`` scaled and then cast to bfloat16 (round to
   nearest even): x, z, dY, dh, dOut ~ N(0, 1); W0 ~ N(0, 1/K0); W1 ~ N(0, 1/D);
   W2 ~ N(0, 1/F) (fan-in = rows of the ``[in, out]`` weight); gamma = 1 + 0.1 N(0, 1);
+* LM head: h ~ N(0, 1) (a normalised hidden state), W [V, D] ~ N(0, 4/D) (logits
+  of standard deviation 2: a peaked softmax), targets uniform in [0, V) with about
+  3 % of the rows set to -100 (ignored), dloss ~ N(0, 1) fp32 per row;
 * eps = 1e-5.
 
 W1's columns are read as interleaved gate/up pairs (column 2f = gate f,
@@ -30,9 +34,11 @@ EPS = 1e-5
 
 IDS = {"x": 1, "W0": 2, "z": 3, "gamma": 4, "W1": 5, "dY": 6,
        "rows": 7, "dgamma_cols": 8, "dw1_cols": 9, "dh": 10, "dw0_cols": 11,
-       "W2": 12, "dOut": 13, "dw2_cols": 14}
+       "W2": 12, "dOut": 13, "dw2_cols": 14,
+       "h_lm": 15, "W_lm": 16, "targets": 17, "dloss": 18, "ignored": 19, "dw_lm_rows": 20}
 
-# name -> (M tokens, K0, D, N = 2 * ffn)
+# name -> (M tokens, K0, D, N = 2 * ffn); the LM head of each model has V = 128256 outputs
+LM_VOCAB = 128256
 CONFIGS = {
     "tiny": dict(M=64, K0=256, D=256, N=512),
     "llama3_1b": dict(M=8192, K0=2048, D=2048, N=16384),
@@ -83,6 +89,17 @@ def swiglu_inputs(M: int, N: int, E: int, seed: int = 0) -> dict:
     F = N // 2
     return {"W2": _randn_bf16((F, E), seed, "W2", scale=1.0 / math.sqrt(F)),
             "dOut": _randn_bf16((M, E), seed, "dOut")}
+
+
+def lm_head_inputs(M: int, D: int, V: int, seed: int = 0) -> dict:
+    """h [M, D] bf16, W [V, D] bf16, targets [M] int64 (about 3 % = -100), dloss [M] fp32."""
+    t = torch.randint(0, V, (M,), generator=generator(seed, "targets"), dtype=torch.int64)
+    ign = torch.rand(M, generator=generator(seed, "ignored")) < 0.03
+    t[ign] = -100
+    return {"h": _randn_bf16((M, D), seed, "h_lm"),
+            "W": _randn_bf16((V, D), seed, "W_lm", scale=2.0 / math.sqrt(D)),
+            "targets": t,
+            "dloss": torch.randn(M, generator=generator(seed, "dloss"), dtype=torch.float32)}
 
 
 def sample(n: int, count: int, seed: int, name: str) -> torch.Tensor:
