@@ -124,6 +124,7 @@ def main():
     ap.add_argument("--cpu-cols", type=int, default=64)
     ap.add_argument("--no-unfused", action="store_true", help="skip timing the unfused baseline")
     ap.add_argument("--no-swiglu", action="store_true", help="skip timing the SwiGLU block")
+    ap.add_argument("--no-ce", action="store_true", help="skip timing the cross-entropy LM head")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many bytes (a reference kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -281,6 +282,39 @@ def main():
         log(f"[bench] SwiGLU block: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {swiglu['tflops']} TFLOP/s")
         del W2, dOut, so, sbo, SF, SB
 
+    # Cross-entropy on the Llama-3-8B LM head (coda_ce_fwd / coda_ce_bwd, V = 128256):
+    # reported beside the headline step.
+    ce = None
+    if not args.no_ce:
+        V = inputs.LM_VOCAB
+        hl, Wl = rnd(M, D), rnd(V, D, scale=2.0 / D ** 0.5)
+        tg = torch.randint(0, V, (M,), generator=gen, device=dev)
+        dloss = torch.randn(M, generator=gen, device=dev)
+        cfo = {"lse": torch.empty(M, dtype=torch.float32, device=dev),
+               "loss": torch.empty(M, dtype=torch.float32, device=dev)}
+        cbo = {"dlogits": torch.empty(M, V, dtype=bf, device=dev), "dh": torch.empty(M, D, dtype=bf, device=dev),
+               "dW": torch.empty(V, D, dtype=bf, device=dev)}
+        CF = L.bind_ce_fwd(hl, Wl, tg, cfo, L.workspace(L.CODA_OP_CE_FWD, M, D, V, dev))
+        CB = L.bind_ce_bwd(hl, Wl, tg, cfo["lse"], dloss, cbo)
+        t = {}
+        for name, obj in (("fwd", CF), ("bwd", CB)):
+            for _ in range(2):
+                obj.run(sp)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                obj.run(sp)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t[name] = a.elapsed_time(b) / args.steps
+        ce_f, ce_b = 2 * M * D * V, 3 * 2 * M * D * V   # logits; recomputed logits, dh, dW
+        ce = {"V": V, "fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
+              "fwd_tflops": round(ce_f / t["fwd"] / 1e9, 1), "bwd_tflops": round(ce_b / t["bwd"] / 1e9, 1),
+              "tflops": round((ce_f + ce_b) / (t["fwd"] + t["bwd"]) / 1e9, 1)}
+        ce["pct_peak"] = round(100 * ce["tflops"] / PEAK_BF16_TFLOPS, 2)
+        log(f"[bench] cross-entropy LM head: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {ce['tflops']} TFLOP/s")
+        del hl, Wl, tg, dloss, cfo, cbo, CF, CB
+
     unfused = None
     if not args.no_unfused:
         log("[bench] timing the unfused baseline")
@@ -324,7 +358,7 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
                 "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
-        "bwd_gemm0": bwd_gemm0, "swiglu": swiglu,
+        "bwd_gemm0": bwd_gemm0, "swiglu": swiglu, "cross_entropy": ce,
         "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

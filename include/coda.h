@@ -76,7 +76,9 @@ typedef enum {
   CODA_OP_UNFUSED_FWD = 2,  /* coda_unfused_ref(CODA_OP_FWD)  */
   CODA_OP_UNFUSED_BWD = 3,  /* coda_unfused_ref(CODA_OP_BWD)  */
   CODA_OP_FWD_SWIGLU = 4,   /* coda_fwd_swiglu */
-  CODA_OP_BWD_SWIGLU = 5    /* coda_bwd_swiglu */
+  CODA_OP_BWD_SWIGLU = 5,   /* coda_bwd_swiglu */
+  CODA_OP_CE_FWD = 6,       /* coda_ce_fwd (pass the vocabulary size V as N) */
+  CODA_OP_CE_BWD = 7        /* coda_ce_bwd (none) */
 } coda_op_t;
 
 /* Forward arguments.
@@ -200,6 +202,52 @@ typedef struct {
   coda_dtype_t dW2_dtype;
 } coda_bwd_swiglu_args_t;
 
+/* Cross-entropy on an LM-head GEMM (hotdry blog, section "五类 Epilogue 原语": the
+ * stateful-transform primitive keeps tile-level online log-sum-exp and cross-entropy
+ * statistics; kucoin, section "五つの「ブロック」": block log-sum-exp, running max and
+ * sum-exp). For hidden states h [M, D], an output weight W [V, D] (one row per
+ * vocabulary entry, the nn.Linear / tied-embedding layout) and targets t [M]:
+ *     logits = h @ W^T (never stored),
+ *     lse_i  = log sum_v exp(logits_iv),   loss_i = lse_i - logits_i,t_i.
+ * The logits GEMM's epilogue reduces each (row, 64-column) tile to its max m and
+ * sum exp(logit - m) and picks out the target logit; a row kernel combines the
+ * tile statistics in a fixed order. A target outside [0, V) marks an ignored row:
+ * its loss is 0 (lse is still written). D and V multiples of 256 in [256, 2^20]
+ * (Llama-3's V = 128256 = 501 * 256).
+ *   in : h [M,D] bf16, W [V,D] bf16, targets [M] int64.
+ *   out: lse [M] f32, loss [M] f32 (per row; a mean is the caller's sum / count).
+ * Workspace: coda_workspace_bytes(CODA_OP_CE_FWD, M, D, V). */
+typedef struct {
+  int64_t M, D, V;
+  const void* h;
+  const void* W;
+  const int64_t* targets;
+  float* lse;
+  float* loss;
+} coda_ce_fwd_args_t;
+
+/* Backward of L = sum_i dloss_i loss_i for the forward's lse (same sections; the
+ * backward of a tile-local epilogue is again tile-local, on the logits recomputed by
+ * the same GEMM):
+ *     dlogits_iv = dloss_i (exp(logits_iv - lse_i) - [v = t_i]), 0 on ignored rows,
+ *     dh = dlogits @ W,   dW = dlogits^T @ h.
+ *   in : h, W, targets as in the forward; lse [M] f32 (the forward's); dloss [M] f32.
+ *   out: dlogits [M,V] bf16 (the operand of the two products, written as an output),
+ *        dh [M,D] in dh_dtype, dW [V,D] in dW_dtype. No workspace. */
+typedef struct {
+  int64_t M, D, V;
+  const void* h;
+  const void* W;
+  const int64_t* targets;
+  const float* lse;
+  const float* dloss;
+  void* dlogits;
+  void* dh;
+  void* dW;
+  coda_dtype_t dh_dtype;
+  coda_dtype_t dW_dtype;
+} coda_ce_bwd_args_t;
+
 /* Operand layouts for coda_gemm. */
 typedef enum {
   CODA_ROW = 0, /* A: element (m,k) at A[m*lda + k];  B: element (k,n) at B[k*ldb + n] */
@@ -238,6 +286,8 @@ coda_status_t coda_validate_gemm(const coda_gemm_args_t* a);
 coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a);
 coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const void* ws, size_t ws_bytes);
+coda_status_t coda_validate_ce_fwd(const coda_ce_fwd_args_t* a, const void* ws, size_t ws_bytes);
+coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a);
 /* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD or CODA_OP_BWD). */
 coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
 
@@ -277,6 +327,10 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
 /* SwiGLU forward and backward (see coda_fwd_swiglu_args_t, coda_bwd_swiglu_args_t). */
 coda_status_t coda_fwd_swiglu(const coda_fwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream);
 coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Cross-entropy forward and backward (see coda_ce_fwd_args_t, coda_ce_bwd_args_t). */
+coda_status_t coda_ce_fwd(const coda_ce_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
+coda_status_t coda_ce_bwd(const coda_ce_bwd_args_t* a, void* stream);
 
 /* Backward through the first GEMM (see coda_bwd_gemm0_args_t): dx, then dW0. */
 coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream);

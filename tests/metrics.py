@@ -19,6 +19,12 @@ Tolerances (fp32 accumulate, bf16 storage):
   + 0.25 d^3, plus 1e-5 |o_ref| for the fp32 evaluation itself.
 * dY of the SwiGLU backward and dW2 (plain products of bf16 operands with fp32
   accumulation, rounded once): within 1e-4 rms plus half a bf16 ulp.
+* cross-entropy: lse and loss (fp32 logits of exact bf16 products, never rounded)
+  within 1e-4 rms; dlogits (bf16) faithfully rounded: within one bf16 ulp of the
+  exact value (+1e-4 rms), because the softmax makes a few elements much larger
+  than the rms and their fp32 error, though far below an ulp, can tip the
+  rounding; dh and dW within 1e-4 rms plus sum ulp(dlogits) |W| (resp. |h|), the
+  first-order effect of that rounding.
 * da and dgamma of the SwiGLU backward: dY is produced in fp32 and rounded to
   bf16 before G = dY @ W1^T, so |dG_ij| <= A_ij = sum_n ulp(dY_in)/2 |W1_jn| and
   the bounds add r_i |gamma_j| A_ij (da) and sum_i r_i |h_ij| A_ij (dgamma).
@@ -66,6 +72,14 @@ def bf16_within(x, ref, tol=Y_TOL) -> float:
     """Largest |x - ref| / (tol rms(ref) + ulp/2 of max(|x|,|ref|)); <= 1 passes."""
     x, ref = f64(x), f64(ref)
     bound = tol * rms(ref) + 0.5 * bf16_ulp(np.maximum(np.abs(x), np.abs(ref)))
+    return float(np.max(np.abs(x - ref) / bound))
+
+
+def bf16_faithful(x, ref, tol) -> float:
+    """Largest |x - ref| / (ulp of max(|x|,|ref|) + tol rms(ref)); <= 1 passes: x is one of the two
+    bf16 neighbours of ref (up to tol rms)."""
+    x, ref = f64(x), f64(ref)
+    bound = tol * rms(ref) + bf16_ulp(np.maximum(np.abs(x), np.abs(ref)))
     return float(np.max(np.abs(x - ref) / bound))
 
 

@@ -35,9 +35,10 @@ def test_struct_layout_matches_c_header():
 #include "coda.h"
 #define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
 int main(void) {
-  printf("fwd %zu bwd %zu gemm %zu bwd0 %zu fsw %zu bsw %zu\n", sizeof(coda_fwd_args_t), sizeof(coda_bwd_args_t),
-         sizeof(coda_gemm_args_t), sizeof(coda_bwd_gemm0_args_t), sizeof(coda_fwd_swiglu_args_t),
-         sizeof(coda_bwd_swiglu_args_t));
+  printf("fwd %zu bwd %zu gemm %zu bwd0 %zu fsw %zu bsw %zu cef %zu ceb %zu\n", sizeof(coda_fwd_args_t),
+         sizeof(coda_bwd_args_t), sizeof(coda_gemm_args_t), sizeof(coda_bwd_gemm0_args_t),
+         sizeof(coda_fwd_swiglu_args_t), sizeof(coda_bwd_swiglu_args_t), sizeof(coda_ce_fwd_args_t),
+         sizeof(coda_ce_bwd_args_t));
   O(coda_fwd_args_t, eps); O(coda_fwd_args_t, x); O(coda_fwd_args_t, y); O(coda_fwd_args_t, y_dtype);
   O(coda_bwd_args_t, dY); O(coda_bwd_args_t, s); O(coda_bwd_args_t, da_dtype); O(coda_bwd_args_t, dW1_dtype);
   O(coda_gemm_args_t, a_layout); O(coda_gemm_args_t, B); O(coda_gemm_args_t, b_layout); O(coda_gemm_args_t, c_dtype);
@@ -47,6 +48,9 @@ int main(void) {
   O(coda_bwd_swiglu_args_t, E); O(coda_bwd_swiglu_args_t, dOut); O(coda_bwd_swiglu_args_t, W1);
   O(coda_bwd_swiglu_args_t, dY); O(coda_bwd_swiglu_args_t, dW2); O(coda_bwd_swiglu_args_t, s);
   O(coda_bwd_swiglu_args_t, da_dtype); O(coda_bwd_swiglu_args_t, dW2_dtype);
+  O(coda_ce_fwd_args_t, V); O(coda_ce_fwd_args_t, targets); O(coda_ce_fwd_args_t, loss);
+  O(coda_ce_bwd_args_t, dloss); O(coda_ce_bwd_args_t, dW); O(coda_ce_bwd_args_t, dh_dtype);
+  O(coda_ce_bwd_args_t, dW_dtype);
   return 0;
 }
 """
@@ -63,9 +67,12 @@ int main(void) {
     assert int(head[7]) == ctypes.sizeof(L.BwdGemm0Args)
     assert int(head[9]) == ctypes.sizeof(L.FwdSwigluArgs)
     assert int(head[11]) == ctypes.sizeof(L.BwdSwigluArgs)
+    assert int(head[13]) == ctypes.sizeof(L.CeFwdArgs)
+    assert int(head[15]) == ctypes.sizeof(L.CeBwdArgs)
     types = {"coda_fwd_args_t": L.FwdArgs, "coda_bwd_args_t": L.BwdArgs, "coda_gemm_args_t": L.GemmArgs,
              "coda_bwd_gemm0_args_t": L.BwdGemm0Args, "coda_fwd_swiglu_args_t": L.FwdSwigluArgs,
-             "coda_bwd_swiglu_args_t": L.BwdSwigluArgs}
+             "coda_bwd_swiglu_args_t": L.BwdSwigluArgs, "coda_ce_fwd_args_t": L.CeFwdArgs,
+             "coda_ce_bwd_args_t": L.CeBwdArgs}
     for line in out[1:]:
         if not line:
             continue
@@ -90,6 +97,10 @@ def test_workspace_sizes():
         a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4) + a256(M * (N2 // 2 // 64) * 4))
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0
+    V = 128256  # cross-entropy: tile statistics (m, l) [M, V/64] and the target logits [M]
+    assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, V) == a256(M * (V // 64) * 8) + a256(M * 4)
+    assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, 1000) == 0
+    assert L.workspace_bytes(L.CODA_OP_CE_BWD, M, D, V) == 0
 
 
 def _fwd(**kw):
@@ -232,6 +243,30 @@ def test_validate_swiglu():
     # rejected before any launch
     assert lib.coda_fwd_swiglu(ctypes.byref(_fsw(o_dtype=9)), WS, need, None) == L.CODA_ERR_ARG
     assert lib.coda_bwd_swiglu(ctypes.byref(_bsw(E=100)), WS, need, None) == L.CODA_ERR_SHAPE
+
+
+def test_validate_cross_entropy():
+    lib = L.lib()
+    f = L.CeFwdArgs(300, 256, 1024, *[fake(i) for i in range(5)])
+    need = L.workspace_bytes(L.CODA_OP_CE_FWD, 300, 256, 1024)
+    assert lib.coda_validate_ce_fwd(ctypes.byref(f), WS, need) == L.CODA_OK
+    assert lib.coda_validate_ce_fwd(ctypes.byref(f), WS, need - 1) == L.CODA_ERR_WORKSPACE
+    assert lib.coda_validate_ce_fwd(None, WS, need) == L.CODA_ERR_NULL
+    for k, v, want in (("M", 0, L.CODA_ERR_SHAPE), ("V", 1000, L.CODA_ERR_SHAPE), ("D", 128, L.CODA_ERR_SHAPE),
+                       ("targets", None, L.CODA_ERR_NULL), ("loss", ctypes.c_void_p(A + 4), L.CODA_ERR_ALIGN)):
+        g = L.CeFwdArgs.from_buffer_copy(f)
+        setattr(g, k, v)
+        assert lib.coda_validate_ce_fwd(ctypes.byref(g), WS, need) == want, k
+        assert lib.coda_ce_fwd(ctypes.byref(g), WS, need, None) == want, k  # rejected before any launch
+    b = L.CeBwdArgs(300, 256, 1024, *[fake(i) for i in range(8)], L.CODA_BF16, L.CODA_F32)
+    assert lib.coda_validate_ce_bwd(ctypes.byref(b)) == L.CODA_OK
+    for k, v, want in (("V", 0, L.CODA_ERR_SHAPE), ("dlogits", None, L.CODA_ERR_NULL),
+                       ("dW", ctypes.c_void_p(A + 8), L.CODA_ERR_ALIGN), ("dh_dtype", 3, L.CODA_ERR_ARG),
+                       ("dW_dtype", -1, L.CODA_ERR_ARG)):
+        c = L.CeBwdArgs.from_buffer_copy(b)
+        setattr(c, k, v)
+        assert lib.coda_validate_ce_bwd(ctypes.byref(c)) == want, k
+        assert lib.coda_ce_bwd(ctypes.byref(c), None) == want, k
 
 
 def test_entry_points_reject_without_launching():

@@ -20,7 +20,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "coda.h")
 
 CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA_ERR_ARG, CODA_ERR_HIP = range(7)
 CODA_BF16, CODA_F32 = 0, 1
-CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD, CODA_OP_FWD_SWIGLU, CODA_OP_BWD_SWIGLU = range(6)
+(CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD, CODA_OP_FWD_SWIGLU, CODA_OP_BWD_SWIGLU,
+ CODA_OP_CE_FWD, CODA_OP_CE_BWD) = range(8)
 CODA_ROW, CODA_COL = 0, 1
 CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 4
 FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
@@ -67,6 +68,17 @@ class BwdSwigluArgs(ctypes.Structure):
                 ("s", c_void_p), ("da_dtype", c_int), ("dW1_dtype", c_int), ("dW2_dtype", c_int)]
 
 
+class CeFwdArgs(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("D", c_int64), ("V", c_int64), ("h", c_void_p), ("W", c_void_p),
+                ("targets", c_void_p), ("lse", c_void_p), ("loss", c_void_p)]
+
+
+class CeBwdArgs(ctypes.Structure):
+    _fields_ = [("M", c_int64), ("D", c_int64), ("V", c_int64), ("h", c_void_p), ("W", c_void_p),
+                ("targets", c_void_p), ("lse", c_void_p), ("dloss", c_void_p),
+                ("dlogits", c_void_p), ("dh", c_void_p), ("dW", c_void_p), ("dh_dtype", c_int), ("dW_dtype", c_int)]
+
+
 class CodaError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: status {status} ({status_string(status)})")
@@ -100,7 +112,11 @@ def lib() -> ctypes.CDLL:
                            ("coda_validate_fwd_swiglu", [POINTER(FwdSwigluArgs), c_void_p, c_size_t]),
                            ("coda_validate_bwd_swiglu", [POINTER(BwdSwigluArgs), c_void_p, c_size_t]),
                            ("coda_fwd_swiglu", [POINTER(FwdSwigluArgs), c_void_p, c_size_t, c_void_p]),
-                           ("coda_bwd_swiglu", [POINTER(BwdSwigluArgs), c_void_p, c_size_t, c_void_p])):
+                           ("coda_bwd_swiglu", [POINTER(BwdSwigluArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_validate_ce_fwd", [POINTER(CeFwdArgs), c_void_p, c_size_t]),
+                           ("coda_validate_ce_bwd", [POINTER(CeBwdArgs)]),
+                           ("coda_ce_fwd", [POINTER(CeFwdArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_ce_bwd", [POINTER(CeBwdArgs), c_void_p])):
             fn = getattr(L, name)
             fn.restype = c_int
             fn.argtypes = argt
@@ -331,6 +347,81 @@ def bind_fwd_swiglu(x, W0, z, gamma, W1, eps, out, ws):
 def bind_bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, out, ws):
     return BoundSwiglu("bwd", _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out), ws,
                        (dOut, W2, o, y, h, g, r, gamma, W1, out))
+
+
+def _ce_fwd_args(h, W, targets, lse, loss):
+    M, D = h.shape
+    V = W.shape[0]
+    _want(h, "h", torch.bfloat16, (M, D))
+    _want(W, "W", torch.bfloat16, (V, D))
+    _want(targets, "targets", torch.int64, (M,))
+    _want(lse, "lse", torch.float32, (M,))
+    _want(loss, "loss", torch.float32, (M,))
+    return CeFwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(loss))
+
+
+def ce_fwd(h, W, targets, ws=None, out=None):
+    """Cross-entropy of the LM-head logits h @ W^T against targets (int64; outside [0, V) = ignored).
+    Returns dict(lse, loss), both [M] fp32."""
+    M, D = h.shape
+    V = W.shape[0]
+    dev = h.device
+    if out is None:
+        out = {"lse": torch.empty(M, dtype=torch.float32, device=dev),
+               "loss": torch.empty(M, dtype=torch.float32, device=dev)}
+    a = _ce_fwd_args(h, W, targets, out["lse"], out["loss"])
+    if ws is None:
+        ws = workspace(CODA_OP_CE_FWD, M, D, V, dev)
+    _check(lib().coda_ce_fwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_ce_fwd")
+    return out
+
+
+def _ce_bwd_args(h, W, targets, lse, dloss, out):
+    M, D = h.shape
+    V = W.shape[0]
+    _want(h, "h", torch.bfloat16, (M, D))
+    _want(W, "W", torch.bfloat16, (V, D))
+    _want(targets, "targets", torch.int64, (M,))
+    _want(lse, "lse", torch.float32, (M,))
+    _want(dloss, "dloss", torch.float32, (M,))
+    _want(out["dlogits"], "dlogits", torch.bfloat16, (M, V))
+    return CeBwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(dloss), _ptr(out["dlogits"]),
+                     _ptr(out["dh"]), _ptr(out["dW"]), _dt(out["dh"].dtype), _dt(out["dW"].dtype))
+
+
+def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bfloat16, out=None):
+    """Backward of sum_i dloss_i loss_i: dict(dlogits [M,V] bf16, dh [M,D], dW [V,D])."""
+    M, D = h.shape
+    V = W.shape[0]
+    dev = h.device
+    if out is None:
+        out = {"dlogits": torch.empty(M, V, dtype=torch.bfloat16, device=dev),
+               "dh": torch.empty(M, D, dtype=dh_dtype, device=dev),
+               "dW": torch.empty(V, D, dtype=dW_dtype, device=dev)}
+    a = _ce_bwd_args(h, W, targets, lse, dloss, out)
+    _check(lib().coda_ce_bwd(ctypes.byref(a), _stream(dev)), "coda_ce_bwd")
+    return out
+
+
+class BoundCe:
+    """coda_ce_fwd / coda_ce_bwd with arguments marshalled once (benchmarks)."""
+
+    def __init__(self, kind, args, ws, keep):
+        self.kind, self.args, self.ws, self._keep = kind, args, ws, keep
+
+    def run(self, stream):
+        if self.kind == "fwd":
+            _check(lib().coda_ce_fwd(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), "coda_ce_fwd")
+        else:
+            _check(lib().coda_ce_bwd(ctypes.byref(self.args), stream), "coda_ce_bwd")
+
+
+def bind_ce_fwd(h, W, targets, out, ws):
+    return BoundCe("fwd", _ce_fwd_args(h, W, targets, out["lse"], out["loss"]), ws, (h, W, targets, out))
+
+
+def bind_ce_bwd(h, W, targets, lse, dloss, out):
+    return BoundCe("bwd", _ce_bwd_args(h, W, targets, lse, dloss, out), None, (h, W, targets, lse, dloss, out))
 
 
 class BoundGemm0:

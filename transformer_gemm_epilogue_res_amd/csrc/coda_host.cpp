@@ -69,7 +69,6 @@ coda_status_t validate_bwd_common(const coda_bwd_args_t* a) {
 extern "C" {
 
 size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
-  (void)N;
   if (!rows_ok(M) || !dim_ok(D)) return 0;
   switch (op) {
     case CODA_OP_FWD: return fwd_ws(M, D);
@@ -78,6 +77,8 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_UNFUSED_BWD: return unfused_bwd_ws(M, D);
     case CODA_OP_FWD_SWIGLU: return N % 512 == 0 ? fwd_ws(M, D) : 0;
     case CODA_OP_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? bwd_swiglu_ws(M, D, N) : 0;
+    case CODA_OP_CE_FWD: return dim_ok(N) ? ce_fwd_ws(M, N) : 0;
+    case CODA_OP_CE_BWD: return 0;
   }
   return 0;
 }
@@ -149,6 +150,25 @@ coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const vo
   if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 512) return CODA_ERR_SHAPE;
   if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype) || !dtype_ok(a->dW2_dtype)) return CODA_ERR_ARG;
   return check_ws(ws, ws_bytes, bwd_swiglu_ws(a->M, a->D, a->N));
+}
+
+coda_status_t coda_validate_ce_fwd(const coda_ce_fwd_args_t* a, const void* ws, size_t ws_bytes) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->h, a->W, a->targets, a->lse, a->loss};
+  coda_status_t st = check_ptrs(ps, 5);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V)) return CODA_ERR_SHAPE;
+  return check_ws(ws, ws_bytes, ce_fwd_ws(a->M, a->V));
+}
+
+coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->h, a->W, a->targets, a->lse, a->dloss, a->dlogits, a->dh, a->dW};
+  coda_status_t st = check_ptrs(ps, 8);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V)) return CODA_ERR_SHAPE;
+  if (!dtype_ok(a->dh_dtype) || !dtype_ok(a->dW_dtype)) return CODA_ERR_ARG;
+  return CODA_OK;
 }
 
 coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a) {

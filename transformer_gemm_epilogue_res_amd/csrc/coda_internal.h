@@ -32,6 +32,12 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int64_t ssq_cols(int64_t D) { return D / kWaveTileN; }
 // Column count of the SwiGLU backward's s partials Ps[M, (N / 2) / kWaveTileN].
 inline int64_t swiglu_s_cols(int64_t N) { return (N / 2) / kWaveTileN; }
+// Column count of the cross-entropy tile statistics Pml[M, V / kWaveTileN] (float2).
+inline int64_t ce_stat_cols(int64_t V) { return V / kWaveTileN; }
+// Cross-entropy forward workspace: Pml, then the target logits [M] fp32.
+inline size_t ce_fwd_ws(int64_t M, int64_t V) {
+  return align256(size_t(M) * size_t(ce_stat_cols(V)) * 8) + align256(size_t(M) * 4);
+}
 // Row count of the fused backward's dgamma partials Pg[ceil(M / kWaveTileM), D].
 inline int64_t dgamma_rows(int64_t M) { return ceil_div(M, kWaveTileM); }
 

@@ -322,6 +322,92 @@ struct EpiSwigluBwd {
   }
 };
 
+// ---------------------------------------------------------- cross-entropy
+// LM-head GEMM logits = h @ W^T with the stateful log-sum-exp epilogue (blog,
+// section "五类 Epilogue 原语": tile-level online log-sum-exp / cross-entropy
+// statistics). A target outside [0, V) marks an ignored row.
+
+__device__ __forceinline__ bool ce_valid(int64_t t, int64_t V) { return t >= 0 && t < V; }
+
+// Per (row, wave tile of 64 columns): the running statistics of the row's
+// logits over those columns, m = max and l = sum exp(logit - m) -> Pml[i, nb / 64];
+// the lane that holds column t_i writes the target logit to tgt[i].
+struct EpiCeStats {
+  const int64_t* targets;
+  float2* Pml;
+  float* tgt;
+  int64_t M, V, pcols;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t*) const {
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      const bool ok = i < M;
+      float m = -INFINITY;
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, acc[tm][tn][e]);
+      m = fmaxf(m, shfl_xor(m, 16));
+      m = fmaxf(m, shfl_xor(m, 32));
+      float l = 0.f;
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l += expf(acc[tm][tn][e] - m);
+      l += shfl_xor(l, 16);
+      l += shfl_xor(l, 32);
+      if (ok && lg == 0) Pml[i * pcols + nb / kWaveTileN] = make_float2(m, l);
+      const int64_t t = ok ? targets[i] : -1;
+      const int64_t c = t - nb;  // the target's column inside the wave tile
+      if (ok && ce_valid(t, V) && c >= 0 && c < kWaveTileN && ((c >> 2) & 3) == lg) {
+        float v = 0.f;
+#pragma unroll
+        for (int tn = 0; tn < kTN; ++tn)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v = (16 * tn + 4 * lg + e == c) ? acc[tm][tn][e] : v;
+        tgt[i] = v;
+      }
+    }
+  }
+};
+
+// Backward epilogue on the recomputed logits: dlogits = dloss_i (exp(logit - lse_i)
+// - [v = t_i]), 0 on ignored rows; stored bf16 (the operand of the two GEMMs that follow).
+struct EpiCeBwd {
+  const int64_t* targets;
+  const float* lse;
+  const float* dloss;
+  uint16_t* dlogits;
+  int64_t M, V;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
+    const int li = lane & 15, lg = lane >> 4;
+    float ls[kTM], dl[kTM];
+    int tc[kTM];
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+      const int64_t i = mb + 16 * tm + li;
+      const int64_t t = i < M ? targets[i] : -1;
+      const bool ok = i < M && ce_valid(t, V);
+      ls[tm] = ok ? lse[i] : 0.f;
+      dl[tm] = ok ? dloss[i] : 0.f;
+      const int64_t c = t - nb - 4 * lg;  // target column relative to the lane's first column of tile 0
+      tc[tm] = (c >= 0 && c < kWaveTileN) ? int(c) : -1;
+    }
+    store_block<false>(stage, lane, dlogits, V, mb, nb, M, [&](int tm, int tn) {
+      f32x4_t d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = expf(acc[tm][tn][e] - ls[tm]);
+        d[e] = dl[tm] * (p - (tc[tm] == 16 * tn + e ? 1.0f : 0.0f));
+      }
+      return d;
+    });
+  }
+};
+
 // Data-gradient epilogue on G = dY @ W1^T:
 //   da = r gamma G - (s r^2 / D) h,  Pg[row tile, j] = sum over the wave's 128 rows of G r h.
 template <bool F32>
@@ -537,6 +623,42 @@ __global__ __launch_bounds__(256) void scombine_gr_kernel(const float* Ps, const
     const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
     const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
     go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+__device__ __forceinline__ float block_max256(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return t;
+}
+
+// Cross-entropy combine: one 256-thread block per row. lse_i = m + log sum_t l_t
+// exp(m_t - m) with m = max_t m_t over the row's (m_t, l_t) tile statistics (fixed
+// order); loss_i = lse_i - target logit, 0 for an ignored row.
+__global__ __launch_bounds__(256) void ce_combine_kernel(const float2* Pml, const float* tgt, const int64_t* targets,
+                                                         float* lse, float* loss, int64_t pcols, int64_t V) {
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const float2* p = Pml + i * pcols;
+  float m = -INFINITY;
+  for (int64_t t = threadIdx.x; t < pcols; t += 256) m = fmaxf(m, p[t].x);
+  m = block_max256(m, red);
+  float l = 0.f;
+  for (int64_t t = threadIdx.x; t < pcols; t += 256) {
+    const float2 v = p[t];
+    l += v.y * expf(v.x - m);
+  }
+  l = block_sum256(l, red);
+  if (threadIdx.x == 0) {
+    const float ls = m + logf(l);
+    const int64_t t = targets[i];
+    lse[i] = ls;
+    loss[i] = ce_valid(t, V) ? ls - tgt[i] : 0.f;
   }
 }
 
@@ -804,6 +926,39 @@ coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t 
   // dW2 [F, E] = o^T @ dOut: A(m=f, k=i) = o[i, f] (m contiguous), B(k=i, n=e) = dOut[i, e] (n contiguous), K = M
   const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
   return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));
+}
+
+coda_status_t coda_ce_fwd(const coda_ce_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  coda_status_t v = coda_validate_ce_fwd(a, ws, ws_bytes);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t pcols = ce_stat_cols(a->V);
+  float2* Pml = reinterpret_cast<float2*>(ws);
+  float* tgt = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(pcols) * 8)));
+  // logits = h @ W^T: A = h [M, D], B(k=d, v) = W[v, d] (both k contiguous)
+  const GemmShape p{a->M, a->V, a->D, a->h, a->D, a->W, a->D};
+  hipError_t e = launch_gemm<true, true>(p, EpiCeStats{a->targets, Pml, tgt, a->M, a->V, pcols}, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  hipLaunchKernelGGL(ce_combine_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, (const float2*)Pml, (const float*)tgt,
+                     a->targets, a->lse, a->loss, pcols, a->V);
+  return to_status(hipGetLastError());
+}
+
+coda_status_t coda_ce_bwd(const coda_ce_bwd_args_t* a, void* stream) {
+  coda_status_t v = coda_validate_ce_bwd(a);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // recomputed logits with the dlogits epilogue
+  const GemmShape p{a->M, a->V, a->D, a->h, a->D, a->W, a->D};
+  hipError_t e = launch_gemm<true, true>(
+      p, EpiCeBwd{a->targets, a->lse, a->dloss, static_cast<uint16_t*>(a->dlogits), a->M, a->V}, st);
+  if (e != hipSuccess) return CODA_ERR_HIP;
+  // dh [M, D] = dlogits @ W: A = dlogits [M, V] (k contiguous), B(k=v, d) = W[v, d] (n contiguous)
+  const GemmShape pd{a->M, a->D, a->V, a->dlogits, a->V, a->W, a->D};
+  if ((e = gemm_plain(pd, true, false, a->dh, a->D, a->dh_dtype == CODA_F32, st)) != hipSuccess) return CODA_ERR_HIP;
+  // dW [V, D] = dlogits^T @ h: A(m=v, k=i) = dlogits[i, v] (m contiguous), B(k=i, d) = h[i, d] (n contiguous), K = M
+  const GemmShape pw{a->V, a->D, a->M, a->dlogits, a->V, a->h, a->D};
+  return to_status(gemm_plain(pw, false, false, a->dW, a->D, a->dW_dtype == CODA_F32, st));
 }
 
 coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream) {
