@@ -43,8 +43,7 @@ def stage_work(M, K0, D, N):
         "gemm1_rowscale": ("flop", 2 * M * D * N),
         "rowstat_s_rg": ("byte", 2 * M * N * 2 + 2 * M * D * 2 + 2 * M * 4),
         "dgrad_rmsnorm_bwd": ("flop", 2 * M * N * D),
-        "dgamma_combine": ("byte", ((M + 127) // 128) * D * 4 + D * 4),
-        "wgrad": ("flop", 2 * M * D * N),
+        "wgrad_dgamma": ("flop", 2 * M * D * N),
     }
 
 
@@ -78,7 +77,7 @@ def measured_traffic(kernel: str):
     return None if k is None else k["bytes_per_launch"]
 
 
-def cpu_baseline(host, rows, ncols, seed=0):
+def cpu_baseline(host, rows, ncols, total_rows, seed=0):
     """Time the fp64 oracle (as it is) on a sub-batch of sampled rows of the workload."""
     import numpy as np
     import torch
@@ -100,18 +99,21 @@ def cpu_baseline(host, rows, ncols, seed=0):
     g_s = torch.from_numpy(f["h"] * gam[None, :]).to(torch.bfloat16)
     y_s = torch.from_numpy(f["y"]).to(torch.bfloat16)
     r_s = torch.from_numpy(f["r"]).to(torch.float32)
-    jc = inputs.sample(D, ncols, seed, "dgamma_cols").numpy()
-    nc = inputs.sample(N, ncols, seed, "dw1_cols").numpy()
+    jc = None if ncols <= 0 else inputs.sample(D, ncols, seed, "dgamma_cols").numpy()
+    nc = None if ncols <= 0 else inputs.sample(N, ncols, seed, "dw1_cols").numpy()
+    cj, cn = (D, N) if ncols <= 0 else (ncols, ncols)
     t2 = time.perf_counter()
     orc.backward(host["dY"], y_s, h_s, g_s, r_s, host["gamma"], host["W1"], dgamma_cols=jc, dw1_cols=nc)
     t3 = time.perf_counter()
-    flops = 2 * R * (K0 * D + D * N) + 2 * R * N * D + 2 * R * N + 2 * R * N * ncols + 2 * R * D * ncols
+    # forward; s, G, da of every row; dgamma (G recomputed on its columns) and dW1 on their columns
+    flops = 2 * R * (K0 * D + D * N) + 2 * R * N * D + 2 * R * N + 2 * R * N * cj + 2 * R * D * cn
     secs = (t1 - t0) + (t3 - t2)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    what = "all" if ncols <= 0 else f"{ncols} sampled"
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle on {R} sampled rows of the 8B workload: forward of those rows, then "
-                       f"the backward of that {R}-row sub-batch (s, G, da for every row; dgamma and dW1 on "
-                       f"{ncols} sampled columns each); {flops / 1e9:.1f} GFLOP in {secs:.2f} s"),
+            "sample": (f"fp64 numpy oracle on {R} of the 8B workload's {total_rows} rows: forward of those rows, then "
+                       f"the backward of that {R}-row batch (s, G, da for every row; dgamma and dW1 on "
+                       f"{what} columns); {flops / 1e9:.1f} GFLOP in {secs:.2f} s"),
             "seconds": secs, "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
 
 
@@ -120,8 +122,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows in the oracle's timed sample (0 = skip)")
-    ap.add_argument("--cpu-cols", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="rows in the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-cols", type=int, default=0,
+                    help="dgamma / dW1 columns in the oracle's timed sample (0 = all)")
     ap.add_argument("--no-unfused", action="store_true", help="skip timing the unfused baseline")
     ap.add_argument("--no-swiglu", action="store_true", help="skip timing the SwiGLU block")
     ap.add_argument("--no-ce", action="store_true", help="skip timing the cross-entropy LM head")
@@ -343,7 +346,7 @@ def main():
         rows = inputs.sample(M, args.cpu_rows, 0, "rows").to(dev)
         host = {"x": x.index_select(0, rows).cpu(), "z": z.index_select(0, rows).cpu(), "W0": W0.cpu(),
                 "gamma": gamma.cpu(), "W1": W1.cpu(), "dY": dY.index_select(0, rows).cpu()}
-        cpu = cpu_baseline(host, rows.cpu().numpy(), args.cpu_cols)
+        cpu = cpu_baseline(host, rows.cpu().numpy(), args.cpu_cols, M)
         log(f"[bench] cpu baseline {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
 
     rec = {

@@ -296,8 +296,10 @@ coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* 
 coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
 /* Fused backward: row statistic s and bf16(r*g) -> G = dY@W1^T with the
- * RMSNorm-backward epilogue (da, dgamma column partials) -> dgamma combine ->
- * dW1 = bf16(r*g)^T @ dY. */
+ * RMSNorm-backward epilogue (da, dgamma column partials) -> dW1 = bf16(r*g)^T @ dY,
+ * whose blocks also reduce the dgamma partials, 64 columns at a time in a fixed
+ * order, before their own tiles: the auxiliary reduction folded into the next
+ * kernel. */
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
 /* The stages of coda_fwd and coda_bwd, one kernel each, for callers that
@@ -308,9 +310,9 @@ coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void
  *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine,
  *             2 GEMM1 + row-scale epilogue
  *   backward: 0 s and bf16(r*g), 1 G = dY@W1^T + RMSNorm-backward epilogue,
- *             2 dgamma combine, 3 dW1 GEMM */
+ *             2 dW1 GEMM, whose first blocks also reduce the dgamma partials */
 #define CODA_FWD_STAGES 3
-#define CODA_BWD_STAGES 4
+#define CODA_BWD_STAGES 3
 coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 

@@ -23,9 +23,9 @@ CODA_BF16, CODA_F32 = 0, 1
 (CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD, CODA_OP_FWD_SWIGLU, CODA_OP_BWD_SWIGLU,
  CODA_OP_CE_FWD, CODA_OP_CE_BWD) = range(8)
 CODA_ROW, CODA_COL = 0, 1
-CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 4
+CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 3
 FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
-BWD_STAGE_NAMES = ("rowstat_s_rg", "dgrad_rmsnorm_bwd", "dgamma_combine", "wgrad")
+BWD_STAGE_NAMES = ("rowstat_s_rg", "dgrad_rmsnorm_bwd", "wgrad_dgamma")
 
 
 class FwdArgs(ctypes.Structure):

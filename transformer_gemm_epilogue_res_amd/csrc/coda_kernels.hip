@@ -10,6 +10,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "coda.h"
 #include "coda_internal.h"
 #include "gemm_mainloop.hpp"
@@ -122,6 +125,44 @@ template <bool F32>
 struct EpiStore {
   void* C;
   int64_t ldc, M;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
+    store_block<F32>(stage, lane, C, ldc, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
+  }
+};
+
+// The weight-gradient GEMM's store, which also finishes dgamma: before its
+// mainloop, block b reduces the 64-column chunks b, b + grid, ... of the
+// data-gradient GEMM's column partials, dgamma_j = sum_t Pg[t, j], in a fixed
+// order (eight row groups t = q mod 8, then the groups in order) -- the
+// auxiliary dgamma reduction folded into the kernel that runs next.
+template <bool F32>
+struct EpiStoreDgamma {
+  void* C;
+  int64_t ldc, M;
+  const float* Pg;
+  float* dgamma;
+  int64_t rows, D;
+  __device__ __forceinline__ void prologue(lds_char_t* smem) const {
+    // 64-column chunks dealt round-robin over the blocks (a small GEMM may have fewer blocks than chunks)
+    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+    LDS_AS float* part = reinterpret_cast<LDS_AS float*>(smem);
+    for (int64_t chunk = blockIdx.x; chunk < dceil_div(D, 64); chunk += gridDim.x) {  // uniform per block
+      const int64_t j = chunk * 64 + c;
+      float acc = 0.f;
+      if (j < D)
+        for (int64_t t = q; t < rows; t += 8) acc += Pg[t * D + j];
+      part[q * 64 + c] = acc;
+      __syncthreads();
+      if (q == 0 && j < D) {
+        float tot = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) tot += part[g * 64 + c];
+        dgamma[j] = tot;
+      }
+      __syncthreads();  // part is rewritten by the next chunk; the mainloop's loads overwrite the LDS
+    }
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
                                              lds_char_t* stage) const {
     store_block<F32>(stage, lane, C, ldc, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
@@ -470,10 +511,18 @@ struct EpiRmsNormBwd {
   }
 };
 
+// An epilogue may also carry block-level work that runs before the mainloop
+// (prologue(smem), all threads; the LDS is free until the mainloop starts).
+template <class Epi, class = void>
+struct HasPrologue : std::false_type {};
+template <class Epi>
+struct HasPrologue<Epi, decltype(std::declval<const Epi&>().prologue(nullptr), void())> : std::true_type {};
+
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
   lds_char_t* smem = (lds_char_t*)smem_raw;
+  if constexpr (HasPrologue<Epi>::value) epi.prologue(smem);
   int tile_m, tile_n;
   map_tile(p.M, p.N, tile_m, tile_n);
   const int64_t m0 = int64_t(tile_m) * kBM, n0 = int64_t(tile_n) * kBN;
@@ -776,6 +825,15 @@ hipError_t bwd_wgrad(const coda_bwd_args_t* a, const uint16_t* gr, hipStream_t s
   return gemm_plain(p, false, false, a->dW1, a->N, a->dW1_dtype == CODA_F32, st);
 }
 
+// The same GEMM, finishing dgamma from the partials Pg[rows, D] in its prologue.
+hipError_t bwd_wgrad_dgamma(const coda_bwd_args_t* a, const uint16_t* gr, const float* Pg, int64_t rows,
+                            hipStream_t st) {
+  const GemmShape p{a->D, a->N, a->M, gr, a->D, a->dY, a->N};
+  if (a->dW1_dtype == CODA_F32)
+    return launch_gemm<false, false>(p, EpiStoreDgamma<true>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
+  return launch_gemm<false, false>(p, EpiStoreDgamma<false>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
+}
+
 hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, hipStream_t st) {
   hipLaunchKernelGGL(dgamma_combine_kernel, dim3(unsigned(ceil_div(a->D, kDgCols))), dim3(256), 0, st, Pg, a->dgamma,
                      rows, a->D);
@@ -838,8 +896,7 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
   float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
   if (stage == 0) return to_status(bwd_rowstat(a, gr, st));
   if (stage == 1) return to_status(bwd_dgrad(a, Pg, st));
-  if (stage == 2) return to_status(bwd_dgamma(Pg, dgamma_rows(a->M), a, st));
-  return to_status(bwd_wgrad(a, gr, st));
+  return to_status(bwd_wgrad_dgamma(a, gr, Pg, dgamma_rows(a->M), st));
 }
 
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
@@ -921,8 +978,7 @@ coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t 
                           a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
   float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
   if ((e = bwd_dgrad(&c, Pg, st)) != hipSuccess) return CODA_ERR_HIP;
-  if ((e = bwd_dgamma(Pg, dgamma_rows(a->M), &c, st)) != hipSuccess) return CODA_ERR_HIP;
-  if ((e = bwd_wgrad(&c, gr, st)) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_wgrad_dgamma(&c, gr, Pg, dgamma_rows(a->M), st)) != hipSuccess) return CODA_ERR_HIP;
   // dW2 [F, E] = o^T @ dOut: A(m=f, k=i) = o[i, f] (m contiguous), B(k=i, n=e) = dOut[i, e] (n contiguous), K = M
   const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
   return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));
