@@ -361,6 +361,47 @@ def test_no_writes_outside_outputs(M):
     assert torch.isfinite(out["y"].float()).all() and torch.isfinite(bo["da"]).all()
 
 
+def test_graph_capture_replays_match_eager():
+    """The step (coda_fwd + coda_bwd) captured into a HIP graph: the library allocates, frees and
+    clears nothing, so every replay reproduces the eager results bit for bit."""
+    c = FWD_SMALL["ragged"]
+    announce(f"graph capture coda_fwd + coda_bwd {c}")
+    M, D, N = c["M"], c["D"], c["N"]
+    inp = to_dev(inputs.forward_inputs(**c, seed=4))
+    dY = inputs.output_grad(M, N, seed=4).to(DEV)
+    fo = {"h": torch.empty(M, D, dtype=torch.bfloat16, device=DEV), "g": torch.empty(M, D, dtype=torch.bfloat16, device=DEV),
+          "r": torch.empty(M, dtype=torch.float32, device=DEV), "y": torch.empty(M, N, dtype=torch.bfloat16, device=DEV)}
+    bo = {"da": torch.empty(M, D, dtype=torch.bfloat16, device=DEV), "dgamma": torch.empty(D, dtype=torch.float32, device=DEV),
+          "dW1": torch.empty(D, N, dtype=torch.bfloat16, device=DEV), "s": torch.empty(M, dtype=torch.float32, device=DEV)}
+    fws = L.workspace(L.CODA_OP_FWD, M, D, N, DEV)
+    bws = L.workspace(L.CODA_OP_BWD, M, D, N, DEV)
+
+    def step():
+        L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, ws=fws, out=fo)
+        L.bwd(dY, fo["y"], fo["h"], fo["g"], fo["r"], inp["gamma"], inp["W1"], ws=bws, out=bo)
+
+    step()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in list(fo.items()) + list(bo.items())}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in list(fo.values()) + list(bo.values()):
+            t.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in list(fo.items()) + list(bo.items()):
+            assert torch.equal(v, want[k]), (rep, k)
+
+
 def test_binding_reports_errors_without_launch():
     inp = to_dev(inputs.forward_inputs(**FWD_SMALL["tiny"], seed=0))
     with pytest.raises(L.CodaError) as e:

@@ -587,8 +587,8 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
 
 // One 512-thread block per row i: s_i = sum_n dY_in y_in (fp32) and
 // gr_i = bf16(r_i g_i). The row is read in rounds of kRowUnroll x 16 bytes per
-// thread of each input, all loads of a round issued before any is used (7
-// rounds cover an N = 28672 row in one pass).
+// thread of each input, all loads of a round issued before any is used (one
+// round covers an N = 28672 row).
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 7;
 __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY, const uint16_t* y,
@@ -596,6 +596,17 @@ __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY
                                                               uint16_t* gr, int64_t N, int64_t D) {
   __shared__ float red[kRowThreads / 64];
   const int64_t i = blockIdx.x;
+  // bf16(r g) first: it does not wait for s, and its loads join the row's in the same round
+  const float ri = r[i];
+  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
+  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
+  for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
+    float f[8];
+    unpack8_bf16(gs[v], f);
+    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
+    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
+    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
   const uint4* a = reinterpret_cast<const uint4*>(dY + i * N);
   const uint4* b = reinterpret_cast<const uint4*>(y + i * N);
   const int64_t n8 = N / 8;
@@ -619,16 +630,6 @@ __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY
   }
   const float tot = block_sum512(acc, red);
   if (threadIdx.x == 0) s[i] = tot;
-  const float ri = r[i];
-  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
-  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
-  for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
-    float f[8];
-    unpack8_bf16(gs[v], f);
-    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
-    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
-    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
 }
 
 // dgamma_j = sum_t Pg[t, j]. A 256-thread block covers 32 columns; its 8 row
