@@ -77,6 +77,26 @@ def measured_traffic(kernel: str):
     return None if k is None else k["bytes_per_launch"]
 
 
+def _quantiles(v, qs):
+    import numpy as np
+    return np.quantile(np.asarray(v, dtype=np.float64), qs)
+
+
+def measured_sclk(kernel: str):
+    """Shader clock (GHz) of `kernel` from profiles/sclk_llama3_8b.md (GRBM_GUI_ACTIVE over the 8 XCDs /
+    dispatch duration), or None when that measurement was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "sclk_llama3_8b.md")
+    if not os.path.exists(path):
+        return None
+    try:
+        blob = json.loads(open(path).read().split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if blob.get("source_digest") != kernel_source_digest():
+        return None
+    return blob.get("kernels", {}).get(kernel)
+
+
 def cpu_baseline(host, rows, ncols, total_rows, seed=0):
     """Time the fp64 oracle (as it is) on a sub-batch of sampled rows of the workload."""
     import numpy as np
@@ -226,6 +246,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "per_launch": f"{damount / 1e12:.4f} TFLOP", "avg_us": round(per[dom] * 1e3, 1)}
+        clk = measured_sclk(dom)   # the power-limited clock the kernel runs at (2.4 GHz is the peak's)
+        roof["sclk_ghz"] = clk
+        roof["frac_at_sclk"] = None if clk is None else round(ach / (PEAK_BF16_TFLOPS * clk / 2.4), 4)
     else:
         ach = damount / (per[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -356,6 +379,7 @@ def main():
         "config": {"workload": "llama3_8b fused forward + backward", "M": M, "K0": K0, "D": D, "N": N,
                    "eps": inputs.EPS, "parallelism": "single GPU"},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "step_ms_p10_p50_p90": [round(float(q), 4) for q in _quantiles(step_ms, (0.1, 0.5, 0.9))],
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / fwd_ms / 1e9, 1),
                 "pct_peak": round(100 * fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
