@@ -75,7 +75,7 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_BWD: return bwd_ws(M, D);
     case CODA_OP_UNFUSED_FWD: return unfused_fwd_ws(M, D);
     case CODA_OP_UNFUSED_BWD: return unfused_bwd_ws(M, D);
-    case CODA_OP_FWD_SWIGLU: return N % 512 == 0 ? fwd_ws(M, D) : 0;
+    case CODA_OP_FWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? fwd_ws(M, D) : 0;
     case CODA_OP_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? bwd_swiglu_ws(M, D, N) : 0;
     case CODA_OP_CE_FWD: return dim_ok(N) ? ce_fwd_ws(M, N) : 0;
     case CODA_OP_CE_BWD: return 0;
