@@ -310,14 +310,16 @@ def main():
         SF = L.bind_fwd_swiglu(x, W0, z, gamma, W1, inputs.EPS, so, fws)
         SB = L.bind_bwd_swiglu(dOut, W2, so["o"], so["y"], so["h"], so["g"], so["r"], gamma, W1, sbo,
                                L.workspace(L.CODA_OP_BWD_SWIGLU, M, D, N, dev))
+        USB = L.bind_bwd_swiglu(dOut, W2, so["o"], so["y"], so["h"], so["g"], so["r"], gamma, W1, sbo,
+                                L.workspace(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N, dev))
         t = {}
-        for name, obj in (("fwd", SF), ("bwd", SB)):
+        for name, obj, unf in (("fwd", SF, False), ("bwd", SB, False), ("ufwd", SF, True), ("ubwd", USB, True)):
             for _ in range(2):
-                obj.run(sp)
+                obj.run(sp, unfused=unf)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(args.steps):
-                obj.run(sp)
+                obj.run(sp, unfused=unf)
             b.record(stream)
             torch.cuda.synchronize()
             t[name] = a.elapsed_time(b) / args.steps
@@ -327,8 +329,12 @@ def main():
                   "bwd_tflops": round(s_bwd_flop / t["bwd"] / 1e9, 1),
                   "tflops": round((fwd_flop + s_bwd_flop) / (t["fwd"] + t["bwd"]) / 1e9, 1)}
         swiglu["pct_peak"] = round(100 * swiglu["tflops"] / PEAK_BF16_TFLOPS, 2)
-        log(f"[bench] SwiGLU block: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {swiglu['tflops']} TFLOP/s")
-        del W2, dOut, so, sbo, SF, SB
+        swiglu["unfused"] = {"fwd_ms": round(t["ufwd"], 4), "bwd_ms": round(t["ubwd"], 4),
+                             "fused_fwd_speedup": round(t["ufwd"] / t["fwd"], 3),
+                             "fused_bwd_speedup": round(t["ubwd"] / t["bwd"], 3)}
+        log(f"[bench] SwiGLU block: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {swiglu['tflops']} TFLOP/s; "
+            f"unfused SwiGLU step: fwd {t['ufwd']:.3f} ms, bwd {t['ubwd']:.3f} ms")
+        del W2, dOut, so, sbo, SF, SB, USB
 
     # Cross-entropy on the Llama-3-8B LM head (coda_ce_fwd / coda_ce_bwd, V = 128256):
     # reported beside the headline step.

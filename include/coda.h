@@ -78,7 +78,9 @@ typedef enum {
   CODA_OP_FWD_SWIGLU = 4,   /* coda_fwd_swiglu */
   CODA_OP_BWD_SWIGLU = 5,   /* coda_bwd_swiglu */
   CODA_OP_CE_FWD = 6,       /* coda_ce_fwd (pass the vocabulary size V as N) */
-  CODA_OP_CE_BWD = 7        /* coda_ce_bwd (none) */
+  CODA_OP_CE_BWD = 7,       /* coda_ce_bwd (none) */
+  CODA_OP_UNFUSED_FWD_SWIGLU = 8, /* coda_unfused_ref(CODA_OP_FWD_SWIGLU) */
+  CODA_OP_UNFUSED_BWD_SWIGLU = 9  /* coda_unfused_ref(CODA_OP_BWD_SWIGLU) */
 } coda_op_t;
 
 /* Forward arguments.
@@ -288,7 +290,8 @@ coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const vo
 coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_ce_fwd(const coda_ce_fwd_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a);
-/* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD or CODA_OP_BWD). */
+/* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD, CODA_OP_BWD, CODA_OP_FWD_SWIGLU or
+ * CODA_OP_BWD_SWIGLU). */
 coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
 
 /* Fused forward: GEMM0 + epilogue (residual, h, g, sum-of-squares partials) ->
@@ -323,7 +326,14 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
  *     to the second GEMM).
  *   op = CODA_OP_BWD, args = coda_bwd_args_t*: same s / bf16(r*g) kernel ->
  *     G = dY@W1^T stored as bf16 in the workspace -> RMSNorm-backward row kernel
- *     (da, dgamma partials) -> dgamma combine -> same dW1 GEMM. */
+ *     (da, dgamma partials) -> dgamma combine -> same dW1 GEMM.
+ *   op = CODA_OP_FWD_SWIGLU, args = coda_fwd_swiglu_args_t*: the fused chain
+ *     forward (coda_fwd, y stored bf16) -> a row kernel o = silu(gate) * up from
+ *     the stored y. Only the SwiGLU step is unfused.
+ *   op = CODA_OP_BWD_SWIGLU, args = coda_bwd_swiglu_args_t*: dO = dOut@W2^T
+ *     stored as bf16 in the workspace -> a row kernel (dY from dO and the saved
+ *     y, s from the fp32 dY, bf16(r*g)) -> the fused chain backward's dgrad and
+ *     dW1 GEMMs -> dW2. Only the SwiGLU step is unfused. */
 coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream);
 
 /* SwiGLU forward and backward (see coda_fwd_swiglu_args_t, coda_bwd_swiglu_args_t). */

@@ -40,8 +40,8 @@ S_TOL = 1e-3
 
 
 def f64(t) -> np.ndarray:
-    if isinstance(t, np.ndarray):
-        return t.astype(np.float64)
+    if isinstance(t, (np.ndarray, np.generic, float, int)):
+        return np.asarray(t, dtype=np.float64)
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 

@@ -97,6 +97,9 @@ def test_workspace_sizes():
         a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4) + a256(M * (N2 // 2 // 64) * 4))
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD_SWIGLU, M, D, N2) == a256(M * (D // 64) * 4)
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N2) == (
+        a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4) + a256(M * (N2 // 2) * 2))
     V = 128256  # cross-entropy: tile statistics (m, l) [M, V/64] and the target logits [M]
     assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, V) == a256(M * (V // 64) * 8) + a256(M * 4)
     assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, 1000) == 0
@@ -240,6 +243,13 @@ def test_validate_swiglu():
     need = L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, 300, 256, 1024)
     assert vb(_bsw(), WS, need - 1) == L.CODA_ERR_WORKSPACE
     assert vb(_bsw(), WS, need) == L.CODA_OK
+    # the unfused baseline takes the same structs (its own backward workspace size)
+    un = L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, 300, 256, 1024)
+    assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw()), WS, un) == L.CODA_OK
+    assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw()), WS, un - 1) == L.CODA_ERR_WORKSPACE
+    assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw(N=768)), WS, un) == L.CODA_ERR_SHAPE
+    assert lib.coda_validate_unfused(L.CODA_OP_FWD_SWIGLU, ctypes.byref(_fsw()), WS, 1 << 30) == L.CODA_OK
+    assert lib.coda_unfused_ref(L.CODA_OP_FWD_SWIGLU, ctypes.byref(_fsw(o=None)), WS, 1 << 30, None) == L.CODA_ERR_NULL
     # rejected before any launch
     assert lib.coda_fwd_swiglu(ctypes.byref(_fsw(o_dtype=9)), WS, need, None) == L.CODA_ERR_ARG
     assert lib.coda_bwd_swiglu(ctypes.byref(_bsw(E=100)), WS, need, None) == L.CODA_ERR_SHAPE

@@ -212,9 +212,10 @@ def test_bwd_small_full(name, unfused):
 
 
 @pytest.mark.slow
-def test_bwd_llama3_8b_sampled():
-    c = inputs.CONFIGS["llama3_8b"]
-    announce(f"coda_bwd llama3_8b {c} seed=0 (saved set from the oracle forward), sampled")
+@pytest.mark.parametrize("name", ["llama3_8b", "llama3_1b", "llama3_70b"])
+def test_bwd_llama_shapes_sampled(name):
+    c = inputs.CONFIGS[name]
+    announce(f"coda_bwd {name} {c} seed=0 (saved set from the oracle forward), sampled")
     inp = inputs.forward_inputs(**c, seed=0)
     host = dict(saved_set(inp), dY=inputs.output_grad(c["M"], c["N"], seed=0), gamma=inp["gamma"], W1=inp["W1"])
     del inp

@@ -174,6 +174,52 @@ def test_swiglu_forward_then_backward_on_device():
     assert e["da"] <= 3 * mt.Y_TOL and e["s"] <= 3 * mt.Y_TOL
 
 
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_swiglu_unfused_baseline(name):
+    """coda_unfused_ref's SwiGLU: o from the stored bf16 y, dY from a stored bf16 dO. Its roundings
+    (y and dO to bf16 before the activation and its backward) make it a looser match to the oracle."""
+    c = SMALL[name]
+    announce(f"coda_unfused_ref fwd/bwd SwiGLU {name} {c} seed=0")
+    inp = inputs.forward_inputs(c["M"], c["K0"], c["D"], c["N"], seed=0)
+    d = to_dev(inp)
+    args = (d["x"], d["W0"], d["z"], d["gamma"], d["W1"], EPS)
+    fu = L.fwd_swiglu(*args, o_dtype=torch.float32, unfused=True)
+    ff = L.fwd_swiglu(*args, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for k in ("h", "g", "r", "y"):            # the chain part is the same fused forward
+        assert torch.equal(fu[k], ff[k]), k
+    ref = orc.forward(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
+    # o from the bf16 y: y's elementwise error is at most 1e-2 rms + half an ulp of the largest |y|
+    yr = ref["y"]
+    tol = mt.Y_TOL + 0.5 * float(mt.bf16_ulp(np.max(np.abs(yr)) * (1 + mt.Y_TOL))) / mt.rms(yr)
+    bound = mt.swiglu_o_bound(yr, orc.silu(yr[:, 0::2]), tol)
+    e_o = float(np.max(np.abs(mt.f64(fu["o"]) - orc.swiglu(yr)) / bound))
+    print(f"  unfused o |d|/bound max={e_o:.3f}")
+    assert e_o <= 1.0
+    host = host_case(c)
+    dv = to_dev(host)
+    bargs = (dv["dOut"], dv["W2"], dv["o"], dv["y"], dv["h"], dv["g"], dv["r"], dv["gamma"], dv["W1"])
+    bu = L.bwd_swiglu(*bargs, da_dtype=torch.float32, dW1_dtype=torch.float32, dW2_dtype=torch.float32, unfused=True)
+    bf = L.bwd_swiglu(*bargs, da_dtype=torch.float32, dW1_dtype=torch.float32, dW2_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(bu["dW2"], bf["dW2"])   # the same product of the same operands
+    sw = orc.swiglu_backward(host["dOut"], host["W2"], host["y"], host["o"])
+    rb = orc.backward(sw["dY"], host["y"], host["h"], host["g"], host["r"], host["gamma"], host["W1"])
+    # dO is rounded to bf16 before the SwiGLU backward: a relative error up to 2^-8 (half an ulp of
+    # dO), which is up to one ulp of dY, on top of dY's own half-ulp rounding -- 1.5 ulp in all,
+    # three times the half ulp the fused path's bounds count; s, da, dgamma, dW1 inherit it
+    a_da, a_dg = mt.dgrad_rounding_allowance(sw["dY"], host["W1"], host["r"], host["gamma"], host["h"])
+    a_w1 = mt.operand_rounding_allowance(host["g"], host["r"], sw["dY"], None, dY_rounded=True)
+    dYu, dYr = mt.f64(bu["dY"]), sw["dY"]
+    b_dY = 1.5 * mt.bf16_ulp(np.maximum(np.abs(dYu), np.abs(dYr))) + 1e-4 * mt.rms(dYr)
+    e = {"dY": float(np.max(np.abs(dYu - dYr) / b_dY)), "s": mt.normwise(bu["s"], rb["s"]),
+         "da": mt.within_allowance(bu["da"], rb["da"], 3 * a_da), "dgamma": mt.within_allowance(bu["dgamma"], rb["dgamma"], 3 * a_dg),
+         "dW1": mt.within_allowance(bu["dW1"], rb["dW1"], 3 * a_w1)}
+    print("  unfused " + "  ".join(f"{k}={v:.3e}" for k, v in e.items()) + "  (s: max|d|/rms; others |d| / bound)")
+    assert e["s"] <= 1e-2
+    assert e["dY"] <= 1.0 and e["da"] <= 1.0 and e["dgamma"] <= 1.0 and e["dW1"] <= 1.0
+
+
 @pytest.mark.slow
 def test_swiglu_llama3_8b_sampled():
     c = dict(inputs.CONFIGS["llama3_8b"], E=inputs.CONFIGS["llama3_8b"]["D"])

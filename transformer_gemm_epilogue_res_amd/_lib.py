@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "coda.h")
 CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA_ERR_ARG, CODA_ERR_HIP = range(7)
 CODA_BF16, CODA_F32 = 0, 1
 (CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD, CODA_OP_FWD_SWIGLU, CODA_OP_BWD_SWIGLU,
- CODA_OP_CE_FWD, CODA_OP_CE_BWD) = range(8)
+ CODA_OP_CE_FWD, CODA_OP_CE_BWD, CODA_OP_UNFUSED_FWD_SWIGLU, CODA_OP_UNFUSED_BWD_SWIGLU) = range(10)
 CODA_ROW, CODA_COL = 0, 1
 CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 3
 FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
@@ -271,9 +271,10 @@ def _fwd_swiglu_args(x, W0, z, gamma, W1, eps, out):
                          _ptr(out["o"]), _dt(out["o"].dtype))
 
 
-def fwd_swiglu(x, W0, z, gamma, W1, eps, o_dtype=torch.bfloat16, ws=None, out=None):
+def fwd_swiglu(x, W0, z, gamma, W1, eps, o_dtype=torch.bfloat16, ws=None, out=None, unfused=False):
     """Forward of the chain followed by SwiGLU on y's interleaved (gate, up) columns.
-    Returns dict(h, g, r, y, o); y is bf16, o is [M, N/2] in o_dtype."""
+    Returns dict(h, g, r, y, o); y is bf16, o is [M, N/2] in o_dtype. unfused: the SwiGLU
+    step as a separate row kernel on the stored y (coda_unfused_ref)."""
     M, D, N = x.shape[0], W1.shape[0], W1.shape[1]
     dev = x.device
     if out is None:
@@ -284,8 +285,12 @@ def fwd_swiglu(x, W0, z, gamma, W1, eps, o_dtype=torch.bfloat16, ws=None, out=No
                "o": torch.empty(M, N // 2, dtype=o_dtype, device=dev)}
     a = _fwd_swiglu_args(x, W0, z, gamma, W1, eps, out)
     if ws is None:
-        ws = workspace(CODA_OP_FWD_SWIGLU, M, D, N, dev)
-    _check(lib().coda_fwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_fwd_swiglu")
+        ws = workspace(CODA_OP_UNFUSED_FWD_SWIGLU if unfused else CODA_OP_FWD_SWIGLU, M, D, N, dev)
+    if unfused:
+        _check(lib().coda_unfused_ref(CODA_OP_FWD_SWIGLU, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+               "coda_unfused_ref(fwd_swiglu)")
+    else:
+        _check(lib().coda_fwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_fwd_swiglu")
     return out
 
 
@@ -309,9 +314,10 @@ def _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out):
 
 
 def bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_dtype=torch.bfloat16,
-               dW2_dtype=torch.bfloat16, ws=None, out=None):
+               dW2_dtype=torch.bfloat16, ws=None, out=None, unfused=False):
     """Backward of SwiGLU + output projection out = o @ W2 and of the chain under it.
-    Returns dict(dY, da, dgamma, dW1, dW2, s)."""
+    Returns dict(dY, da, dgamma, dW1, dW2, s). unfused: dO stored, then a separate
+    SwiGLU-backward row kernel (coda_unfused_ref)."""
     M, E = dOut.shape
     D, N = W1.shape
     dev = dOut.device
@@ -324,8 +330,12 @@ def bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_
                "s": torch.empty(M, dtype=torch.float32, device=dev)}
     a = _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out)
     if ws is None:
-        ws = workspace(CODA_OP_BWD_SWIGLU, M, D, N, dev)
-    _check(lib().coda_bwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_bwd_swiglu")
+        ws = workspace(CODA_OP_UNFUSED_BWD_SWIGLU if unfused else CODA_OP_BWD_SWIGLU, M, D, N, dev)
+    if unfused:
+        _check(lib().coda_unfused_ref(CODA_OP_BWD_SWIGLU, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+               "coda_unfused_ref(bwd_swiglu)")
+    else:
+        _check(lib().coda_bwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_bwd_swiglu")
     return out
 
 
@@ -335,7 +345,12 @@ class BoundSwiglu:
     def __init__(self, kind, args, ws, keep):
         self.kind, self.args, self.ws, self._keep = kind, args, ws, keep
 
-    def run(self, stream):
+    def run(self, stream, unfused=False):
+        if unfused:
+            op = CODA_OP_FWD_SWIGLU if self.kind == "fwd" else CODA_OP_BWD_SWIGLU
+            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream),
+                   f"coda_unfused_ref({self.kind}_swiglu)")
+            return
         fn = lib().coda_fwd_swiglu if self.kind == "fwd" else lib().coda_bwd_swiglu
         _check(fn(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}_swiglu")
 

@@ -64,6 +64,17 @@ coda_status_t validate_bwd_common(const coda_bwd_args_t* a) {
   return CODA_OK;
 }
 
+coda_status_t validate_bwd_swiglu_common(const coda_bwd_swiglu_args_t* a) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->dOut, a->W2, a->o, a->y, a->h, a->g, a->r, a->gamma, a->W1, a->dY, a->da, a->dgamma,
+                      a->dW1, a->dW2, a->s};
+  coda_status_t st = check_ptrs(ps, 15);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 512) return CODA_ERR_SHAPE;
+  if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype) || !dtype_ok(a->dW2_dtype)) return CODA_ERR_ARG;
+  return CODA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +90,8 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? bwd_swiglu_ws(M, D, N) : 0;
     case CODA_OP_CE_FWD: return dim_ok(N) ? ce_fwd_ws(M, N) : 0;
     case CODA_OP_CE_BWD: return 0;
+    case CODA_OP_UNFUSED_FWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? fwd_ws(M, D) : 0;
+    case CODA_OP_UNFUSED_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? unfused_bwd_swiglu_ws(M, D, N) : 0;
   }
   return 0;
 }
@@ -109,6 +122,14 @@ coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* 
     coda_status_t st = validate_bwd_common(a);
     if (st != CODA_OK) return st;
     return check_ws(ws, ws_bytes, unfused_bwd_ws(a->M, a->D));
+  }
+  if (op == CODA_OP_FWD_SWIGLU)  // the fused chain forward's workspace
+    return coda_validate_fwd_swiglu(static_cast<const coda_fwd_swiglu_args_t*>(args), ws, ws_bytes);
+  if (op == CODA_OP_BWD_SWIGLU) {
+    const coda_bwd_swiglu_args_t* a = static_cast<const coda_bwd_swiglu_args_t*>(args);
+    coda_status_t st = validate_bwd_swiglu_common(a);
+    if (st != CODA_OK) return st;
+    return check_ws(ws, ws_bytes, unfused_bwd_swiglu_ws(a->M, a->D, a->N));
   }
   return CODA_ERR_ARG;
 }
@@ -142,13 +163,8 @@ coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const vo
 }
 
 coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const void* ws, size_t ws_bytes) {
-  if (a == nullptr) return CODA_ERR_NULL;
-  const void* ps[] = {a->dOut, a->W2, a->o, a->y, a->h, a->g, a->r, a->gamma, a->W1, a->dY, a->da, a->dgamma,
-                      a->dW1, a->dW2, a->s};
-  coda_status_t st = check_ptrs(ps, 15);
+  coda_status_t st = validate_bwd_swiglu_common(a);
   if (st != CODA_OK) return st;
-  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 512) return CODA_ERR_SHAPE;
-  if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype) || !dtype_ok(a->dW2_dtype)) return CODA_ERR_ARG;
   return check_ws(ws, ws_bytes, bwd_swiglu_ws(a->M, a->D, a->N));
 }
 

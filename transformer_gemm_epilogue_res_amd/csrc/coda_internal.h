@@ -49,6 +49,10 @@ inline size_t bwd_ws(int64_t M, int64_t D) {
 inline size_t bwd_swiglu_ws(int64_t M, int64_t D, int64_t N) {
   return bwd_ws(M, D) + align256(size_t(M) * size_t(swiglu_s_cols(N)) * 4);
 }
+// Unfused SwiGLU backward workspace: the fused backward's, then dO [M, N / 2] bf16.
+inline size_t unfused_bwd_swiglu_ws(int64_t M, int64_t D, int64_t N) {
+  return bwd_ws(M, D) + align256(size_t(M) * size_t(N / 2) * 2);
+}
 
 }  // namespace coda
 

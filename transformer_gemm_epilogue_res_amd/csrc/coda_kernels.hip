@@ -10,6 +10,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -712,6 +713,66 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2* Pml, cons
   }
 }
 
+// Unfused SwiGLU: o = silu(gate) * up from the stored bf16 y, four pairs (16 bytes
+// of y) per thread; y [M, 2F] and o [M, F] are walked as flat arrays (pair p of
+// the flat o is y elements 2p, 2p + 1).
+template <bool F32>
+__global__ __launch_bounds__(256) void swiglu_rows_kernel(const uint16_t* y, void* o, int64_t quads) {
+  for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < quads; v += int64_t(gridDim.x) * 256) {
+    float f[8];
+    unpack8_bf16(reinterpret_cast<const uint4*>(y)[v], f);
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = f[2 * e] * sigmoidf_(f[2 * e]) * f[2 * e + 1];
+    if constexpr (F32) {
+      reinterpret_cast<float4*>(o)[v] = make_float4(q[0], q[1], q[2], q[3]);
+    } else {
+      reinterpret_cast<uint2*>(o)[v] = pack4_bf16(q[0], q[1], q[2], q[3]);
+    }
+  }
+}
+
+// Unfused SwiGLU backward: one 512-thread block per row i, from the stored bf16 dO:
+// dY_2f = dO up silu'(gate), dY_2f+1 = dO silu(gate) (bf16), s_i = sum dY y (fp32 dY,
+// bf16 y), and gr_i = bf16(r_i g_i).
+__global__ __launch_bounds__(kRowThreads) void swiglu_bwd_rows_kernel(const uint16_t* dO, const uint16_t* y,
+                                                                      const uint16_t* g, const float* r,
+                                                                      uint16_t* dY, float* s, uint16_t* gr,
+                                                                      int64_t F, int64_t D) {
+  __shared__ float red[kRowThreads / 64];
+  const int64_t i = blockIdx.x;
+  const float ri = r[i];
+  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
+  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
+  for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
+    float f[8];
+    unpack8_bf16(gs[v], f);
+    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
+    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
+    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  const uint2* ov = reinterpret_cast<const uint2*>(dO + i * F);
+  const uint4* yv = reinterpret_cast<const uint4*>(y + i * 2 * F);
+  uint4* dv = reinterpret_cast<uint4*>(dY + i * 2 * F);
+  float part = 0.f;
+  for (int64_t v = threadIdx.x; v < F / 4; v += kRowThreads) {
+    float d4[4], yy[8], d[8];
+    unpack4_bf16(ov[v], d4);
+    unpack8_bf16(yv[v], yy);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gate = yy[2 * e], up = yy[2 * e + 1], sg = sigmoidf_(gate);
+      d[2 * e] = d4[e] * up * (sg * (1.0f + gate * (1.0f - sg)));
+      d[2 * e + 1] = d4[e] * (gate * sg);
+      part += d[2 * e] * gate + d[2 * e + 1] * up;
+    }
+    const uint2 lo = pack4_bf16(d[0], d[1], d[2], d[3]), hi = pack4_bf16(d[4], d[5], d[6], d[7]);
+    dv[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  const float tot = block_sum512(part, red);
+  if (threadIdx.x == 0) s[i] = tot;
+}
+
 // Unfused: one block per row. h = t + z (fp32, stored bf16), r from the fp32 h,
 // n = bf16(r h gamma) for the second GEMM.
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* t, const uint16_t* z,
@@ -925,6 +986,36 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
     if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
     const GemmShape p1{a->M, a->N, a->D, n, a->D, a->W1, a->N};
     return to_status(gemm_plain(p1, true, false, a->y, a->N, a->y_dtype == CODA_F32, st));
+  }
+  if (op == CODA_OP_FWD_SWIGLU) {
+    const coda_fwd_swiglu_args_t* a = static_cast<const coda_fwd_swiglu_args_t*>(args);
+    if ((v = coda_fwd(&a->chain, ws, ws_bytes, stream)) != CODA_OK) return v;
+    const int64_t quads = a->chain.M * (a->chain.N / 2) / 4;
+    const unsigned grid = unsigned(std::min<int64_t>(ceil_div(quads, 256), 16384));
+    if (a->o_dtype == CODA_F32)
+      hipLaunchKernelGGL(swiglu_rows_kernel<true>, dim3(grid), dim3(256), 0, st, (const uint16_t*)a->chain.y, a->o, quads);
+    else
+      hipLaunchKernelGGL(swiglu_rows_kernel<false>, dim3(grid), dim3(256), 0, st, (const uint16_t*)a->chain.y, a->o, quads);
+    return to_status(hipGetLastError());
+  }
+  if (op == CODA_OP_BWD_SWIGLU) {
+    const coda_bwd_swiglu_args_t* a = static_cast<const coda_bwd_swiglu_args_t*>(args);
+    const int64_t F = a->N / 2;
+    uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
+    float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
+    uint16_t* dO = reinterpret_cast<uint16_t*>(ws_at(ws, bwd_ws(a->M, a->D)));
+    const GemmShape po{a->M, F, a->E, a->dOut, a->E, a->W2, a->E};
+    hipError_t e = gemm_plain(po, true, true, dO, F, false, st);
+    if (e != hipSuccess) return CODA_ERR_HIP;
+    hipLaunchKernelGGL(swiglu_bwd_rows_kernel, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)dO,
+                       (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, (uint16_t*)a->dY, a->s, gr, F, a->D);
+    if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+    const coda_bwd_args_t c{a->M, a->D, a->N, a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1,
+                            a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
+    if ((e = bwd_dgrad(&c, Pg, st)) != hipSuccess) return CODA_ERR_HIP;
+    if ((e = bwd_wgrad_dgamma(&c, gr, Pg, dgamma_rows(a->M), st)) != hipSuccess) return CODA_ERR_HIP;
+    const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
+    return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));
   }
   const coda_bwd_args_t* a = static_cast<const coda_bwd_args_t*>(args);
   const size_t md = align256(size_t(a->M) * size_t(a->D) * 2);
