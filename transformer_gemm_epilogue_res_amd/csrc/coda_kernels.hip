@@ -88,6 +88,39 @@ struct StageBf16 {
   __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
     flush_raw(reinterpret_cast<char*>(out), 2 * ldc, mb, 2 * nb, M);
   }
+  // The reverse of flush: rows mb .. mb+127 (0 past M), columns nb .. nb+63 of src[., ldc] into
+  // the staging area with whole-row 16-byte loads; get() then returns a lane's four values.
+  __device__ __forceinline__ void fill(const uint16_t* src, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
+    const int c = lane & 7;
+    constexpr int kBatch = kWaveTileM / 16;  // two batches of eight 16-byte loads in flight
+#pragma unroll
+    for (int q0 = 0; q0 < kWaveTileM / 8; q0 += kBatch) {
+      u32x4_t v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int64_t i = mb + 8 * (q0 + q) + (lane >> 3);
+        v[q] = i < M ? *reinterpret_cast<const u32x4_t*>(src + i * ldc + nb + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int row = 8 * (q0 + q) + (lane >> 3);
+        *reinterpret_cast<LDS_AS u32x4_t*>(base + row * 128 + ((c ^ (row & 7)) << 4)) = v[q];
+      }
+    }
+  }
+  // Sixteen bytes (chunk `chunk` of staged row `row`).
+  __device__ __forceinline__ u32x4_t get16(int row, int chunk) const {
+    return *reinterpret_cast<const LDS_AS u32x4_t*>(base + row * 128 + ((chunk ^ (row & 7)) << 4));
+  }
+  __device__ __forceinline__ void put16(int row, int chunk, u32x4_t v) const {
+    *reinterpret_cast<LDS_AS u32x4_t*>(base + row * 128 + ((chunk ^ (row & 7)) << 4)) = v;
+  }
+  __device__ __forceinline__ uint2 get(int tm, int tn) const {
+    const int li = lane & 15, lg = lane >> 4;
+    const int row = 16 * tm + li, c = 2 * tn + (lg >> 1);
+    const u32x2_t p = *reinterpret_cast<const LDS_AS u32x2_t*>(base + row * 128 + ((c ^ (row & 7)) << 4) + (lg & 1) * 8);
+    return make_uint2(p.x, p.y);
+  }
 };
 
 // out[rows of tile tm, columns of tile tn] for this lane, fp32 (16 bytes per lane).
@@ -186,7 +219,10 @@ struct EpiResidualSsq {
     float gam[kTN][4];
 #pragma unroll
     for (int tn = 0; tn < kTN; ++tn) unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
-    // h = acc + z in place, and the row sums of squares
+    // z through the staging area (whole 128-byte rows per load), then h = acc + z in place and
+    // the row sums of squares
+    const StageBf16 zs{stage, lane};
+    zs.fill(z, D, mb, nb, M);
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
@@ -194,8 +230,8 @@ struct EpiResidualSsq {
       float ssq = 0.f;
 #pragma unroll
       for (int tn = 0; tn < kTN; ++tn) {
-        float zz[4] = {0.f, 0.f, 0.f, 0.f};
-        if (ok) unpack4_bf16(*reinterpret_cast<const uint2*>(z + i * D + nb + 16 * tn + lj), zz);
+        float zz[4];
+        unpack4_bf16(zs.get(tm, tn), zz);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[tm][tn][e] += zz[e];
@@ -317,50 +353,102 @@ struct EpiRowScaleSwiglu {
   }
 };
 
+// Staging of 64 rows x 256 bytes (a wave's y or dY block for 4 of its 8 row
+// tiles): 16-byte chunk c of row r at c ^ (r & 15), so 16 lanes reading one
+// chunk of 16 consecutive rows, and 16 lanes reading one whole row, each touch
+// all 64 banks once.
+struct StageRows256 {
+  lds_char_t* base;
+  int lane;
+  __device__ __forceinline__ int off(int row, int chunk) const { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+  // rows mb .. mb+63 (0 past M), 128 bf16 columns from cb, of src[., ldc]
+  __device__ __forceinline__ void fill(const uint16_t* src, int64_t ldc, int64_t mb, int64_t cb, int64_t M) const {
+    const int c = lane & 15;
+#pragma unroll
+    for (int q0 = 0; q0 < 16; q0 += 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t i = mb + 4 * (q0 + q) + (lane >> 4);
+        v[q] = i < M ? *reinterpret_cast<const u32x4_t*>(src + i * ldc + cb + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<LDS_AS u32x4_t*>(base + off(4 * (q0 + q) + (lane >> 4), c)) = v[q];
+    }
+  }
+  __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t cb, int64_t M) const {
+    const int c = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 4 * q + (lane >> 4);
+      const u32x4_t v = *reinterpret_cast<const LDS_AS u32x4_t*>(base + off(row, c));
+      const int64_t i = mb + row;
+      if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldc + cb + 8 * c) = v;
+    }
+  }
+  __device__ __forceinline__ u32x4_t get(int row, int chunk) const {
+    return *reinterpret_cast<const LDS_AS u32x4_t*>(base + off(row, chunk));
+  }
+  __device__ __forceinline__ void put(int row, int chunk, u32x4_t v) const {
+    *reinterpret_cast<LDS_AS u32x4_t*>(base + off(row, chunk)) = v;
+  }
+};
+
 // Epilogue of the output projection's data gradient dO = dOut @ W2^T with the
 // SwiGLU backward (the dimension-expanding step): for the four features
-// f = nb + 16 tn + 4 (l / 16) + {0..3} of a lane it reads the saved gate/up pairs
-// y[i, 2f], y[i, 2f+1] (16 contiguous bytes), writes
+// f = nb + 16 tn + 4 (l / 16) + {0..3} of a lane it takes the saved gate/up pairs
+// y[i, 2f], y[i, 2f+1], writes
 //   dY[i, 2f] = dO up silu'(gate),  dY[i, 2f+1] = dO silu(gate)   (bf16)
 // and the row statistic's partial sum over the wave's 64 features,
 //   Ps[i, nb / 64] = sum over its 128 columns of dY y   (fp32 dY, bf16 y).
+// The wave's 128 x 128 block of y passes through the staging area in two halves
+// of 64 rows, read and written as whole 256-byte rows; each lane's dY replaces
+// the y it has just read, and the half is then stored.
 struct EpiSwigluBwd {
   const uint16_t* y;
   uint16_t* dY;
   float* Ps;
   int64_t M, F, pcols;
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t*) const {
-    const int li = lane & 15, lj = 4 * (lane >> 4);
+                                             lds_char_t* stage) const {
+    const int li = lane & 15, lg = lane >> 4;
+    const StageRows256 st{stage, lane};
+    auto do_half = [&](auto H) {  // H: std::integral_constant, so every acc index is a constant
+      constexpr int half = decltype(H)::value;
+      const int64_t hb = mb + 64 * half;  // first row of this half
+      st.fill(y, 2 * F, hb, 2 * nb, M);
 #pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      const bool ok = i < M;
-      float part = 0.f;
+      for (int t = 0; t < kTM / 2; ++t) {
+        const int tm = (kTM / 2) * half + t, row = 16 * t + li;
+        float part = 0.f;
 #pragma unroll
-      for (int tn = 0; tn < kTN; ++tn) {
-        const int64_t c = i * (2 * F) + 2 * (nb + 16 * tn + lj);
-        float yv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (ok) unpack8_bf16(*reinterpret_cast<const uint4*>(y + c), yv);
-        float d[8];
+        for (int tn = 0; tn < kTN; ++tn) {
+          const int chunk = 4 * tn + lg;
+          const u32x4_t raw = st.get(row, chunk);
+          float yv[8], d[8];
+          unpack8_bf16(make_uint4(raw.x, raw.y, raw.z, raw.w), yv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gate = yv[2 * e], up = yv[2 * e + 1], dO = acc[tm][tn][e];
-          const float sg = sigmoidf_(gate);
-          d[2 * e] = dO * up * (sg * (1.0f + gate * (1.0f - sg)));
-          d[2 * e + 1] = dO * (gate * sg);
-          part += d[2 * e] * gate + d[2 * e + 1] * up;
-        }
-        if (ok) {
+          for (int e = 0; e < 4; ++e) {
+            const float gate = yv[2 * e], up = yv[2 * e + 1], dO = acc[tm][tn][e];
+            const float sg = sigmoidf_(gate);
+            d[2 * e] = dO * up * (sg * (1.0f + gate * (1.0f - sg)));
+            d[2 * e + 1] = dO * (gate * sg);
+            part += d[2 * e] * gate + d[2 * e + 1] * up;
+          }
           const uint2 lo = pack4_bf16(d[0], d[1], d[2], d[3]), hi = pack4_bf16(d[4], d[5], d[6], d[7]);
-          *reinterpret_cast<uint4*>(dY + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          st.put(row, chunk, u32x4_t{lo.x, lo.y, hi.x, hi.y});
         }
+        // the 4 lanes l % 16 == li hold the rest of row i's 64 features
+        part += shfl_xor(part, 16);
+        part += shfl_xor(part, 32);
+        const int64_t i = hb + row;
+        if (lane < 16 && i < M) Ps[i * pcols + nb / kWaveTileN] = part;
       }
-      // the 4 lanes l % 16 == li hold the rest of row i's 64 features
-      part += shfl_xor(part, 16);
-      part += shfl_xor(part, 32);
-      if (lane < 16 && ok) Ps[i * pcols + nb / kWaveTileN] = part;
-    }
+      st.flush(dY, 2 * F, hb, 2 * nb, M);
+    };
+    do_half(std::integral_constant<int, 0>{});
+    do_half(std::integral_constant<int, 1>{});
   }
 };
 
