@@ -140,6 +140,26 @@ def test_ce_extreme_logits():
     check_fwd(f, ref, host["targets"])
 
 
+def test_ce_all_rows_ignored():
+    """Every target outside [0, V) (negative and >= V): loss 0, lse still the row's log-sum-exp,
+    and every gradient exactly 0."""
+    c = dict(M=70, D=256, V=512)
+    announce(f"coda_ce_fwd / coda_ce_bwd all rows ignored {c}")
+    host = inputs.lm_head_inputs(c["M"], c["D"], c["V"], seed=5)
+    host["targets"][:] = -100
+    host["targets"][::3] = c["V"]           # past the vocabulary: also ignored
+    d = {k: v.to(DEV) for k, v in host.items()}
+    f = L.ce_fwd(d["h"], d["W"], d["targets"])
+    b = L.ce_bwd(d["h"], d["W"], d["targets"], f["lse"], d["dloss"], dh_dtype=torch.float32, dW_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = orc.lm_head_cross_entropy(host["h"], host["W"], host["targets"])
+    assert not ref["valid"].any()
+    assert torch.all(f["loss"] == 0)
+    assert mt.normwise(f["lse"], ref["lse"]) <= TOL
+    for k in ("dlogits", "dh", "dW"):
+        assert torch.all(b[k] == 0), k
+
+
 @pytest.mark.slow
 def test_ce_llama3_8b_lm_head_sampled():
     c = dict(M=8192, D=4096, V=inputs.LM_VOCAB)

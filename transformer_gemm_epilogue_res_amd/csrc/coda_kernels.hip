@@ -553,6 +553,11 @@ struct EpiRmsNormBwd {
                                              lds_char_t* stage) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
     const float invD = 1.0f / float(D);
+    // h through the staging area first (whole 128-byte rows per load; before the row factors, so the
+    // loads do not share registers with them); each lane's bf16 da for a (tm, tn) tile then takes
+    // the place of the h values it has just read
+    const StageBf16 st{stage, lane};
+    st.fill(h, D, mb, nb, M);
     float rr[kTM], c2[kTM];
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
@@ -561,7 +566,6 @@ struct EpiRmsNormBwd {
       rr[tm] = ok ? r[i] : 0.f;
       c2[tm] = ok ? s[i] * rr[tm] * rr[tm] * invD : 0.f;
     }
-    const StageBf16 st{stage, lane};
     // da tile by tile, and the dgamma column partials
 #pragma unroll
     for (int tn = 0; tn < kTN; ++tn) {
@@ -570,9 +574,8 @@ struct EpiRmsNormBwd {
       unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gam);
 #pragma unroll
       for (int tm = 0; tm < kTM; ++tm) {
-        const int64_t i = mb + 16 * tm + li;
-        float hv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (i < M) unpack4_bf16(*reinterpret_cast<const uint2*>(h + i * D + j), hv);
+        float hv[4];
+        unpack4_bf16(st.get(tm, tn), hv);
         f32x4_t d;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
