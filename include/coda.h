@@ -278,7 +278,14 @@ typedef struct {
  * workspace of the fused forward holds the partial sums of squares; the
  * fused backward holds bf16(r*g) [M,D] and the dgamma column partials (the
  * SwiGLU backward also the partial sums of s); the unfused baseline also holds
- * its materialised intermediates. */
+ * its materialised intermediates. When the backward's data-gradient GEMM has
+ * fewer than 192 tiles of 256 x 256 (few rows M, e.g. a data-parallel shard),
+ * its contraction over N is split into S = min(ceil(256 / tiles), 8, N / 256)
+ * slices and the workspace also holds their fp32 partial products [S, M, D]
+ * (the dgamma partials then have ceil(M / 32) rows instead of ceil(M / 128)).
+ * The forward splits GEMM0 by the same rule (tiles = ceil(M/256) * D/256); its
+ * workspace, sized without K0, then also holds min(ceil(256 / tiles), 8) fp32
+ * partial products [., M, D]. */
 size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N);
 
 /* Host-only argument checks (no HIP call). Return CODA_OK or the first error. */
@@ -305,10 +312,12 @@ coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void
  * kernel. */
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
-/* The stages of coda_fwd and coda_bwd, one kernel each, for callers that
+/* The stages of coda_fwd and coda_bwd, one kernel each (two for a split GEMM), for callers that
  * interleave their own work or time the kernels. Running stages 0..n-1 in order
  * on one stream is exactly coda_fwd / coda_bwd; a stage reads what earlier
- * stages wrote into the outputs and the workspace. Each call validates the
+ * stages wrote into the outputs and the workspace. (A stage whose GEMM is split
+ * over its contraction -- see coda_workspace_bytes -- launches the GEMM and a row
+ * kernel that finishes its epilogue.) Each call validates the
  * whole argument set; a stage index out of range returns CODA_ERR_ARG.
  *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine,
  *             2 GEMM1 + row-scale epilogue

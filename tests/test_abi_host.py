@@ -85,25 +85,49 @@ def test_workspace_sizes():
     def a256(v):
         return (v + 255) // 256 * 256
     M, D, N = 300, 512, 768
-    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == a256(M * (D // 64) * 4)
-    assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4)
+    def fwd_ws(M, D):  # P [M, D/64], and min(ceil(256 / tiles), 8) split-K partials when GEMM0 has < 192 tiles
+        tiles = math.ceil(M / 256) * (D // 256)
+        S = 1 if tiles >= 192 else min(math.ceil(256 / tiles), 8)
+        return a256(M * (D // 64) * 4) + (a256(S * M * D * 4) if S > 1 else 0)
+    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == fwd_ws(M, D) == a256(M * 8 * 4) + a256(8 * M * D * 4)
+    assert L.workspace_bytes(L.CODA_OP_FWD, 8192, 4096, 28672) == a256(8192 * 64 * 4)   # 512 tiles: no split
+    # the backward splits the data-gradient contraction when its tiles cannot fill the chip (few rows)
+    S, ks = dgrad_split(M, D, N)
+    assert (S, ks) == (3, 256)                      # 4 tiles; 12 K steps of 64 -> 3 slices of 4 steps
+    assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == (
+        a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4) + a256(S * M * D * 4))
+    assert dgrad_split(8192, 4096, 28672) == (1, 0)  # the Llama-3-8B step: 512 tiles, no split
+    assert L.workspace_bytes(L.CODA_OP_BWD, 8192, 4096, 28672) == a256(8192 * 4096 * 2) + a256(64 * 4096 * 4)
+    assert dgrad_split(1024, 4096, 28672) == (4, 7168)  # a data-parallel shard: 64 tiles -> 4 slices
+    assert L.workspace_bytes(L.CODA_OP_BWD, 1024, 4096, 28672) == (
+        a256(1024 * 4096 * 2) + a256(32 * 4096 * 4) + a256(4 * 1024 * 4096 * 4))
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD, M, D, N) == 2 * a256(M * D * 2)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD, 0, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_FWD, M, 100, N) == 0
     N2 = 1024  # SwiGLU needs N % 512 == 0; its backward adds the s partials Ps[M, (N/2)/64]
-    assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N2) == a256(M * (D // 64) * 4)
-    assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == (
-        a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4) + a256(M * (N2 // 2 // 64) * 4))
+    assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
+    S2, _ = dgrad_split(M, D, N2)
+    bwd2 = a256(M * D * 2) + a256(math.ceil(M / (32 if S2 > 1 else 128)) * D * 4) + (a256(S2 * M * D * 4) if S2 > 1 else 0)
+    assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2 // 64) * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0
-    assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD_SWIGLU, M, D, N2) == a256(M * (D // 64) * 4)
-    assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N2) == (
-        a256(M * D * 2) + a256(math.ceil(M / 128) * D * 4) + a256(M * (N2 // 2) * 2))
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2) * 2)
     V = 128256  # cross-entropy: tile statistics (m, l) [M, V/64] and the target logits [M]
     assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, V) == a256(M * (V // 64) * 8) + a256(M * 4)
     assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, 1000) == 0
     assert L.workspace_bytes(L.CODA_OP_CE_BWD, M, D, V) == 0
+
+
+def dgrad_split(M, D, N):
+    """The documented split-K rule of the backward's data-gradient GEMM: (slices, columns per slice)."""
+    tiles = math.ceil(M / 256) * (D // 256)
+    S = min(math.ceil(256 / tiles), 8, N // 64 // 4)
+    if tiles >= 192 or S < 2:
+        return 1, 0
+    ks = math.ceil(math.ceil(N / S) / 64) * 64
+    return math.ceil(N / ks), ks
 
 
 def _fwd(**kw):

@@ -62,6 +62,7 @@ FWD_SMALL = {
     "ragged": dict(M=300, K0=256, D=512, N=768),
     "one_row": dict(M=1, K0=256, D=256, N=256),
     "k0_ne_d": dict(M=130, K0=768, D=256, N=512),
+    "deep_k0": dict(M=64, K0=1024, D=256, N=512),     # GEMM0 split over K0 into 4 slices
 }
 
 
@@ -131,7 +132,7 @@ def test_fwd_special_rows():
     assert mt.normwise(y[keep], ref["y"]) <= mt.Y_TOL
 
 
-FWD_LARGE = ["llama3_1b", "llama3_8b", "llama3_70b"]
+FWD_LARGE = ["llama3_1b", "llama3_8b", "llama3_70b", "llama3_8b_dp8"]
 
 
 @pytest.mark.slow
@@ -212,7 +213,7 @@ def test_bwd_small_full(name, unfused):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["llama3_8b", "llama3_1b", "llama3_70b"])
+@pytest.mark.parametrize("name", ["llama3_8b", "llama3_1b", "llama3_70b", "llama3_8b_dp8"])
 def test_bwd_llama_shapes_sampled(name):
     c = inputs.CONFIGS[name]
     announce(f"coda_bwd {name} {c} seed=0 (saved set from the oracle forward), sampled")

@@ -41,17 +41,67 @@ inline size_t ce_fwd_ws(int64_t M, int64_t V) {
 // Row count of the fused backward's dgamma partials Pg[ceil(M / kWaveTileM), D].
 inline int64_t dgamma_rows(int64_t M) { return ceil_div(M, kWaveTileM); }
 
-// Fused backward workspace: bf16(r g) [M, D], then Pg.
-inline size_t bwd_ws(int64_t M, int64_t D) {
-  return align256(size_t(M) * size_t(D) * 2) + align256(size_t(dgamma_rows(M)) * size_t(D) * 4);
+// Split-K of the data-gradient GEMM G = dY @ W1^T (contraction over N) when its
+// ceil(M / 256) * D / 256 tiles cannot fill the chip (few rows: a data-parallel
+// shard): S slices of kslice columns each (a multiple of the K step, at least four
+// steps), at most 8, aiming at one tile per CU. S = 1: no split.
+struct KSplit {
+  int64_t S, kslice;
+};
+inline KSplit dgrad_split(int64_t M, int64_t D, int64_t N) {
+  const int64_t tiles = ceil_div(M, kBM) * (D / kBN);
+  int64_t S = ceil_div(256, tiles);
+  if (S > 8) S = 8;
+  if (S > N / kBK / 4) S = N / kBK / 4;
+  if (tiles >= 192 || S < 2) return {1, 0};
+  const int64_t kslice = ceil_div(ceil_div(N, S), kBK) * kBK;
+  return {ceil_div(N, kslice), kslice};
+}
+// Split-K of GEMM0 (contraction over K0), by the same rule. The workspace is sized
+// without K0 for S_max = min(ceil(256 / tiles), 8) slices; a call uses
+// S = min(S_max, K0 / 256) of them (at least four K steps each).
+inline int64_t gemm0_split_max(int64_t M, int64_t D) {
+  const int64_t tiles = ceil_div(M, kBM) * (D / kBN);
+  if (tiles >= 192) return 1;
+  const int64_t S = ceil_div(256, tiles);
+  return S > 8 ? 8 : S;
+}
+inline KSplit gemm0_split(int64_t M, int64_t K0, int64_t D) {
+  int64_t S = gemm0_split_max(M, D);
+  if (S > K0 / kBK / 4) S = K0 / kBK / 4;
+  if (S < 2) return {1, 0};
+  const int64_t kslice = ceil_div(ceil_div(K0, S), kBK) * kBK;
+  return {ceil_div(K0, kslice), kslice};
+}
+// Fused forward workspace: the sums of squares P [M, D / 64], then (split-K only) the
+// fp32 partial products [S_max, M, D].
+inline size_t fwd_ws_p(int64_t M, int64_t D) { return align256(size_t(M) * size_t(ssq_cols(D)) * 4); }
+inline size_t fwd_ws(int64_t M, int64_t D) {
+  const int64_t S = gemm0_split_max(M, D);
+  return fwd_ws_p(M, D) + (S > 1 ? align256(size_t(S) * size_t(M) * size_t(D) * 4) : 0);
+}
+// Row group of the split-K reduction kernel (its dgamma partials have ceil(M / 32) rows).
+constexpr int kSplitRows = 32;
+inline int64_t bwd_pg_rows(int64_t M, int64_t D, int64_t N) {
+  return dgrad_split(M, D, N).S > 1 ? ceil_div(M, kSplitRows) : dgamma_rows(M);
+}
+// Fused backward workspace: bf16(r g) [M, D], then the dgamma partials Pg, then
+// (split-K only) the fp32 partial products [S, M, D].
+inline size_t bwd_ws_gr(int64_t M, int64_t D) { return align256(size_t(M) * size_t(D) * 2); }
+inline size_t bwd_ws_part(int64_t M, int64_t D, int64_t N) {
+  return bwd_ws_gr(M, D) + align256(size_t(bwd_pg_rows(M, D, N)) * size_t(D) * 4);
+}
+inline size_t bwd_ws(int64_t M, int64_t D, int64_t N) {
+  const KSplit k = dgrad_split(M, D, N);
+  return bwd_ws_part(M, D, N) + (k.S > 1 ? align256(size_t(k.S) * size_t(M) * size_t(D) * 4) : 0);
 }
 // SwiGLU backward workspace: the fused backward's, then the s partials Ps.
 inline size_t bwd_swiglu_ws(int64_t M, int64_t D, int64_t N) {
-  return bwd_ws(M, D) + align256(size_t(M) * size_t(swiglu_s_cols(N)) * 4);
+  return bwd_ws(M, D, N) + align256(size_t(M) * size_t(swiglu_s_cols(N)) * 4);
 }
 // Unfused SwiGLU backward workspace: the fused backward's, then dO [M, N / 2] bf16.
 inline size_t unfused_bwd_swiglu_ws(int64_t M, int64_t D, int64_t N) {
-  return bwd_ws(M, D) + align256(size_t(M) * size_t(N / 2) * 2);
+  return bwd_ws(M, D, N) + align256(size_t(M) * size_t(N / 2) * 2);
 }
 
 }  // namespace coda

@@ -165,6 +165,20 @@ struct EpiStore {
   }
 };
 
+// Split-K partial products: block row y writes its fp32 tile to part + y * sstride.
+struct EpiPartialF32 {
+  float* part;
+  int64_t ldc, M, sstride;
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t*) const {
+    float* out = part + int64_t(blockIdx.y) * sstride;
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < kTN; ++tn) store_f32(out, ldc, mb, nb, M, lane, tm, tn, acc[tm][tn]);
+  }
+};
+
 // The weight-gradient GEMM's store, which also finishes dgamma: before its
 // mainloop, block b reduces the 64-column chunks b, b + grid, ... of the
 // data-gradient GEMM's column partials, dgamma_j = sum_t Pg[t, j], in a fixed
@@ -611,10 +625,17 @@ template <class Epi>
 struct HasPrologue<Epi, decltype(std::declval<const Epi&>().prologue(nullptr), void())> : std::true_type {};
 
 template <bool A_K, bool B_K, class Epi>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p, const Epi epi) {
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, const Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   if constexpr (HasPrologue<Epi>::value) epi.prologue(smem);
+  GemmShape p = p0;
+  if (p0.kslice > 0) {  // split-K: this block row's slice of the contraction (k offset along the k-contiguous dim or the rows)
+    const int64_t k0 = int64_t(blockIdx.y) * p0.kslice;
+    p.K = p0.K - k0 < p0.kslice ? p0.K - k0 : p0.kslice;
+    p.A = static_cast<const char*>(p0.A) + 2 * (A_K ? k0 : k0 * p0.lda);
+    p.B = static_cast<const char*>(p0.B) + 2 * (B_K ? k0 : k0 * p0.ldb);
+  }
   int tile_m, tile_n;
   map_tile(p.M, p.N, tile_m, tile_n);
   const int64_t m0 = int64_t(tile_m) * kBM, n0 = int64_t(tile_n) * kBN;
@@ -804,6 +825,84 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2* Pml, cons
   }
 }
 
+// Split-K data gradient: G = the S slices' fp32 partial products summed in order, then the
+// RMSNorm-backward algebra of the fused epilogue, da = r gamma G - (s r^2 / D) h, and the
+// dgamma partials of each kSplitRows-row group, Pg[group, j] = sum of G r h. A block covers
+// 1024 columns (4 per thread) of kSplitRows rows.
+template <bool F32>
+__global__ __launch_bounds__(256) void splitk_rmsnorm_bwd_kernel(const float* part, int S, int64_t sstride,
+                                                                 const uint16_t* h, const float* r, const float* s,
+                                                                 const uint16_t* gamma, void* da, float* Pg,
+                                                                 int64_t M, int64_t D) {
+  const int64_t j = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (j >= D) return;
+  const int64_t i0 = int64_t(blockIdx.y) * kSplitRows;
+  const int64_t i1 = i0 + kSplitRows < M ? i0 + kSplitRows : M;
+  const float invD = 1.0f / float(D);
+  float gm[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
+  unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gm);
+  for (int64_t i = i0; i < i1; ++i) {
+    float G[4];
+    {
+      const float4 v = *reinterpret_cast<const float4*>(part + i * D + j);
+      G[0] = v.x, G[1] = v.y, G[2] = v.z, G[3] = v.w;
+    }
+    for (int t = 1; t < S; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(part + t * sstride + i * D + j);
+      G[0] += v.x, G[1] += v.y, G[2] += v.z, G[3] += v.w;
+    }
+    float hv[4], d[4];
+    unpack4_bf16(*reinterpret_cast<const uint2*>(h + i * D + j), hv);
+    const float ri = r[i], c2 = s[i] * ri * ri * invD;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cs[e] += G[e] * ri * hv[e];
+      d[e] = ri * gm[e] * G[e] - c2 * hv[e];
+    }
+    if constexpr (F32) *reinterpret_cast<float4*>(static_cast<float*>(da) + i * D + j) = make_float4(d[0], d[1], d[2], d[3]);
+    else *reinterpret_cast<uint2*>(static_cast<uint16_t*>(da) + i * D + j) = pack4_bf16(d[0], d[1], d[2], d[3]);
+  }
+  *reinterpret_cast<float4*>(Pg + int64_t(blockIdx.y) * D + j) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+}
+
+// Split-K GEMM0: h = the slices' fp32 partial products summed in order + z (fp32), stored
+// bf16; g = bf16(h gamma) from the fp32 h; P[i, j / 64] = the sum of squares of the fp32 h
+// over each 64-column chunk -- what the fused epilogue computes. A block covers 1024 columns
+// (4 per thread; 16 threads per chunk) of one row.
+__global__ __launch_bounds__(256) void splitk_residual_kernel(const float* part, int S, int64_t sstride,
+                                                              const uint16_t* z, const uint16_t* gamma, uint16_t* h,
+                                                              uint16_t* g, float* P, int64_t D, int64_t pcols) {
+  const int64_t i = blockIdx.y;
+  const int64_t j = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const bool ok = j < D;  // uniform over each 16-thread chunk group (D is a multiple of 256)
+  float ssq = 0.f;
+  if (ok) {
+    float hv[4], zz[4], gm[4];
+    {
+      const float4 v = *reinterpret_cast<const float4*>(part + i * D + j);
+      hv[0] = v.x, hv[1] = v.y, hv[2] = v.z, hv[3] = v.w;
+    }
+    for (int t = 1; t < S; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(part + t * sstride + i * D + j);
+      hv[0] += v.x, hv[1] += v.y, hv[2] += v.z, hv[3] += v.w;
+    }
+    unpack4_bf16(*reinterpret_cast<const uint2*>(z + i * D + j), zz);
+    unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gm);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hv[e] += zz[e];
+      ssq += hv[e] * hv[e];
+    }
+    *reinterpret_cast<uint2*>(h + i * D + j) = pack4_bf16(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<uint2*>(g + i * D + j) = pack4_bf16(hv[0] * gm[0], hv[1] * gm[1], hv[2] * gm[2], hv[3] * gm[3]);
+  }
+  ssq += shfl_xor(ssq, 1);
+  ssq += shfl_xor(ssq, 2);
+  ssq += shfl_xor(ssq, 4);
+  ssq += shfl_xor(ssq, 8);
+  if (ok && (threadIdx.x & 15) == 0) P[i * pcols + j / kWaveTileN] = ssq;
+}
+
 // Unfused SwiGLU: o = silu(gate) * up from the stored bf16 y, four pairs (16 bytes
 // of y) per thread; y [M, 2F] and o [M, F] are walked as flat arrays (pair p of
 // the flat o is y elements 2p, 2p + 1).
@@ -946,7 +1045,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* G, con
 template <bool A_K, bool B_K, class Epi>
 hipError_t launch_gemm(const GemmShape& p, const Epi& epi, hipStream_t st) {
   const int64_t blocks = ceil_div(p.M, kBM) * (p.N / kBN);
-  hipLaunchKernelGGL((gemm_kernel<A_K, B_K, Epi>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, p, epi);
+  const int64_t slices = p.kslice > 0 ? ceil_div(p.K, p.kslice) : 1;
+  hipLaunchKernelGGL((gemm_kernel<A_K, B_K, Epi>), dim3(unsigned(blocks), unsigned(slices)), dim3(kThreads), 0, st, p,
+                     epi);
   return hipGetLastError();
 }
 
@@ -993,8 +1094,25 @@ hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, h
   return hipGetLastError();
 }
 
-hipError_t bwd_dgrad(const coda_bwd_args_t* a, float* Pg, hipStream_t st) {
+// The data gradient with its RMSNorm-backward epilogue; with few rows (dgrad_split) the
+// contraction is split over S block rows into fp32 partials `part` and a row kernel finishes.
+hipError_t bwd_dgrad(const coda_bwd_args_t* a, float* Pg, float* part, hipStream_t st) {
   // G = dY @ W1^T: A = dY [M, N] (k contiguous), B(k=n, j) = W1[j, n] (k contiguous)
+  const KSplit ks = dgrad_split(a->M, a->D, a->N);
+  if (ks.S > 1) {
+    const int64_t sstride = a->M * a->D;
+    const GemmShape pp{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N, ks.kslice};
+    hipError_t e = launch_gemm<true, true>(pp, EpiPartialF32{part, a->D, a->M, sstride}, st);
+    if (e != hipSuccess) return e;
+    const dim3 grid(unsigned(ceil_div(a->D, 1024)), unsigned(ceil_div(a->M, kSplitRows)));
+    if (a->da_dtype == CODA_F32)
+      hipLaunchKernelGGL(splitk_rmsnorm_bwd_kernel<true>, grid, dim3(256), 0, st, (const float*)part, int(ks.S), sstride,
+                         (const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D);
+    else
+      hipLaunchKernelGGL(splitk_rmsnorm_bwd_kernel<false>, grid, dim3(256), 0, st, (const float*)part, int(ks.S), sstride,
+                         (const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D);
+    return hipGetLastError();
+  }
   const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
   if (a->da_dtype == CODA_F32)
     return launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
@@ -1002,6 +1120,18 @@ hipError_t bwd_dgrad(const coda_bwd_args_t* a, float* Pg, hipStream_t st) {
 }
 
 coda_status_t to_status(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
+
+// The fused backward's workspace regions (layout in coda_internal.h).
+struct BwdWorkspace {
+  uint16_t* gr;     // bf16(r g) [M, D]
+  float* Pg;        // dgamma partials [pg_rows, D]
+  float* part;      // split-K partial products [S, M, D] (split only)
+  int64_t pg_rows;
+};
+BwdWorkspace bwd_workspace(void* ws, int64_t M, int64_t D, int64_t N) {
+  return {reinterpret_cast<uint16_t*>(ws), reinterpret_cast<float*>(ws_at(ws, bwd_ws_gr(M, D))),
+          reinterpret_cast<float*>(ws_at(ws, bwd_ws_part(M, D, N))), bwd_pg_rows(M, D, N)};
+}
 
 }  // namespace coda
 
@@ -1017,6 +1147,18 @@ coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size
   float* P = reinterpret_cast<float*>(ws);
   const int64_t pcols = ssq_cols(a->D);
   if (stage == 0) {  // GEMM0 x @ W0 with the residual / h / g / sum-of-squares epilogue
+    const KSplit ks = gemm0_split(a->M, a->K0, a->D);
+    if (ks.S > 1) {  // few rows: split the contraction, then a row kernel does the epilogue's work
+      float* part = reinterpret_cast<float*>(ws_at(ws, fwd_ws_p(a->M, a->D)));
+      const int64_t sstride = a->M * a->D;
+      const GemmShape pp{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D, ks.kslice};
+      hipError_t e = launch_gemm<true, false>(pp, EpiPartialF32{part, a->D, a->M, sstride}, st);
+      if (e != hipSuccess) return CODA_ERR_HIP;
+      hipLaunchKernelGGL(splitk_residual_kernel, dim3(unsigned(ceil_div(a->D, 1024)), unsigned(a->M)), dim3(256), 0, st,
+                         (const float*)part, int(ks.S), sstride, (const uint16_t*)a->z, (const uint16_t*)a->gamma,
+                         (uint16_t*)a->h, (uint16_t*)a->g, P, a->D, pcols);
+      return to_status(hipGetLastError());
+    }
     const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
     return to_status(launch_gemm<true, false>(
         p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st));
@@ -1045,11 +1187,10 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
   if (v != CODA_OK) return v;
   if (stage < 0 || stage >= CODA_BWD_STAGES) return CODA_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
-  float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
-  if (stage == 0) return to_status(bwd_rowstat(a, gr, st));
-  if (stage == 1) return to_status(bwd_dgrad(a, Pg, st));
-  return to_status(bwd_wgrad_dgamma(a, gr, Pg, dgamma_rows(a->M), st));
+  const BwdWorkspace w = bwd_workspace(ws, a->M, a->D, a->N);
+  if (stage == 0) return to_status(bwd_rowstat(a, w.gr, st));
+  if (stage == 1) return to_status(bwd_dgrad(a, w.Pg, w.part, st));
+  return to_status(bwd_wgrad_dgamma(a, w.gr, w.Pg, w.pg_rows, st));
 }
 
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
@@ -1092,9 +1233,9 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
   if (op == CODA_OP_BWD_SWIGLU) {
     const coda_bwd_swiglu_args_t* a = static_cast<const coda_bwd_swiglu_args_t*>(args);
     const int64_t F = a->N / 2;
-    uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
-    float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
-    uint16_t* dO = reinterpret_cast<uint16_t*>(ws_at(ws, bwd_ws(a->M, a->D)));
+    const BwdWorkspace w = bwd_workspace(ws, a->M, a->D, a->N);
+    uint16_t* gr = w.gr;
+    uint16_t* dO = reinterpret_cast<uint16_t*>(ws_at(ws, bwd_ws(a->M, a->D, a->N)));
     const GemmShape po{a->M, F, a->E, a->dOut, a->E, a->W2, a->E};
     hipError_t e = gemm_plain(po, true, true, dO, F, false, st);
     if (e != hipSuccess) return CODA_ERR_HIP;
@@ -1103,8 +1244,8 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
     if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
     const coda_bwd_args_t c{a->M, a->D, a->N, a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1,
                             a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
-    if ((e = bwd_dgrad(&c, Pg, st)) != hipSuccess) return CODA_ERR_HIP;
-    if ((e = bwd_wgrad_dgamma(&c, gr, Pg, dgamma_rows(a->M), st)) != hipSuccess) return CODA_ERR_HIP;
+    if ((e = bwd_dgrad(&c, w.Pg, w.part, st)) != hipSuccess) return CODA_ERR_HIP;
+    if ((e = bwd_wgrad_dgamma(&c, gr, w.Pg, w.pg_rows, st)) != hipSuccess) return CODA_ERR_HIP;
     const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
     return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));
   }
@@ -1147,8 +1288,9 @@ coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t 
   if (v != CODA_OK) return v;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t F = a->N / 2, pcols = swiglu_s_cols(a->N);
-  uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
-  float* Ps = reinterpret_cast<float*>(ws_at(ws, bwd_ws(a->M, a->D)));
+  const BwdWorkspace w = bwd_workspace(ws, a->M, a->D, a->N);
+  uint16_t* gr = w.gr;
+  float* Ps = reinterpret_cast<float*>(ws_at(ws, bwd_ws(a->M, a->D, a->N)));
   // dO = dOut @ W2^T with the SwiGLU-backward epilogue: A = dOut [M, E], B(k=e, f) = W2[f, e] (both k contiguous)
   const GemmShape po{a->M, F, a->E, a->dOut, a->E, a->W2, a->E};
   hipError_t e = launch_gemm<true, true>(po, EpiSwigluBwd{(const uint16_t*)a->y, (uint16_t*)a->dY, Ps, a->M, F, pcols}, st);
@@ -1159,9 +1301,8 @@ coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t 
   // the chain's backward on dY, with s and bf16(r g) already in place
   const coda_bwd_args_t c{a->M, a->D, a->N, a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1,
                           a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
-  float* Pg = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(a->D) * 2)));
-  if ((e = bwd_dgrad(&c, Pg, st)) != hipSuccess) return CODA_ERR_HIP;
-  if ((e = bwd_wgrad_dgamma(&c, gr, Pg, dgamma_rows(a->M), st)) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_dgrad(&c, w.Pg, w.part, st)) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = bwd_wgrad_dgamma(&c, gr, w.Pg, w.pg_rows, st)) != hipSuccess) return CODA_ERR_HIP;
   // dW2 [F, E] = o^T @ dOut: A(m=f, k=i) = o[i, f] (m contiguous), B(k=i, n=e) = dOut[i, e] (n contiguous), K = M
   const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
   return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));

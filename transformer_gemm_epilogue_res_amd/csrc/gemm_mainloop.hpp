@@ -314,6 +314,7 @@ struct GemmShape {
   int64_t lda;
   const void* B;    // B_K: [N, ldb] (k contiguous); else [K, ldb] (n contiguous)
   int64_t ldb;
+  int64_t kslice;   // split-K: block row blockIdx.y contracts k in [y kslice, (y + 1) kslice); 0 = no split
 };
 
 // One wave's view of the loop. The A tile of K step s lives in A slot s % 3,

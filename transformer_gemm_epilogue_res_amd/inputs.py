@@ -44,6 +44,8 @@ CONFIGS = {
     "llama3_1b": dict(M=8192, K0=2048, D=2048, N=16384),
     "llama3_8b": dict(M=8192, K0=4096, D=4096, N=28672),
     "llama3_70b": dict(M=8192, K0=8192, D=8192, N=57344),
+    # one GPU's share of the 8B batch under 8-way data parallelism
+    "llama3_8b_dp8": dict(M=1024, K0=4096, D=4096, N=28672),
 }
 
 
