@@ -150,6 +150,7 @@ def main():
     ap.add_argument("--no-swiglu", action="store_true", help="skip timing the SwiGLU block")
     ap.add_argument("--no-ce", action="store_true", help="skip timing the cross-entropy LM head")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache variant of the step")
+    ap.add_argument("--no-shard", action="store_true", help="skip the data-parallel shard (M / 8) step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many bytes (a reference kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -281,6 +282,34 @@ def main():
         cold = {"ms_per_step_median": round(med, 4), "tflops": round((fwd_flop + bwd_flop) / med / 1e9, 1)}
         log(f"[bench] cold-cache step (median) {med:.3f} ms, {cold['tflops']} TFLOP/s")
 
+    # One GPU's share of the batch under 8-way data parallelism (M / 8 rows): the same step at
+    # the shard's shape, where GEMM0 and dgrad split their contraction.
+    shard = None
+    if not args.no_shard:
+        Ms = M // 8
+        xs, zs, dYs = x[:Ms].contiguous(), z[:Ms].contiguous(), dY[:Ms].contiguous()
+        sfo = {k: v[:Ms].contiguous() for k, v in fo.items()}
+        sbo = {"da": bo["da"][:Ms].contiguous(), "dgamma": bo["dgamma"], "dW1": bo["dW1"], "s": bo["s"][:Ms].contiguous()}
+        SF = L.bind_fwd(xs, W0, zs, gamma, W1, inputs.EPS, sfo, L.workspace(L.CODA_OP_FWD, Ms, D, N, dev))
+        SBk = L.bind_bwd(dYs, sfo["y"], sfo["h"], sfo["g"], sfo["r"], gamma, W1, sbo,
+                         L.workspace(L.CODA_OP_BWD, Ms, D, N, dev))
+        for _ in range(2):
+            SF.run(sp)
+            SBk.run(sp)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            SF.run(sp)
+            SBk.run(sp)
+        b.record(stream)
+        torch.cuda.synchronize()
+        sms = a.elapsed_time(b) / args.steps
+        sfl = 2 * Ms * K0 * D + 6 * Ms * D * N
+        shard = {"M": Ms, "ms_per_step": round(sms, 4), "tflops": round(sfl / sms / 1e9, 1),
+                 "pct_peak": round(100 * sfl / sms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+        log(f"[bench] data-parallel shard (M = {Ms}): step {sms:.3f} ms, {shard['tflops']} TFLOP/s")
+        del xs, zs, dYs, sfo, sbo, SF, SBk
+
     # The backward through the first GEMM (dx, dW0 from the step's bf16 da): not part
     # of the headline step (the chain's metric stops at da), reported beside it.
     g0o = {"dx": torch.empty(M, K0, dtype=bf, device=dev), "dW0": torch.empty(K0, D, dtype=bf, device=dev)}
@@ -408,7 +437,7 @@ def main():
                    "eps": inputs.EPS, "parallelism": "single GPU"},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "step_ms_p10_p50_p90": [round(float(q), 4) for q in _quantiles(step_ms, (0.1, 0.5, 0.9))],
-        "cold_cache": cold,
+        "cold_cache": cold, "dp8_shard": shard,
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / fwd_ms / 1e9, 1),
                 "pct_peak": round(100 * fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
