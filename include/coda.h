@@ -276,7 +276,7 @@ typedef struct {
 
 /* Bytes of device workspace `op` needs for these sizes (0 when none). The
  * workspace of the fused forward holds the partial sums of squares; the
- * fused backward holds bf16(r*g) [M,D] and the dgamma column partials (the
+ * fused backward holds bf16(r*g) transposed, [D, M rounded up to 64], and the dgamma column partials (the
  * SwiGLU backward also the partial sums of s); the unfused baseline also holds
  * its materialised intermediates. When the backward's data-gradient GEMM has
  * fewer than 192 tiles of 256 x 256 (few rows M, e.g. a data-parallel shard),
@@ -305,7 +305,8 @@ coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* 
  * row-statistic combine (r) -> GEMM1 + epilogue (row scale r). */
 coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
-/* Fused backward: row statistic s and bf16(r*g) -> G = dY@W1^T with the
+/* Fused backward: row statistic s and bf16(r*g) (transposed, so the dW1
+ * GEMM's left operand is contiguous along its contraction) -> G = dY@W1^T with the
  * RMSNorm-backward epilogue (da, dgamma column partials) -> dW1 = bf16(r*g)^T @ dY,
  * whose blocks also reduce the dgamma partials, 64 columns at a time in a fixed
  * order, before their own tiles: the auxiliary reduction folded into the next
@@ -321,8 +322,9 @@ coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void
  * whole argument set; a stage index out of range returns CODA_ERR_ARG.
  *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine,
  *             2 GEMM1 + row-scale epilogue
- *   backward: 0 s and bf16(r*g), 1 G = dY@W1^T + RMSNorm-backward epilogue,
- *             2 dW1 GEMM, whose first blocks also reduce the dgamma partials */
+ *   backward: 0 s, then bf16(r*g) transposed for the dW1 GEMM (two kernels),
+ *             1 G = dY@W1^T + RMSNorm-backward epilogue, 2 dW1 GEMM, whose blocks
+ *             also reduce the dgamma partials */
 #define CODA_FWD_STAGES 3
 #define CODA_BWD_STAGES 3
 coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);

@@ -94,8 +94,10 @@ def test_workspace_sizes():
     # the backward splits the data-gradient contraction when its tiles cannot fill the chip (few rows)
     S, ks = dgrad_split(M, D, N)
     assert (S, ks) == (3, 256)                      # 4 tiles; 12 K steps of 64 -> 3 slices of 4 steps
+    def gr_bytes(M, D):  # bf16(r g) transposed, [D, M rounded up to 64]
+        return a256(D * math.ceil(M / 64) * 64 * 2)
     assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == (
-        a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4) + a256(S * M * D * 4))
+        gr_bytes(M, D) + a256(math.ceil(M / 32) * D * 4) + a256(S * M * D * 4))
     assert dgrad_split(8192, 4096, 28672) == (1, 0)  # the Llama-3-8B step: 512 tiles, no split
     assert L.workspace_bytes(L.CODA_OP_BWD, 8192, 4096, 28672) == a256(8192 * 4096 * 2) + a256(64 * 4096 * 4)
     assert dgrad_split(1024, 4096, 28672) == (4, 7168)  # a data-parallel shard: 64 tiles -> 4 slices
@@ -108,7 +110,7 @@ def test_workspace_sizes():
     N2 = 1024  # SwiGLU needs N % 512 == 0; its backward adds the s partials Ps[M, (N/2)/64]
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
     S2, _ = dgrad_split(M, D, N2)
-    bwd2 = a256(M * D * 2) + a256(math.ceil(M / (32 if S2 > 1 else 128)) * D * 4) + (a256(S2 * M * D * 4) if S2 > 1 else 0)
+    bwd2 = gr_bytes(M, D) + a256(math.ceil(M / (32 if S2 > 1 else 128)) * D * 4) + (a256(S2 * M * D * 4) if S2 > 1 else 0)
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2 // 64) * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0

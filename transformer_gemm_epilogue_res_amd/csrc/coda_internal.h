@@ -85,9 +85,11 @@ constexpr int kSplitRows = 32;
 inline int64_t bwd_pg_rows(int64_t M, int64_t D, int64_t N) {
   return dgrad_split(M, D, N).S > 1 ? ceil_div(M, kSplitRows) : dgamma_rows(M);
 }
-// Fused backward workspace: bf16(r g) [M, D], then the dgamma partials Pg, then
+// Fused backward workspace: bf16(r g) transposed, [D, gr_cols(M)], then the dgamma partials Pg, then
 // (split-K only) the fp32 partial products [S, M, D].
-inline size_t bwd_ws_gr(int64_t M, int64_t D) { return align256(size_t(M) * size_t(D) * 2); }
+// Rows of the transposed bf16(r g): M rounded up to the K step (the pad is zero).
+inline int64_t gr_cols(int64_t M) { return ceil_div(M, kBK) * kBK; }
+inline size_t bwd_ws_gr(int64_t M, int64_t D) { return align256(size_t(D) * size_t(gr_cols(M)) * 2); }
 inline size_t bwd_ws_part(int64_t M, int64_t D, int64_t N) {
   return bwd_ws_gr(M, D) + align256(size_t(bwd_pg_rows(M, D, N)) * size_t(D) * 4);
 }

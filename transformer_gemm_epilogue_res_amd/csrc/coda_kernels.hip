@@ -698,27 +698,30 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
   return t;
 }
 
-// One 512-thread block per row i: s_i = sum_n dY_in y_in (fp32) and
-// gr_i = bf16(r_i g_i). The row is read in rounds of kRowUnroll x 16 bytes per
+// One 512-thread block per row i: s_i = sum_n dY_in y_in (fp32) and, with GR (the
+// unfused baseline's row layout), gr_i = bf16(r_i g_i). The row is read in rounds of kRowUnroll x 16 bytes per
 // thread of each input, all loads of a round issued before any is used (one
 // round covers an N = 28672 row).
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 7;
+template <bool GR>
 __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY, const uint16_t* y,
                                                               const uint16_t* g, const float* r, float* s,
                                                               uint16_t* gr, int64_t N, int64_t D) {
   __shared__ float red[kRowThreads / 64];
   const int64_t i = blockIdx.x;
   // bf16(r g) first: it does not wait for s, and its loads join the row's in the same round
-  const float ri = r[i];
-  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
-  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
-  for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
-    float f[8];
-    unpack8_bf16(gs[v], f);
-    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
-    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
-    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  if constexpr (GR) {
+    const float ri = r[i];
+    const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
+    uint4* go = reinterpret_cast<uint4*>(gr + i * D);
+    for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
+      float f[8];
+      unpack8_bf16(gs[v], f);
+      const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
+      const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
+      go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
   }
   const uint4* a = reinterpret_cast<const uint4*>(dY + i * N);
   const uint4* b = reinterpret_cast<const uint4*>(y + i * N);
@@ -767,26 +770,50 @@ __global__ __launch_bounds__(256) void dgamma_combine_kernel(const float* Pg, fl
   }
 }
 
-// SwiGLU backward: one 256-thread block per row i: s_i = sum_t Ps[i, t] (fixed
-// order) and gr_i = bf16(r_i g_i).
-__global__ __launch_bounds__(256) void scombine_gr_kernel(const float* Ps, const uint16_t* g, const float* r,
-                                                          float* s, uint16_t* gr, int64_t pcols, int64_t D) {
+// bf16(r g) transposed for the weight-gradient GEMM, whose contraction runs over the
+// rows i: grT[j, i] = bf16(r_i g_ij) for i < M and 0 for M <= i < ldt (the pad to the
+// K step). A 256-thread block moves a 64 x 64 tile through LDS: 16-byte row loads of g,
+// 2-byte transposed LDS writes, 16-byte row stores of grT.
+__global__ __launch_bounds__(256) void gr_transpose_kernel(const uint16_t* g, const float* r, uint16_t* grT, int64_t M,
+                                                           int64_t D, int64_t ldt) {
+  constexpr int kT = 64, kLd = 72;  // LDS row stride 144 bytes: 16-byte aligned rows, spread banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kT * kLd];
+  const int64_t j0 = int64_t(blockIdx.x) * kT, i0 = int64_t(blockIdx.y) * kT;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = threadIdx.x + 256 * q, row = c >> 3, chunk = c & 7;  // row i0 + row, columns j0 + 8 chunk ..
+    const int64_t i = i0 + row;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (i < M) {
+      unpack8_bf16(*reinterpret_cast<const uint4*>(g + i * D + j0 + 8 * chunk), f);
+      const float ri = r[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= ri;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t pk = pack2_bf16(f[e], f[e + 1]);
+      tile[(8 * chunk + e) * kLd + row] = uint16_t(pk & 0xffffu);
+      tile[(8 * chunk + e + 1) * kLd + row] = uint16_t(pk >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = threadIdx.x + 256 * q, jr = c >> 3, chunk = c & 7;  // grT row j0 + jr, columns i0 + 8 chunk ..
+    const uint4 v = *reinterpret_cast<const uint4*>(&tile[jr * kLd + 8 * chunk]);
+    *reinterpret_cast<uint4*>(grT + (j0 + jr) * ldt + i0 + 8 * chunk) = v;
+  }
+}
+
+// SwiGLU backward: one 256-thread block per row i: s_i = sum_t Ps[i, t] (fixed order).
+__global__ __launch_bounds__(256) void scombine_kernel(const float* Ps, float* s, int64_t pcols) {
   __shared__ float red[4];
   const int64_t i = blockIdx.x;
   float acc = 0.f;
   for (int64_t t = threadIdx.x; t < pcols; t += 256) acc += Ps[i * pcols + t];
   const float tot = block_sum256(acc, red);
   if (threadIdx.x == 0) s[i] = tot;
-  const float ri = r[i];
-  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
-  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
-  for (int64_t v = threadIdx.x; v < D / 8; v += 256) {
-    float f[8];
-    unpack8_bf16(gs[v], f);
-    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
-    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
-    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
 }
 
 __device__ __forceinline__ float block_max256(float v, float* red) {
@@ -923,24 +950,12 @@ __global__ __launch_bounds__(256) void swiglu_rows_kernel(const uint16_t* y, voi
 }
 
 // Unfused SwiGLU backward: one 512-thread block per row i, from the stored bf16 dO:
-// dY_2f = dO up silu'(gate), dY_2f+1 = dO silu(gate) (bf16), s_i = sum dY y (fp32 dY,
-// bf16 y), and gr_i = bf16(r_i g_i).
+// dY_2f = dO up silu'(gate), dY_2f+1 = dO silu(gate) (bf16) and s_i = sum dY y (fp32 dY,
+// bf16 y).
 __global__ __launch_bounds__(kRowThreads) void swiglu_bwd_rows_kernel(const uint16_t* dO, const uint16_t* y,
-                                                                      const uint16_t* g, const float* r,
-                                                                      uint16_t* dY, float* s, uint16_t* gr,
-                                                                      int64_t F, int64_t D) {
+                                                                      uint16_t* dY, float* s, int64_t F) {
   __shared__ float red[kRowThreads / 64];
   const int64_t i = blockIdx.x;
-  const float ri = r[i];
-  const uint4* gs = reinterpret_cast<const uint4*>(g + i * D);
-  uint4* go = reinterpret_cast<uint4*>(gr + i * D);
-  for (int64_t v = threadIdx.x; v < D / 8; v += kRowThreads) {
-    float f[8];
-    unpack8_bf16(gs[v], f);
-    const uint2 lo = pack4_bf16(ri * f[0], ri * f[1], ri * f[2], ri * f[3]);
-    const uint2 hi = pack4_bf16(ri * f[4], ri * f[5], ri * f[6], ri * f[7]);
-    go[v] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
   const uint2* ov = reinterpret_cast<const uint2*>(dO + i * F);
   const uint4* yv = reinterpret_cast<const uint4*>(y + i * 2 * F);
   uint4* dv = reinterpret_cast<uint4*>(dY + i * 2 * F);
@@ -1067,8 +1082,26 @@ hipError_t gemm_plain(const GemmShape& p, bool a_k, bool b_k, void* C, int64_t l
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // s and bf16(r * g), then the weight gradient dW1 = bf16(r g)^T @ dY.
-hipError_t bwd_rowstat(const coda_bwd_args_t* a, uint16_t* gr, hipStream_t st) {
-  hipLaunchKernelGGL(rowstat_kernel, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)a->dY,
+// bf16(r g) transposed into grT [D, gr_cols(M)] for the weight-gradient GEMM.
+hipError_t gr_transpose(const uint16_t* g, const float* r, uint16_t* grT, int64_t M, int64_t D, hipStream_t st) {
+  const int64_t ldt = gr_cols(M);
+  hipLaunchKernelGGL(gr_transpose_kernel, dim3(unsigned(D / 64), unsigned(ldt / 64)), dim3(256), 0, st, g, r, grT, M, D,
+                     ldt);
+  return hipGetLastError();
+}
+
+// Fused path: s, then bf16(r g) transposed.
+hipError_t bwd_rowstat(const coda_bwd_args_t* a, uint16_t* grT, hipStream_t st) {
+  hipLaunchKernelGGL(rowstat_kernel<false>, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)a->dY,
+                     (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, a->s, grT, a->N, a->D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return gr_transpose((const uint16_t*)a->g, a->r, grT, a->M, a->D, st);
+}
+
+// Unfused baseline: s and bf16(r g) in row layout from one row kernel.
+hipError_t bwd_rowstat_rows(const coda_bwd_args_t* a, uint16_t* gr, hipStream_t st) {
+  hipLaunchKernelGGL(rowstat_kernel<true>, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)a->dY,
                      (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, a->s, gr, a->N, a->D);
   return hipGetLastError();
 }
@@ -1079,13 +1112,15 @@ hipError_t bwd_wgrad(const coda_bwd_args_t* a, const uint16_t* gr, hipStream_t s
   return gemm_plain(p, false, false, a->dW1, a->N, a->dW1_dtype == CODA_F32, st);
 }
 
-// The same GEMM, finishing dgamma from the partials Pg[rows, D] in its prologue.
-hipError_t bwd_wgrad_dgamma(const coda_bwd_args_t* a, const uint16_t* gr, const float* Pg, int64_t rows,
+// The fused path's weight gradient on the transposed bf16(r g): A(m=j, k=i) = grT[j, i] (k contiguous;
+// zero past M up to the K step), B(k=i, n) = dY[i, n] (n contiguous; rows past M read as 0), K = M.
+// Its prologue finishes dgamma from the partials Pg[rows, D].
+hipError_t bwd_wgrad_dgamma(const coda_bwd_args_t* a, const uint16_t* grT, const float* Pg, int64_t rows,
                             hipStream_t st) {
-  const GemmShape p{a->D, a->N, a->M, gr, a->D, a->dY, a->N};
+  const GemmShape p{a->D, a->N, a->M, grT, gr_cols(a->M), a->dY, a->N};
   if (a->dW1_dtype == CODA_F32)
-    return launch_gemm<false, false>(p, EpiStoreDgamma<true>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
-  return launch_gemm<false, false>(p, EpiStoreDgamma<false>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
+    return launch_gemm<true, false>(p, EpiStoreDgamma<true>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
+  return launch_gemm<true, false>(p, EpiStoreDgamma<false>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
 }
 
 hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, hipStream_t st) {
@@ -1240,8 +1275,9 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
     hipError_t e = gemm_plain(po, true, true, dO, F, false, st);
     if (e != hipSuccess) return CODA_ERR_HIP;
     hipLaunchKernelGGL(swiglu_bwd_rows_kernel, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)dO,
-                       (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, (uint16_t*)a->dY, a->s, gr, F, a->D);
+                       (const uint16_t*)a->y, (uint16_t*)a->dY, a->s, F);
     if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+    if ((e = gr_transpose((const uint16_t*)a->g, a->r, gr, a->M, a->D, st)) != hipSuccess) return CODA_ERR_HIP;
     const coda_bwd_args_t c{a->M, a->D, a->N, a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1,
                             a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
     if ((e = bwd_dgrad(&c, w.Pg, w.part, st)) != hipSuccess) return CODA_ERR_HIP;
@@ -1254,7 +1290,7 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
   uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, md));
   float* Pg = reinterpret_cast<float*>(ws_at(ws, 2 * md));
-  hipError_t e = bwd_rowstat(a, gr, st);
+  hipError_t e = bwd_rowstat_rows(a, gr, st);
   if (e != hipSuccess) return CODA_ERR_HIP;
   const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
   if ((e = gemm_plain(pd, true, true, G, a->D, false, st)) != hipSuccess) return CODA_ERR_HIP;
@@ -1295,9 +1331,9 @@ coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t 
   const GemmShape po{a->M, F, a->E, a->dOut, a->E, a->W2, a->E};
   hipError_t e = launch_gemm<true, true>(po, EpiSwigluBwd{(const uint16_t*)a->y, (uint16_t*)a->dY, Ps, a->M, F, pcols}, st);
   if (e != hipSuccess) return CODA_ERR_HIP;
-  hipLaunchKernelGGL(scombine_gr_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, Ps, (const uint16_t*)a->g, a->r, a->s,
-                     gr, pcols, a->D);
+  hipLaunchKernelGGL(scombine_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, Ps, a->s, pcols);
   if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+  if ((e = gr_transpose((const uint16_t*)a->g, a->r, gr, a->M, a->D, st)) != hipSuccess) return CODA_ERR_HIP;
   // the chain's backward on dY, with s and bf16(r g) already in place
   const coda_bwd_args_t c{a->M, a->D, a->N, a->dY, a->y, a->h, a->g, a->r, a->gamma, a->W1,
                           a->da, a->dgamma, a->dW1, a->s, a->da_dtype, a->dW1_dtype};
