@@ -36,9 +36,10 @@
  *     hipStream_t; NULL is the default stream) and the call returns at once.
  *     Calls on one stream with distinct outputs/workspaces are independent; the
  *     library keeps no global state.
- *   - Shapes: 1 <= M <= 2^24 (any value; the last row tile is masked); K0, D
- *     and N are multiples of 256 in [256, 2^20]. Anything else returns
- *     CODA_ERR_SHAPE.
+ *   - Shapes: 1 <= M <= 2^22 (any value; the last row tile is masked); K0, D
+ *     and N are multiples of 256 in [256, 2^20]; and every GEMM of the call has
+ *     at most 2^23 output tiles of 256 x 256 (its launch stays within 2^32
+ *     work-items). Anything else returns CODA_ERR_SHAPE.
  *   - eps must be finite and > 0.
  *   - Arguments are validated on the host before anything is launched; on any
  *     error nothing is enqueued and the status is returned. A failed launch

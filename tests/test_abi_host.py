@@ -164,8 +164,11 @@ def test_validate_fwd_ok_and_errors():
     for f in ("x", "W0", "z", "gamma", "W1", "h", "g", "r", "y"):
         assert vfwd(_fwd(**{f: None})) == L.CODA_ERR_NULL, f
         assert vfwd(_fwd(**{f: ctypes.c_void_p(A + 8)})) == L.CODA_ERR_ALIGN, f
-    for k, v in (("M", 0), ("M", -5), ("M", (1 << 24) + 1), ("K0", 128), ("D", 300), ("N", 0), ("N", 1 << 21)):
+    for k, v in (("M", 0), ("M", -5), ("M", (1 << 22) + 1), ("K0", 128), ("D", 300), ("N", 0), ("N", 1 << 21)):
         assert vfwd(_fwd(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
+    # every GEMM's launch stays within 2^32 work-items: 2^14 row tiles x 2^12 column tiles x 512 is too many
+    assert vfwd(_fwd(M=1 << 22, N=1 << 20)) == L.CODA_ERR_SHAPE
+    assert vfwd(_fwd(M=1 << 22, N=1 << 12)) == L.CODA_OK
     for eps in (0.0, -1e-5, float("nan"), float("inf")):
         assert vfwd(_fwd(eps=eps)) == L.CODA_ERR_ARG, eps
     assert vfwd(_fwd(y_dtype=7)) == L.CODA_ERR_ARG

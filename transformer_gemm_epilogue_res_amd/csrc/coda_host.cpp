@@ -15,6 +15,9 @@ bool dim_ok(int64_t v) { return v >= kDimQuantum && v <= kMaxDim && v % kDimQuan
 
 bool rows_ok(int64_t M) { return M >= 1 && M <= kMaxRows; }
 
+// A GEMM's grid (one 512-thread block per 256 x 256 output tile) fits a launch: at most 2^32 - 1 work-items.
+bool grid_ok(int64_t rows, int64_t cols) { return ceil_div(rows, kBM) * (cols / kBN) * kThreads <= 0xFFFFFFFFll; }
+
 bool dtype_ok(coda_dtype_t t) { return t == CODA_BF16 || t == CODA_F32; }
 
 // First failing pointer check over a list: NULL beats misalignment.
@@ -48,6 +51,7 @@ coda_status_t validate_fwd_common(const coda_fwd_args_t* a, bool need_g) {
   if (st != CODA_OK) return st;
   if (!need_g && a->g != nullptr && !aligned16(a->g)) return CODA_ERR_ALIGN;
   if (!rows_ok(a->M) || !dim_ok(a->K0) || !dim_ok(a->D) || !dim_ok(a->N)) return CODA_ERR_SHAPE;
+  if (!grid_ok(a->M, a->D) || !grid_ok(a->M, a->N)) return CODA_ERR_SHAPE;
   if (!(isfinite(a->eps) && a->eps > 0.0f)) return CODA_ERR_ARG;
   if (!dtype_ok(a->y_dtype)) return CODA_ERR_ARG;
   return CODA_OK;
@@ -59,6 +63,7 @@ coda_status_t validate_bwd_common(const coda_bwd_args_t* a) {
   coda_status_t st = check_ptrs(ps, 11);
   if (st != CODA_OK) return st;
   if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N)) return CODA_ERR_SHAPE;
+  if (!grid_ok(a->M, a->D) || !grid_ok(a->D, a->N)) return CODA_ERR_SHAPE;
   if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype)) return CODA_ERR_ARG;
   return CODA_OK;
 }
@@ -70,6 +75,8 @@ coda_status_t validate_bwd_swiglu_common(const coda_bwd_swiglu_args_t* a) {
   coda_status_t st = check_ptrs(ps, 15);
   if (st != CODA_OK) return st;
   if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 512) return CODA_ERR_SHAPE;
+  if (!grid_ok(a->M, a->D) || !grid_ok(a->D, a->N) || !grid_ok(a->M, a->N / 2) || !grid_ok(a->N / 2, a->E))
+    return CODA_ERR_SHAPE;
   if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype) || !dtype_ok(a->dW2_dtype)) return CODA_ERR_ARG;
   return CODA_OK;
 }
@@ -138,7 +145,7 @@ coda_status_t coda_validate_gemm(const coda_gemm_args_t* a) {
   const void* ps[] = {a->A, a->B, a->C};
   coda_status_t st = check_ptrs(ps, 3);
   if (st != CODA_OK) return st;
-  if (!rows_ok(a->M) || !dim_ok(a->N) || !dim_ok(a->K)) return CODA_ERR_SHAPE;
+  if (!rows_ok(a->M) || !dim_ok(a->N) || !dim_ok(a->K) || !grid_ok(a->M, a->N)) return CODA_ERR_SHAPE;
   if ((a->a_layout != CODA_ROW && a->a_layout != CODA_COL) ||
       (a->b_layout != CODA_ROW && a->b_layout != CODA_COL) || !dtype_ok(a->c_dtype))
     return CODA_ERR_ARG;
@@ -172,7 +179,7 @@ coda_status_t coda_validate_ce_fwd(const coda_ce_fwd_args_t* a, const void* ws, 
   const void* ps[] = {a->h, a->W, a->targets, a->lse, a->loss};
   coda_status_t st = check_ptrs(ps, 5);
   if (st != CODA_OK) return st;
-  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V)) return CODA_ERR_SHAPE;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V) || !grid_ok(a->M, a->V)) return CODA_ERR_SHAPE;
   return check_ws(ws, ws_bytes, ce_fwd_ws(a->M, a->V));
 }
 
@@ -182,6 +189,7 @@ coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a) {
   coda_status_t st = check_ptrs(ps, 8);
   if (st != CODA_OK) return st;
   if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V)) return CODA_ERR_SHAPE;
+  if (!grid_ok(a->M, a->V) || !grid_ok(a->M, a->D) || !grid_ok(a->V, a->D)) return CODA_ERR_SHAPE;
   if (!dtype_ok(a->dh_dtype) || !dtype_ok(a->dW_dtype)) return CODA_ERR_ARG;
   return CODA_OK;
 }
@@ -192,6 +200,7 @@ coda_status_t coda_validate_bwd_gemm0(const coda_bwd_gemm0_args_t* a) {
   coda_status_t st = check_ptrs(ps, 5);
   if (st != CODA_OK) return st;
   if (!rows_ok(a->M) || !dim_ok(a->K0) || !dim_ok(a->D)) return CODA_ERR_SHAPE;
+  if (!grid_ok(a->M, a->K0) || !grid_ok(a->K0, a->D)) return CODA_ERR_SHAPE;
   if (!dtype_ok(a->dx_dtype) || !dtype_ok(a->dW0_dtype)) return CODA_ERR_ARG;
   return CODA_OK;
 }

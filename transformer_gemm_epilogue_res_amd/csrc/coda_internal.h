@@ -18,9 +18,11 @@ constexpr int kThreads = 512;
 
 // K0, D and N must be multiples of this.
 constexpr int64_t kDimQuantum = 256;
-// Largest accepted K0 / D / N and M (keeps every per-tile buffer offset < 2^31).
+// Largest accepted K0 / D / N and M (keeps every per-tile buffer offset < 2^31 and a
+// one-block-per-row launch of 512-thread blocks within 2^32 work-items); each GEMM's
+// grid is also checked against that limit.
 constexpr int64_t kMaxDim = int64_t(1) << 20;
-constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxRows = int64_t(1) << 22;
 
 // Row block of the unfused RMSNorm-backward kernel (its dgamma partial granularity).
 constexpr int kUnfusedBwdRows = 32;
