@@ -379,14 +379,19 @@ def main():
                "dW": torch.empty(V, D, dtype=bf, device=dev)}
         CF = L.bind_ce_fwd(hl, Wl, tg, cfo, L.workspace(L.CODA_OP_CE_FWD, M, D, V, dev))
         CB = L.bind_ce_bwd(hl, Wl, tg, cfo["lse"], dloss, cbo)
+        # the unfused baseline stores the fp32 logits [M, V] in its workspace
+        uws = None if args.no_unfused else L.workspace(L.CODA_OP_UNFUSED_CE_FWD, M, D, V, dev)
         t = {}
-        for name, obj in (("fwd", CF), ("bwd", CB)):
+        runs = [("fwd", CF, None), ("bwd", CB, None)]
+        if uws is not None:
+            runs += [("ufwd", CF, uws), ("ubwd", CB, uws)]
+        for name, obj, w in runs:
             for _ in range(2):
-                obj.run(sp)
+                obj.run(sp, unfused_ws=w)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(args.steps):
-                obj.run(sp)
+                obj.run(sp, unfused_ws=w)
             b.record(stream)
             torch.cuda.synchronize()
             t[name] = a.elapsed_time(b) / args.steps
@@ -396,7 +401,13 @@ def main():
               "tflops": round((ce_f + ce_b) / (t["fwd"] + t["bwd"]) / 1e9, 1)}
         ce["pct_peak"] = round(100 * ce["tflops"] / PEAK_BF16_TFLOPS, 2)
         log(f"[bench] cross-entropy LM head: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {ce['tflops']} TFLOP/s")
-        del hl, Wl, tg, dloss, cfo, cbo, CF, CB
+        if uws is not None:
+            ce["unfused"] = {"fwd_ms": round(t["ufwd"], 4), "bwd_ms": round(t["ubwd"], 4),
+                             "fused_fwd_speedup": round(t["ufwd"] / t["fwd"], 3),
+                             "fused_bwd_speedup": round(t["ubwd"] / t["bwd"], 3)}
+            log(f"[bench] unfused cross-entropy (stored fp32 logits): fwd {t['ufwd']:.3f} ms, "
+                f"bwd {t['ubwd']:.3f} ms")
+        del hl, Wl, tg, dloss, cfo, cbo, CF, CB, uws
 
     unfused = None
     if not args.no_unfused:

@@ -81,7 +81,9 @@ typedef enum {
   CODA_OP_CE_FWD = 6,       /* coda_ce_fwd (pass the vocabulary size V as N) */
   CODA_OP_CE_BWD = 7,       /* coda_ce_bwd (none) */
   CODA_OP_UNFUSED_FWD_SWIGLU = 8, /* coda_unfused_ref(CODA_OP_FWD_SWIGLU) */
-  CODA_OP_UNFUSED_BWD_SWIGLU = 9  /* coda_unfused_ref(CODA_OP_BWD_SWIGLU) */
+  CODA_OP_UNFUSED_BWD_SWIGLU = 9, /* coda_unfused_ref(CODA_OP_BWD_SWIGLU) */
+  CODA_OP_UNFUSED_CE_FWD = 10,    /* coda_unfused_ref(CODA_OP_CE_FWD) (V as N) */
+  CODA_OP_UNFUSED_CE_BWD = 11     /* coda_unfused_ref(CODA_OP_CE_BWD) (V as N) */
 } coda_op_t;
 
 /* Forward arguments.
@@ -298,8 +300,8 @@ coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const vo
 coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_ce_fwd(const coda_ce_fwd_args_t* a, const void* ws, size_t ws_bytes);
 coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a);
-/* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD, CODA_OP_BWD, CODA_OP_FWD_SWIGLU or
- * CODA_OP_BWD_SWIGLU). */
+/* Checks of coda_unfused_ref's arguments (op = CODA_OP_FWD, CODA_OP_BWD, CODA_OP_FWD_SWIGLU,
+ * CODA_OP_BWD_SWIGLU, CODA_OP_CE_FWD or CODA_OP_CE_BWD). */
 coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
 
 /* Fused forward: GEMM0 + epilogue (residual, h, g, sum-of-squares partials) ->
@@ -345,7 +347,11 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
  *   op = CODA_OP_BWD_SWIGLU, args = coda_bwd_swiglu_args_t*: dO = dOut@W2^T
  *     stored as bf16 in the workspace -> a row kernel (dY from dO and the saved
  *     y, s from the fp32 dY, bf16(r*g)) -> the fused chain backward's dgrad and
- *     dW1 GEMMs -> dW2. Only the SwiGLU step is unfused. */
+ *     dW1 GEMMs -> dW2. Only the SwiGLU step is unfused.
+ *   op = CODA_OP_CE_FWD, args = coda_ce_fwd_args_t*: the logits h@W^T stored as
+ *     fp32 in the workspace ([M, V]) -> a row kernel for lse and loss.
+ *   op = CODA_OP_CE_BWD, args = coda_ce_bwd_args_t*: the logits stored as fp32
+ *     in the workspace -> a row kernel for dlogits -> the same dh and dW GEMMs. */
 coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream);
 
 /* SwiGLU forward and backward (see coda_fwd_swiglu_args_t, coda_bwd_swiglu_args_t). */

@@ -120,6 +120,10 @@ def test_workspace_sizes():
     assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, V) == a256(M * (V // 64) * 8) + a256(M * 4)
     assert L.workspace_bytes(L.CODA_OP_CE_FWD, M, D, 1000) == 0
     assert L.workspace_bytes(L.CODA_OP_CE_BWD, M, D, V) == 0
+    # the unfused cross-entropy stores the fp32 logits [M, V]
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_CE_FWD, M, D, V) == a256(M * V * 4)
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_CE_BWD, M, D, V) == a256(M * V * 4)
+    assert L.workspace_bytes(L.CODA_OP_UNFUSED_CE_FWD, M, D, 1000) == 0
 
 
 def dgrad_split(M, D, N):
@@ -306,6 +310,18 @@ def test_validate_cross_entropy():
         setattr(c, k, v)
         assert lib.coda_validate_ce_bwd(ctypes.byref(c)) == want, k
         assert lib.coda_ce_bwd(ctypes.byref(c), None) == want, k
+    # the unfused baseline takes the same structs and needs the [M, V] fp32 logits workspace
+    un = L.workspace_bytes(L.CODA_OP_UNFUSED_CE_FWD, 300, 256, 1024)
+    for op, args in ((L.CODA_OP_CE_FWD, f), (L.CODA_OP_CE_BWD, b)):
+        assert lib.coda_validate_unfused(op, ctypes.byref(args), WS, un) == L.CODA_OK
+        assert lib.coda_validate_unfused(op, ctypes.byref(args), WS, un - 1) == L.CODA_ERR_WORKSPACE
+        assert lib.coda_validate_unfused(op, ctypes.byref(args), None, un) == L.CODA_ERR_WORKSPACE
+    g = L.CeFwdArgs.from_buffer_copy(f)
+    g.lse = None
+    assert lib.coda_unfused_ref(L.CODA_OP_CE_FWD, ctypes.byref(g), WS, un, None) == L.CODA_ERR_NULL
+    c = L.CeBwdArgs.from_buffer_copy(b)
+    c.V = 1000
+    assert lib.coda_unfused_ref(L.CODA_OP_CE_BWD, ctypes.byref(c), WS, un, None) == L.CODA_ERR_SHAPE
 
 
 def test_entry_points_reject_without_launching():

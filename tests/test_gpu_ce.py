@@ -6,6 +6,10 @@ of exact bf16 products and never rounded); ignored rows have loss exactly 0.
 Backward, fed the oracle's lse: dlogits faithfully rounded to bf16 (within one
 ulp, +1e-4 rms); dh and dW within 1e-4 rms plus the first-order effect of that
 rounding of dlogits before the two products.
+
+The unfused baseline (coda_unfused_ref: fp32 logits stored, then row kernels) is
+held to the same bounds; its logits come from the same mainloop, so its backward
+matches the fused one bit for bit.
 """
 import numpy as np
 import pytest
@@ -109,6 +113,14 @@ def test_ce_small_full(name):
     assert torch.equal(mt.rne_bf16(b32["dh"]).view(torch.int16), b16["dh"].view(torch.int16))
     assert torch.equal(mt.rne_bf16(b32["dW"]).view(torch.int16), b16["dW"].view(torch.int16))
     check_bwd(b32, host, lse_ref)
+    # the unfused baseline
+    fu = L.ce_fwd(d["h"], d["W"], d["targets"], unfused=True)
+    bu = L.ce_bwd(d["h"], d["W"], d["targets"], lse_ref.to(DEV), d["dloss"], dh_dtype=torch.float32,
+                  dW_dtype=torch.float32, unfused=True)
+    torch.cuda.synchronize()
+    check_fwd(fu, ref, host["targets"])
+    for k in ("dlogits", "dh", "dW"):
+        assert torch.equal(bu[k], b32[k]), k
 
 
 def test_ce_forward_then_backward_on_device():
@@ -124,20 +136,32 @@ def test_ce_forward_then_backward_on_device():
     check_bwd(b, host, torch.from_numpy(ref["lse"]).to(torch.float32))
 
 
-def test_ce_extreme_logits():
-    """Logits of size ~60 (a peaked softmax) and an all-equal row: the tile statistics keep exp in range."""
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_ce_extreme_logits(unfused):
+    """Logits of size ~60 (a peaked softmax) and an all-equal row: the tile statistics keep exp in range.
+    The ignored row 1 has logits above 88 (exp overflows fp32 there): its gradient is still exactly 0."""
     c = dict(M=32, D=256, V=768)
-    announce(f"coda_ce_fwd extreme logits {c}")
+    announce(f"coda_ce_fwd / coda_ce_bwd extreme logits {c} unfused={unfused}")
     host = case_inputs(c, seed=2)
     host["W"] = (host["W"].float() * 30).to(torch.bfloat16)   # logits std ~60
     host["h"][5] = 0                                          # all logits 0: lse = log V, loss = log V
+    assert host["targets"][1] == -100
+    assert (mt.f64(host["h"][1]) @ mt.f64(host["W"]).T).max() > 89.0
     d = {k: v.to(DEV) for k, v in host.items()}
-    f = L.ce_fwd(d["h"], d["W"], d["targets"])
+    f = L.ce_fwd(d["h"], d["W"], d["targets"], unfused=unfused)
     torch.cuda.synchronize()
     ref = orc.lm_head_cross_entropy(host["h"], host["W"], host["targets"])
     assert torch.all(torch.isfinite(f["lse"])) and torch.all(torch.isfinite(f["loss"]))
     assert abs(f["lse"][5].item() - np.log(768)) < 1e-5
     check_fwd(f, ref, host["targets"])
+    lse_ref = torch.from_numpy(ref["lse"]).to(torch.float32)
+    b = L.ce_bwd(d["h"], d["W"], d["targets"], lse_ref.to(DEV), d["dloss"], dh_dtype=torch.float32,
+                 dW_dtype=torch.float32, unfused=unfused)
+    torch.cuda.synchronize()
+    for k in ("dlogits", "dh", "dW"):
+        assert torch.all(torch.isfinite(b[k].float())), k
+    assert torch.all(b["dlogits"][1] == 0)
+    check_bwd(b, host, lse_ref)
 
 
 def test_ce_all_rows_ignored():
@@ -149,15 +173,17 @@ def test_ce_all_rows_ignored():
     host["targets"][:] = -100
     host["targets"][::3] = c["V"]           # past the vocabulary: also ignored
     d = {k: v.to(DEV) for k, v in host.items()}
-    f = L.ce_fwd(d["h"], d["W"], d["targets"])
-    b = L.ce_bwd(d["h"], d["W"], d["targets"], f["lse"], d["dloss"], dh_dtype=torch.float32, dW_dtype=torch.float32)
-    torch.cuda.synchronize()
     ref = orc.lm_head_cross_entropy(host["h"], host["W"], host["targets"])
     assert not ref["valid"].any()
-    assert torch.all(f["loss"] == 0)
-    assert mt.normwise(f["lse"], ref["lse"]) <= TOL
-    for k in ("dlogits", "dh", "dW"):
-        assert torch.all(b[k] == 0), k
+    for unfused in (False, True):
+        f = L.ce_fwd(d["h"], d["W"], d["targets"], unfused=unfused)
+        b = L.ce_bwd(d["h"], d["W"], d["targets"], f["lse"], d["dloss"], dh_dtype=torch.float32,
+                     dW_dtype=torch.float32, unfused=unfused)
+        torch.cuda.synchronize()
+        assert torch.all(f["loss"] == 0)
+        assert mt.normwise(f["lse"], ref["lse"]) <= TOL
+        for k in ("dlogits", "dh", "dW"):
+            assert torch.all(b[k] == 0), (k, unfused)
 
 
 @pytest.mark.slow

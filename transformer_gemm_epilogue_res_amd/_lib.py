@@ -21,7 +21,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "coda.h")
 CODA_OK, CODA_ERR_NULL, CODA_ERR_SHAPE, CODA_ERR_ALIGN, CODA_ERR_WORKSPACE, CODA_ERR_ARG, CODA_ERR_HIP = range(7)
 CODA_BF16, CODA_F32 = 0, 1
 (CODA_OP_FWD, CODA_OP_BWD, CODA_OP_UNFUSED_FWD, CODA_OP_UNFUSED_BWD, CODA_OP_FWD_SWIGLU, CODA_OP_BWD_SWIGLU,
- CODA_OP_CE_FWD, CODA_OP_CE_BWD, CODA_OP_UNFUSED_FWD_SWIGLU, CODA_OP_UNFUSED_BWD_SWIGLU) = range(10)
+ CODA_OP_CE_FWD, CODA_OP_CE_BWD, CODA_OP_UNFUSED_FWD_SWIGLU, CODA_OP_UNFUSED_BWD_SWIGLU,
+ CODA_OP_UNFUSED_CE_FWD, CODA_OP_UNFUSED_CE_BWD) = range(12)
 CODA_ROW, CODA_COL = 0, 1
 CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 3
 FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
@@ -375,9 +376,10 @@ def _ce_fwd_args(h, W, targets, lse, loss):
     return CeFwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(loss))
 
 
-def ce_fwd(h, W, targets, ws=None, out=None):
+def ce_fwd(h, W, targets, ws=None, out=None, unfused=False):
     """Cross-entropy of the LM-head logits h @ W^T against targets (int64; outside [0, V) = ignored).
-    Returns dict(lse, loss), both [M] fp32."""
+    Returns dict(lse, loss), both [M] fp32. unfused: the fp32 logits stored, then a row
+    kernel (coda_unfused_ref)."""
     M, D = h.shape
     V = W.shape[0]
     dev = h.device
@@ -386,8 +388,12 @@ def ce_fwd(h, W, targets, ws=None, out=None):
                "loss": torch.empty(M, dtype=torch.float32, device=dev)}
     a = _ce_fwd_args(h, W, targets, out["lse"], out["loss"])
     if ws is None:
-        ws = workspace(CODA_OP_CE_FWD, M, D, V, dev)
-    _check(lib().coda_ce_fwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_ce_fwd")
+        ws = workspace(CODA_OP_UNFUSED_CE_FWD if unfused else CODA_OP_CE_FWD, M, D, V, dev)
+    if unfused:
+        _check(lib().coda_unfused_ref(CODA_OP_CE_FWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+               "coda_unfused_ref(ce_fwd)")
+    else:
+        _check(lib().coda_ce_fwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_ce_fwd")
     return out
 
 
@@ -404,8 +410,10 @@ def _ce_bwd_args(h, W, targets, lse, dloss, out):
                      _ptr(out["dh"]), _ptr(out["dW"]), _dt(out["dh"].dtype), _dt(out["dW"].dtype))
 
 
-def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bfloat16, out=None):
-    """Backward of sum_i dloss_i loss_i: dict(dlogits [M,V] bf16, dh [M,D], dW [V,D])."""
+def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bfloat16, out=None, unfused=False,
+           ws=None):
+    """Backward of sum_i dloss_i loss_i: dict(dlogits [M,V] bf16, dh [M,D], dW [V,D]).
+    unfused: the fp32 logits stored in a workspace, then a dlogits row kernel."""
     M, D = h.shape
     V = W.shape[0]
     dev = h.device
@@ -414,7 +422,13 @@ def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bf
                "dh": torch.empty(M, D, dtype=dh_dtype, device=dev),
                "dW": torch.empty(V, D, dtype=dW_dtype, device=dev)}
     a = _ce_bwd_args(h, W, targets, lse, dloss, out)
-    _check(lib().coda_ce_bwd(ctypes.byref(a), _stream(dev)), "coda_ce_bwd")
+    if unfused:
+        if ws is None:
+            ws = workspace(CODA_OP_UNFUSED_CE_BWD, M, D, V, dev)
+        _check(lib().coda_unfused_ref(CODA_OP_CE_BWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+               "coda_unfused_ref(ce_bwd)")
+    else:
+        _check(lib().coda_ce_bwd(ctypes.byref(a), _stream(dev)), "coda_ce_bwd")
     return out
 
 
@@ -424,8 +438,13 @@ class BoundCe:
     def __init__(self, kind, args, ws, keep):
         self.kind, self.args, self.ws, self._keep = kind, args, ws, keep
 
-    def run(self, stream):
-        if self.kind == "fwd":
+    def run(self, stream, unfused_ws=None):
+        """unfused_ws: run coda_unfused_ref (stored fp32 logits) in that workspace instead."""
+        if unfused_ws is not None:
+            op = CODA_OP_CE_FWD if self.kind == "fwd" else CODA_OP_CE_BWD
+            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(unfused_ws), unfused_ws.numel(), stream),
+                   f"coda_unfused_ref(ce_{self.kind})")
+        elif self.kind == "fwd":
             _check(lib().coda_ce_fwd(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), "coda_ce_fwd")
         else:
             _check(lib().coda_ce_bwd(ctypes.byref(self.args), stream), "coda_ce_bwd")

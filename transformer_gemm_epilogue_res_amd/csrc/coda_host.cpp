@@ -68,6 +68,15 @@ coda_status_t validate_bwd_common(const coda_bwd_args_t* a) {
   return CODA_OK;
 }
 
+coda_status_t validate_ce_fwd_common(const coda_ce_fwd_args_t* a) {
+  if (a == nullptr) return CODA_ERR_NULL;
+  const void* ps[] = {a->h, a->W, a->targets, a->lse, a->loss};
+  coda_status_t st = check_ptrs(ps, 5);
+  if (st != CODA_OK) return st;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V) || !grid_ok(a->M, a->V)) return CODA_ERR_SHAPE;
+  return CODA_OK;
+}
+
 coda_status_t validate_bwd_swiglu_common(const coda_bwd_swiglu_args_t* a) {
   if (a == nullptr) return CODA_ERR_NULL;
   const void* ps[] = {a->dOut, a->W2, a->o, a->y, a->h, a->g, a->r, a->gamma, a->W1, a->dY, a->da, a->dgamma,
@@ -98,6 +107,8 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_CE_BWD: return 0;
     case CODA_OP_UNFUSED_FWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? fwd_ws(M, D) : 0;
     case CODA_OP_UNFUSED_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? unfused_bwd_swiglu_ws(M, D, N) : 0;
+    case CODA_OP_UNFUSED_CE_FWD:
+    case CODA_OP_UNFUSED_CE_BWD: return dim_ok(N) ? unfused_ce_ws(M, N) : 0;
   }
   return 0;
 }
@@ -137,6 +148,18 @@ coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* 
     if (st != CODA_OK) return st;
     return check_ws(ws, ws_bytes, unfused_bwd_swiglu_ws(a->M, a->D, a->N));
   }
+  if (op == CODA_OP_CE_FWD) {
+    const coda_ce_fwd_args_t* a = static_cast<const coda_ce_fwd_args_t*>(args);
+    coda_status_t st = validate_ce_fwd_common(a);
+    if (st != CODA_OK) return st;
+    return check_ws(ws, ws_bytes, unfused_ce_ws(a->M, a->V));
+  }
+  if (op == CODA_OP_CE_BWD) {
+    const coda_ce_bwd_args_t* a = static_cast<const coda_ce_bwd_args_t*>(args);
+    coda_status_t st = coda_validate_ce_bwd(a);
+    if (st != CODA_OK) return st;
+    return check_ws(ws, ws_bytes, unfused_ce_ws(a->M, a->V));
+  }
   return CODA_ERR_ARG;
 }
 
@@ -175,11 +198,8 @@ coda_status_t coda_validate_bwd_swiglu(const coda_bwd_swiglu_args_t* a, const vo
 }
 
 coda_status_t coda_validate_ce_fwd(const coda_ce_fwd_args_t* a, const void* ws, size_t ws_bytes) {
-  if (a == nullptr) return CODA_ERR_NULL;
-  const void* ps[] = {a->h, a->W, a->targets, a->lse, a->loss};
-  coda_status_t st = check_ptrs(ps, 5);
+  coda_status_t st = validate_ce_fwd_common(a);
   if (st != CODA_OK) return st;
-  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V) || !grid_ok(a->M, a->V)) return CODA_ERR_SHAPE;
   return check_ws(ws, ws_bytes, ce_fwd_ws(a->M, a->V));
 }
 

@@ -40,6 +40,8 @@ inline int64_t ce_stat_cols(int64_t V) { return V / kWaveTileN; }
 inline size_t ce_fwd_ws(int64_t M, int64_t V) {
   return align256(size_t(M) * size_t(ce_stat_cols(V)) * 8) + align256(size_t(M) * 4);
 }
+// Unfused cross-entropy workspace: the fp32 logits [M, V].
+inline size_t unfused_ce_ws(int64_t M, int64_t V) { return align256(size_t(M) * size_t(V) * 4); }
 // Row count of the fused backward's dgamma partials Pg[ceil(M / kWaveTileM), D].
 inline int64_t dgamma_rows(int64_t M) { return ceil_div(M, kWaveTileM); }
 

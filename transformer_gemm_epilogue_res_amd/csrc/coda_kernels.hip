@@ -535,7 +535,9 @@ struct EpiCeBwd {
       const int64_t i = mb + 16 * tm + li;
       const int64_t t = i < M ? targets[i] : -1;
       const bool ok = i < M && ce_valid(t, V);
-      ls[tm] = ok ? lse[i] : 0.f;
+      // an ignored row takes lse = +inf, so exp() is 0 there rather than overflowing to inf
+      // (0 * inf would make its zero gradient NaN)
+      ls[tm] = ok ? lse[i] : INFINITY;
       dl[tm] = ok ? dloss[i] : 0.f;
       const int64_t c = t - nb - 4 * lg;  // target column relative to the lane's first column of tile 0
       tc[tm] = (c >= 0 && c < kWaveTileN) ? int(c) : -1;
@@ -849,6 +851,52 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2* Pml, cons
     const int64_t t = targets[i];
     lse[i] = ls;
     loss[i] = ce_valid(t, V) ? ls - tgt[i] : 0.f;
+  }
+}
+
+// Unfused cross-entropy rows, one 256-thread block per row of the stored fp32 logits.
+// Forward: each thread keeps a running (max, sum exp) over its columns in one pass,
+// then the block combines them; lse_i = m + log l, loss_i = lse_i - logit[i, t_i], 0
+// for an ignored row.
+__global__ __launch_bounds__(256) void ce_rows_fwd_kernel(const float* logits, const int64_t* targets, float* lse,
+                                                          float* loss, int64_t V) {
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const float4* lv = reinterpret_cast<const float4*>(logits + i * V);
+  float m = -INFINITY, l = 0.f;
+  for (int64_t v = threadIdx.x; v < V / 4; v += 256) {
+    const float4 x = lv[v];
+    const float mn = fmaxf(m, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+    l = l * expf(m - mn) + ((expf(x.x - mn) + expf(x.y - mn)) + (expf(x.z - mn) + expf(x.w - mn)));
+    m = mn;
+  }
+  const float mb = block_max256(m, red);
+  const float lb = block_sum256(m == -INFINITY ? 0.f : l * expf(m - mb), red);
+  if (threadIdx.x == 0) {
+    const float ls = mb + logf(lb);
+    const int64_t t = targets[i];
+    lse[i] = ls;
+    loss[i] = ce_valid(t, V) ? ls - logits[i * V + t] : 0.f;
+  }
+}
+
+// Backward: dlogits = dloss_i (exp(logit - lse_i) - [v = t_i]) stored bf16, 0 on an ignored row.
+__global__ __launch_bounds__(256) void ce_rows_bwd_kernel(const float* logits, const int64_t* targets,
+                                                          const float* lse, const float* dloss, uint16_t* dlogits,
+                                                          int64_t V) {
+  const int64_t i = blockIdx.x;
+  const int64_t t = targets[i];
+  const bool ok = ce_valid(t, V);
+  const float ls = ok ? lse[i] : INFINITY, dl = ok ? dloss[i] : 0.f;
+  const float4* lv = reinterpret_cast<const float4*>(logits + i * V);
+  uint2* dv = reinterpret_cast<uint2*>(dlogits + i * V);
+  for (int64_t v = threadIdx.x; v < V / 4; v += 256) {
+    const float4 x = lv[v];
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    float d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = dl * (expf(xs[e] - ls) - (4 * v + e == t ? 1.0f : 0.0f));
+    dv[v] = pack4_bf16(d[0], d[1], d[2], d[3]);
   }
 }
 
@@ -1168,6 +1216,17 @@ BwdWorkspace bwd_workspace(void* ws, int64_t M, int64_t D, int64_t N) {
           reinterpret_cast<float*>(ws_at(ws, bwd_ws_part(M, D, N))), bwd_pg_rows(M, D, N)};
 }
 
+// dh and dW from the bf16 dlogits (shared by the fused and the unfused backward).
+hipError_t ce_bwd_products(const coda_ce_bwd_args_t* a, hipStream_t st) {
+  // dh [M, D] = dlogits @ W: A = dlogits [M, V] (k contiguous), B(k=v, d) = W[v, d] (n contiguous)
+  const GemmShape pd{a->M, a->D, a->V, a->dlogits, a->V, a->W, a->D};
+  hipError_t e = gemm_plain(pd, true, false, a->dh, a->D, a->dh_dtype == CODA_F32, st);
+  if (e != hipSuccess) return e;
+  // dW [V, D] = dlogits^T @ h: A(m=v, k=i) = dlogits[i, v] (m contiguous), B(k=i, d) = h[i, d] (n contiguous), K = M
+  const GemmShape pw{a->V, a->D, a->M, a->dlogits, a->V, a->h, a->D};
+  return gemm_plain(pw, false, false, a->dW, a->D, a->dW_dtype == CODA_F32, st);
+}
+
 }  // namespace coda
 
 using namespace coda;
@@ -1285,6 +1344,28 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
     const GemmShape pw{F, a->E, a->M, a->o, F, a->dOut, a->E};
     return to_status(gemm_plain(pw, false, false, a->dW2, a->E, a->dW2_dtype == CODA_F32, st));
   }
+  if (op == CODA_OP_CE_FWD || op == CODA_OP_CE_BWD) {
+    // the fp32 logits h @ W^T stored in the workspace, then a row kernel
+    const coda_ce_fwd_args_t* f = static_cast<const coda_ce_fwd_args_t*>(args);
+    const coda_ce_bwd_args_t* b = static_cast<const coda_ce_bwd_args_t*>(args);
+    const int64_t M = op == CODA_OP_CE_FWD ? f->M : b->M, D = op == CODA_OP_CE_FWD ? f->D : b->D;
+    const int64_t V = op == CODA_OP_CE_FWD ? f->V : b->V;
+    const void* h = op == CODA_OP_CE_FWD ? f->h : b->h;
+    const void* W = op == CODA_OP_CE_FWD ? f->W : b->W;
+    float* logits = reinterpret_cast<float*>(ws);
+    const GemmShape p{M, V, D, h, D, W, D};
+    hipError_t e = gemm_plain(p, true, true, logits, V, true, st);
+    if (e != hipSuccess) return CODA_ERR_HIP;
+    if (op == CODA_OP_CE_FWD) {
+      hipLaunchKernelGGL(ce_rows_fwd_kernel, dim3(unsigned(M)), dim3(256), 0, st, (const float*)logits, f->targets,
+                         f->lse, f->loss, V);
+      return to_status(hipGetLastError());
+    }
+    hipLaunchKernelGGL(ce_rows_bwd_kernel, dim3(unsigned(M)), dim3(256), 0, st, (const float*)logits, b->targets,
+                       b->lse, b->dloss, (uint16_t*)b->dlogits, V);
+    if ((e = hipGetLastError()) != hipSuccess) return CODA_ERR_HIP;
+    return to_status(ce_bwd_products(b, st));
+  }
   const coda_bwd_args_t* a = static_cast<const coda_bwd_args_t*>(args);
   const size_t md = align256(size_t(a->M) * size_t(a->D) * 2);
   uint16_t* gr = reinterpret_cast<uint16_t*>(ws);
@@ -1369,12 +1450,7 @@ coda_status_t coda_ce_bwd(const coda_ce_bwd_args_t* a, void* stream) {
   hipError_t e = launch_gemm<true, true>(
       p, EpiCeBwd{a->targets, a->lse, a->dloss, static_cast<uint16_t*>(a->dlogits), a->M, a->V}, st);
   if (e != hipSuccess) return CODA_ERR_HIP;
-  // dh [M, D] = dlogits @ W: A = dlogits [M, V] (k contiguous), B(k=v, d) = W[v, d] (n contiguous)
-  const GemmShape pd{a->M, a->D, a->V, a->dlogits, a->V, a->W, a->D};
-  if ((e = gemm_plain(pd, true, false, a->dh, a->D, a->dh_dtype == CODA_F32, st)) != hipSuccess) return CODA_ERR_HIP;
-  // dW [V, D] = dlogits^T @ h: A(m=v, k=i) = dlogits[i, v] (m contiguous), B(k=i, d) = h[i, d] (n contiguous), K = M
-  const GemmShape pw{a->V, a->D, a->M, a->dlogits, a->V, a->h, a->D};
-  return to_status(gemm_plain(pw, false, false, a->dW, a->D, a->dW_dtype == CODA_F32, st));
+  return to_status(ce_bwd_products(a, st));
 }
 
 coda_status_t coda_bwd_gemm0(const coda_bwd_gemm0_args_t* a, void* stream) {
