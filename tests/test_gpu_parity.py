@@ -195,9 +195,10 @@ def check_bwd(o32, o16, host, rows=None, jcols=None, ncols=None, unfused=False):
 
 
 BWD_SMALL = {
-    "tiny": dict(M=64, K0=256, D=256, N=512),
+    "tiny": dict(M=64, K0=256, D=256, N=512),       # dW1 contracts over one K step
     "ragged": dict(M=300, K0=256, D=512, N=768),
     "one_row": dict(M=1, K0=256, D=256, N=256),
+    "two_k_steps": dict(M=100, K0=256, D=256, N=512),  # dW1 contracts over two K steps (rows padded to 128)
 }
 
 

@@ -108,6 +108,25 @@ struct StageBf16 {
       }
     }
   }
+  // fill()'s staged layout written by LDS DMA: sixteen 1 KB instructions, eight rows each;
+  // lane L fills byte slot L % 8 of row L / 8 with global chunk (L % 8) ^ (L / 8). Instruction
+  // q gets a descriptor based at row mb + 8 q, so the per-lane offset is the same for all q
+  // (and the range check, which covers the lane offset, is exact): rows past M read 0.
+  // Completes on vmcnt (wait_vm0 before get()).
+  __device__ __forceinline__ void fill_dma(const uint16_t* src, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
+    const int rl = lane >> 3, c = (lane & 7) ^ rl;
+    const uint32_t voff = uint32_t((rl * ldc + 8 * c) * 2);
+    const uint16_t* p = src + mb * ldc + nb;
+    int64_t bytes = (M - mb) * ldc * 2 - nb * 2;
+    lds_char_t* dst = base;
+#pragma unroll 1  // one descriptor live at a time (the loop runs inside the mainloop's last step)
+    for (int q = 0; q < kWaveTileM / 8; ++q) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p, bytes), (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+      p += 8 * ldc;
+      bytes -= 16 * ldc;
+      dst += 1024;
+    }
+  }
   // Sixteen bytes (chunk `chunk` of staged row `row`).
   __device__ __forceinline__ u32x4_t get16(int row, int chunk) const {
     return *reinterpret_cast<const LDS_AS u32x4_t*>(base + row * 128 + ((chunk ^ (row & 7)) << 4));
@@ -122,6 +141,21 @@ struct StageBf16 {
     return make_uint2(p.x, p.y);
   }
 };
+
+// LDS DMA of a vector: the first 256 N bytes at src (0 at or past `bytes`) to dst (wave-uniform),
+// 4 bytes per lane and instruction (the bounds check is then exact to the element).
+template <int N>
+__device__ __forceinline__ void dma_vec(lds_char_t* dst, const void* src, int64_t bytes, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
+#pragma unroll
+  for (int q = 0; q < N; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + q * 256), 4, uint32_t(q * 256 + lane * 4), 0, 0, 0);
+}
+__device__ __forceinline__ float lds_f32(const lds_char_t* p) { return *reinterpret_cast<const LDS_AS float*>(p); }
+__device__ __forceinline__ uint2 lds_u2(const lds_char_t* p) {
+  const u32x2_t v = *reinterpret_cast<const LDS_AS u32x2_t*>(p);
+  return make_uint2(v.x, v.y);
+}
 
 // out[rows of tile tm, columns of tile tn] for this lane, fp32 (16 bytes per lane).
 __device__ __forceinline__ void store_f32(float* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M, int lane,
@@ -227,16 +261,20 @@ struct EpiResidualSsq {
   uint16_t* g;
   float* P;
   int64_t M, D, pcols;
+  // during the last K step: the z block into the staging area, the wave's 64 gamma values into aux
+  __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int64_t nb, int lane) const {
+    StageBf16{stage, lane}.fill_dma(z, D, mb, nb, M);
+    dma_vec<1>(aux, gamma + nb, (D - nb) * 2, lane);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t* stage) const {
+                                             lds_char_t* stage, lds_char_t* aux) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
+    wait_vm0();  // early()'s DMA
     float gam[kTN][4];
 #pragma unroll
-    for (int tn = 0; tn < kTN; ++tn) unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + nb + 16 * tn + lj), gam[tn]);
-    // z through the staging area (whole 128-byte rows per load), then h = acc + z in place and
-    // the row sums of squares
+    for (int tn = 0; tn < kTN; ++tn) unpack4_bf16(lds_u2(aux + (16 * tn + lj) * 2), gam[tn]);
+    // h = acc + z (z staged by early()) in place, and the row sums of squares
     const StageBf16 zs{stage, lane};
-    zs.fill(z, D, mb, nb, M);
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
@@ -273,15 +311,17 @@ struct EpiRowScale {
   const float* r;
   void* y;
   int64_t M, N;
+  // during the last K step: the wave's 128 row scales into aux (0 past M)
+  __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
+    dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t* stage) const {
+                                             lds_char_t* stage, lds_char_t* aux) const {
     const int li = lane & 15;
+    wait_vm0();
     float rr[kTM];
 #pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      rr[tm] = i < M ? r[i] : 0.f;
-    }
+    for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
     store_block<F32>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
       f32x4_t v = acc[tm][tn];
 #pragma unroll
@@ -331,15 +371,16 @@ struct EpiRowScaleSwiglu {
   void* y;
   void* o;
   int64_t M, N;  // o has N / 2 columns
+  __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
+    dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t* stage) const {
+                                             lds_char_t* stage, lds_char_t* aux) const {
     const int li = lane & 15;
+    wait_vm0();
     float rr[kTM];
 #pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      rr[tm] = i < M ? r[i] : 0.f;
-    }
+    for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
     store_block<false>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
       f32x4_t v = acc[tm][tn];
 #pragma unroll
@@ -565,29 +606,34 @@ struct EpiRmsNormBwd {
   void* da;
   float* Pg;
   int64_t M, D;
+  // during the last K step: the h block into the staging area; r, s (0 past M) and the wave's 64
+  // gamma values into aux
+  __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int64_t nb, int lane) const {
+    StageBf16{stage, lane}.fill_dma(h, D, mb, nb, M);
+    dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
+    dma_vec<2>(aux + 1024, s + mb, (M - mb) * 4, lane);
+    dma_vec<1>(aux + 2048, gamma + nb, (D - nb) * 2, lane);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t* stage) const {
+                                             lds_char_t* stage, lds_char_t* aux) const {
     const int li = lane & 15, lj = 4 * (lane >> 4);
     const float invD = 1.0f / float(D);
-    // h through the staging area first (whole 128-byte rows per load; before the row factors, so the
-    // loads do not share registers with them); each lane's bf16 da for a (tm, tn) tile then takes
-    // the place of the h values it has just read
+    wait_vm0();  // early()'s DMA
+    // each lane's bf16 da for a (tm, tn) tile takes the place of the h values it has just read
     const StageBf16 st{stage, lane};
-    st.fill(h, D, mb, nb, M);
     float rr[kTM], c2[kTM];
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      const bool ok = i < M;
-      rr[tm] = ok ? r[i] : 0.f;
-      c2[tm] = ok ? s[i] * rr[tm] * rr[tm] * invD : 0.f;
+      const int row = 16 * tm + li;
+      rr[tm] = lds_f32(aux + row * 4);
+      c2[tm] = lds_f32(aux + 1024 + row * 4) * rr[tm] * rr[tm] * invD;
     }
     // da tile by tile, and the dgamma column partials
 #pragma unroll
     for (int tn = 0; tn < kTN; ++tn) {
       const int64_t j = nb + 16 * tn + lj;
       float gam[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
-      unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gam);
+      unpack4_bf16(lds_u2(aux + 2048 + (16 * tn + lj) * 2), gam);
 #pragma unroll
       for (int tm = 0; tm < kTM; ++tm) {
         float hv[4];
@@ -625,6 +671,12 @@ template <class Epi, class = void>
 struct HasPrologue : std::false_type {};
 template <class Epi>
 struct HasPrologue<Epi, decltype(std::declval<const Epi&>().prologue(nullptr), void())> : std::true_type {};
+// ... and DMA of its inputs into its LDS during the last K step (early(stage, aux, mb, nb,
+// lane)); such an epilogue takes the auxiliary area too and waits for that DMA itself.
+template <class Epi, class = void>
+struct HasEarly : std::false_type {};
+template <class Epi>
+struct HasEarly<Epi, decltype(std::declval<const Epi&>().early(nullptr, nullptr, 0, 0, 0), void())> : std::true_type {};
 
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, const Epi epi) {
@@ -642,14 +694,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
   map_tile(p.M, p.N, tile_m, tile_n);
   const int64_t m0 = int64_t(tile_m) * kBM, n0 = int64_t(tile_n) * kBN;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int64_t nb = n0 + (wave & 3) * kWaveTileN;
+  lds_char_t *stage, *aux;
+  epi_regions(smem, wave, int(dceil_div(p.K, kBK)), stage, aux);
   f32x4_t acc[kTM][kTN];
   if (wave < 4) {
-    mainloop<A_K, B_K, 0>(p, m0, n0, smem, acc);
-    epi(acc, m0, nb, threadIdx.x & 63, smem + wave * kEpiWaveBytes);
+    mainloop<A_K, B_K, 0>(p, m0, n0, smem, acc, [&] {
+      if constexpr (HasEarly<Epi>::value) epi.early(stage, aux, m0, nb, lane);
+    });
+    if constexpr (HasEarly<Epi>::value) epi(acc, m0, nb, lane, stage, aux);
+    else epi(acc, m0, nb, lane, stage);
   } else {
-    mainloop<A_K, B_K, 1>(p, m0, n0, smem, acc);
-    epi(acc, m0 + kWaveTileM, nb, threadIdx.x & 63, smem + wave * kEpiWaveBytes);
+    mainloop<A_K, B_K, 1>(p, m0, n0, smem, acc, [&] {
+      if constexpr (HasEarly<Epi>::value) epi.early(stage, aux, m0 + kWaveTileM, nb, lane);
+    });
+    if constexpr (HasEarly<Epi>::value) epi(acc, m0 + kWaveTileM, nb, lane, stage, aux);
+    else epi(acc, m0 + kWaveTileM, nb, lane, stage);
   }
 }
 

@@ -76,6 +76,7 @@ constexpr int kASlots = 3, kBSlots = 2;            // LDS ring slots of the A an
 constexpr int kBBase = kASlots * kTileBytes;       // B slots follow the A slots
 constexpr int kSmemBytes = (kASlots + kBSlots) * kTileBytes;  // 160 KB, all of a CU's LDS
 constexpr int kEpiWaveBytes = 16384;               // per-wave LDS staging of the epilogue (reuses the slots)
+constexpr int kAuxWaveBytes = 4096;                // per-wave LDS of the epilogue's row / column vectors
 constexpr int kDmaWaves = 4;                       // one wave group loads each operand
 constexpr int kSegs = kTileBytes / 1024 / kDmaWaves;  // 1 KB DMA segments per wave per tile
 static_assert(kWaves == 8 && kTM == 8 && kTN == 4, "two groups of four 128 x 64 wave tiles");
@@ -364,12 +365,40 @@ __device__ __forceinline__ void compute(f32x4_t (&acc)[kTM][kTN], const Frag (&a
   });
 }
 
+// The epilogue's LDS, given K steps KT. Wave 4 G + p gets a 16 KB staging area and 4 KB
+// of auxiliary space, all disjoint, placed so that each group may start DMA into them
+// during its last K step (the `early` hook of mainloop):
+//   group 0 (from the start of its last step, phase 2 KT - 2): the two A slots other
+//     than (KT - 1) % 3, which no wave reads again;
+//   group 1 (after the barrier that ends phase 2 KT - 1, when both groups' last
+//     fragment reads are done): A slot (KT - 1) % 3 and B slot (KT - 1) % 2;
+//   auxiliary areas: B slot KT % 2, idle from phase 2 KT - 2 (its last tile, K step
+//     KT - 2, was read by phase 2 KT - 3).
+__device__ __forceinline__ void epi_regions(lds_char_t* smem, int wave, int KT, lds_char_t*& stage,
+                                            lds_char_t*& aux) {
+  constexpr int kPerSlot = kTileBytes / kEpiWaveBytes;  // 2 staging areas per slot
+  const int sa = (KT - 1) % kASlots, p = wave & 3;
+  int region;
+  if (wave < 4) {
+    const int other = (p >> 1) == 0 ? (sa == 0 ? 1 : 0) : (sa == 2 ? 1 : 2);  // the A slots != sa, ascending
+    region = other * kPerSlot + (p & 1);
+  } else {
+    region = p < 2 ? sa * kPerSlot + p : (kASlots + ((KT - 1) & 1)) * kPerSlot + (p - 2);
+  }
+  stage = smem + region * kEpiWaveBytes;
+  aux = smem + kBBase + (KT & 1) * kTileBytes + wave * kAuxWaveBytes;
+}
+static_assert(kTileBytes == 2 * kEpiWaveBytes && kWaves * kAuxWaveBytes <= kTileBytes, "epilogue LDS layout");
+
 // Group G's side of the loop, for wave 4 G + p:
 //   acc[tm][tn] (lane l, reg e) = C[m0 + 128 G + 16 tm + l % 16][n0 + 64 p + 16 tn + 4 (l / 16) + e].
-// Both groups pass the same number of barriers (1 + 2 KT).
-template <bool A_K, bool B_K, int G>
+// Both groups pass the same number of barriers (1 + 2 KT). early() issues the
+// epilogue's DMA into its LDS (epi_regions) during the last K step: group 0 at the
+// start of that step, group 1 after its last barrier; it adds only to vmcnt, which
+// the epilogue waits for.
+template <bool A_K, bool B_K, int G, class Early>
 __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
-                                         f32x4_t (&acc)[kTM][kTN]) {
+                                         f32x4_t (&acc)[kTM][kTN], Early&& early) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Loop<A_K, B_K> L;
@@ -385,25 +414,35 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
 
   Frag a[2][kTM], b[2][kTN];
   auto none = [](auto) {};
+  // step(k, first, last): the last step is peeled off (its DMA is the epilogue's), so the
+  // loop body carries none of it.
+  auto run = [&](auto&& step) {
+    if (KT == 1) {
+      step(0, std::true_type{}, std::true_type{});
+    } else {
+      step(0, std::true_type{}, std::false_type{});
+      for (int k = 1; k < KT - 1; ++k) step(k, std::false_type{}, std::false_type{});
+      step(KT - 1, std::false_type{}, std::true_type{});
+    }
+  };
   if constexpr (G == 0) {
     // prologue: B(0). Phase 2k: the DMA of B(k+1), then L(k); phase 2k+1:
     // C(k), then wait for B(k+1).
     L.dma_b(0);
     wait_vm0();
     block_barrier();
-    auto step = [&](int k, auto first) {
-      if (k + 1 < KT) L.dma_b(k + 1);
+    run([&](int k, auto first, auto last) {
+      if constexpr (decltype(last)::value) early();
+      else L.dma_b(k + 1);
       L.load(k, a, b);
       wait_lgkm0();
       block_barrier();
       prio_high();
       compute<decltype(first)::value>(acc, a, b, none);
       prio_low();
-      wait_vm0();
+      if constexpr (!decltype(last)::value) wait_vm0();  // B(k + 1); the last step's DMA is the epilogue's
       block_barrier();
-    };
-    step(0, std::true_type{});
-    for (int k = 1; k < KT; ++k) step(k, std::false_type{});
+    });
   } else {
     // prologue: A(0), and A(1) left in flight (it is first read in phase 2).
     // Phase 0: nothing; phase 2k+1: the DMA of A(k+2), then L(k), then wait
@@ -417,7 +456,7 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
     }
     block_barrier();
     block_barrier();
-    auto step = [&](int k, auto first) {
+    run([&](int k, auto first, auto last) {
       const bool more = k + 2 < KT;
       if (more) L.dma_a(k + 2);
       L.load(k, a, b);
@@ -425,13 +464,12 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
       else wait_vm0();
       wait_lgkm0();
       block_barrier();
+      if constexpr (decltype(last)::value) early();
       prio_high();
       compute<decltype(first)::value>(acc, a, b, none);
       prio_low();
-      if (k + 1 < KT) block_barrier();
-    };
-    step(0, std::true_type{});
-    for (int k = 1; k < KT; ++k) step(k, std::false_type{});
+      if constexpr (!decltype(last)::value) block_barrier();
+    });
   }
   mfma_drain(acc);
 }
