@@ -152,6 +152,7 @@ __device__ __forceinline__ void dma_vec(lds_char_t* dst, const void* src, int64_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + q * 256), 4, uint32_t(q * 256 + lane * 4), 0, 0, 0);
 }
 __device__ __forceinline__ float lds_f32(const lds_char_t* p) { return *reinterpret_cast<const LDS_AS float*>(p); }
+__device__ __forceinline__ int64_t lds_i64(const lds_char_t* p) { return *reinterpret_cast<const LDS_AS int64_t*>(p); }
 __device__ __forceinline__ uint2 lds_u2(const lds_char_t* p) {
   const u32x2_t v = *reinterpret_cast<const LDS_AS u32x2_t*>(p);
   return make_uint2(v.x, v.y);
@@ -522,9 +523,14 @@ struct EpiCeStats {
   float2* Pml;
   float* tgt;
   int64_t M, V, pcols;
+  // during the last K step: the wave's 128 targets into aux
+  __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
+    dma_vec<4>(aux, targets + mb, (M - mb) * 8, lane);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t*) const {
+                                             lds_char_t*, lds_char_t* aux) const {
     const int li = lane & 15, lg = lane >> 4;
+    wait_vm0();
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
@@ -544,7 +550,7 @@ struct EpiCeStats {
       l += shfl_xor(l, 16);
       l += shfl_xor(l, 32);
       if (ok && lg == 0) Pml[i * pcols + nb / kWaveTileN] = make_float2(m, l);
-      const int64_t t = ok ? targets[i] : -1;
+      const int64_t t = ok ? lds_i64(aux + (16 * tm + li) * 8) : -1;
       const int64_t c = t - nb;  // the target's column inside the wave tile
       if (ok && ce_valid(t, V) && c >= 0 && c < kWaveTileN && ((c >> 2) & 3) == lg) {
         float v = 0.f;
@@ -566,20 +572,28 @@ struct EpiCeBwd {
   const float* dloss;
   uint16_t* dlogits;
   int64_t M, V;
+  // during the last K step: the wave's 128 targets, lse and dloss values into aux
+  __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
+    dma_vec<4>(aux, targets + mb, (M - mb) * 8, lane);
+    dma_vec<2>(aux + 1024, lse + mb, (M - mb) * 4, lane);
+    dma_vec<2>(aux + 2048, dloss + mb, (M - mb) * 4, lane);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t* stage) const {
+                                             lds_char_t* stage, lds_char_t* aux) const {
     const int li = lane & 15, lg = lane >> 4;
+    wait_vm0();
     float ls[kTM], dl[kTM];
     int tc[kTM];
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      const int64_t t = i < M ? targets[i] : -1;
+      const int row = 16 * tm + li;
+      const int64_t i = mb + row;
+      const int64_t t = i < M ? lds_i64(aux + row * 8) : -1;
       const bool ok = i < M && ce_valid(t, V);
       // an ignored row takes lse = +inf, so exp() is 0 there rather than overflowing to inf
       // (0 * inf would make its zero gradient NaN)
-      ls[tm] = ok ? lse[i] : INFINITY;
-      dl[tm] = ok ? dloss[i] : 0.f;
+      ls[tm] = ok ? lds_f32(aux + 1024 + row * 4) : INFINITY;
+      dl[tm] = ok ? lds_f32(aux + 2048 + row * 4) : 0.f;
       const int64_t c = t - nb - 4 * lg;  // target column relative to the lane's first column of tile 0
       tc[tm] = (c >= 0 && c < kWaveTileN) ? int(c) : -1;
     }
