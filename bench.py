@@ -379,10 +379,15 @@ def main():
                "dW": torch.empty(V, D, dtype=bf, device=dev)}
         CF = L.bind_ce_fwd(hl, Wl, tg, cfo, L.workspace(L.CODA_OP_CE_FWD, M, D, V, dev))
         CB = L.bind_ce_bwd(hl, Wl, tg, cfo["lse"], dloss, cbo)
+        # the forward storing its fp32 logits [M, V] and the backward reading them
+        lg = torch.empty(M, V, dtype=torch.float32, device=dev)
+        cso = {k: torch.empty_like(v) for k, v in cfo.items()}
+        CFS = L.bind_ce_fwd(hl, Wl, tg, cso, L.workspace(L.CODA_OP_CE_FWD, M, D, V, dev), logits=lg)
+        CBS = L.bind_ce_bwd(hl, Wl, tg, cso["lse"], dloss, cbo, logits=lg)
         # the unfused baseline stores the fp32 logits [M, V] in its workspace
         uws = None if args.no_unfused else L.workspace(L.CODA_OP_UNFUSED_CE_FWD, M, D, V, dev)
         t = {}
-        runs = [("fwd", CF, None), ("bwd", CB, None)]
+        runs = [("fwd", CF, None), ("bwd", CB, None), ("sfwd", CFS, None), ("sbwd", CBS, None)]
         if uws is not None:
             runs += [("ufwd", CF, uws), ("ubwd", CB, uws)]
         for name, obj, w in runs:
@@ -401,13 +406,18 @@ def main():
               "tflops": round((ce_f + ce_b) / (t["fwd"] + t["bwd"]) / 1e9, 1)}
         ce["pct_peak"] = round(100 * ce["tflops"] / PEAK_BF16_TFLOPS, 2)
         log(f"[bench] cross-entropy LM head: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {ce['tflops']} TFLOP/s")
+        ce["stored_logits"] = {"fwd_ms": round(t["sfwd"], 4), "bwd_ms": round(t["sbwd"], 4),
+                               "logits_gb": round(M * V * 4 / 1e9, 2),
+                               "speedup_vs_recompute": round((t["fwd"] + t["bwd"]) / (t["sfwd"] + t["sbwd"]), 3)}
+        log(f"[bench] cross-entropy with stored fp32 logits ({M * V * 4 / 1e9:.1f} GB): fwd {t['sfwd']:.3f} ms, "
+            f"bwd {t['sbwd']:.3f} ms")
         if uws is not None:
             ce["unfused"] = {"fwd_ms": round(t["ufwd"], 4), "bwd_ms": round(t["ubwd"], 4),
                              "fused_fwd_speedup": round(t["ufwd"] / t["fwd"], 3),
                              "fused_bwd_speedup": round(t["ubwd"] / t["bwd"], 3)}
             log(f"[bench] unfused cross-entropy (stored fp32 logits): fwd {t['ufwd']:.3f} ms, "
                 f"bwd {t['ubwd']:.3f} ms")
-        del hl, Wl, tg, dloss, cfo, cbo, CF, CB, uws
+        del hl, Wl, tg, dloss, cfo, cbo, CF, CB, uws, lg, cso, CFS, CBS
 
     unfused = None
     if not args.no_unfused:

@@ -212,7 +212,7 @@ typedef struct {
  * statistics; kucoin, section "五つの「ブロック」": block log-sum-exp, running max and
  * sum-exp). For hidden states h [M, D], an output weight W [V, D] (one row per
  * vocabulary entry, the nn.Linear / tied-embedding layout) and targets t [M]:
- *     logits = h @ W^T (never stored),
+ *     logits = h @ W^T (not stored unless asked for, see below),
  *     lse_i  = log sum_v exp(logits_iv),   loss_i = lse_i - logits_i,t_i.
  * The logits GEMM's epilogue reduces each (row, 64-column) tile to its max m and
  * sum exp(logit - m) and picks out the target logit; a row kernel combines the
@@ -220,7 +220,10 @@ typedef struct {
  * its loss is 0 (lse is still written). D and V multiples of 256 in [256, 2^20]
  * (Llama-3's V = 128256 = 501 * 256).
  *   in : h [M,D] bf16, W [V,D] bf16, targets [M] int64.
- *   out: lse [M] f32, loss [M] f32 (per row; a mean is the caller's sum / count).
+ *   out: lse [M] f32, loss [M] f32 (per row; a mean is the caller's sum / count);
+ *        logits [M,V] f32, optional (NULL: not stored): the same epilogue also stores the
+ *        fp32 logits, which coda_ce_bwd then reads instead of recomputing them -- 4 M V
+ *        bytes (4.2 GB at M = 8192, V = 128256) traded for the backward's logits GEMM.
  * Workspace: coda_workspace_bytes(CODA_OP_CE_FWD, M, D, V). */
 typedef struct {
   int64_t M, D, V;
@@ -229,6 +232,7 @@ typedef struct {
   const int64_t* targets;
   float* lse;
   float* loss;
+  float* logits;
 } coda_ce_fwd_args_t;
 
 /* Backward of L = sum_i dloss_i loss_i for the forward's lse (same sections; the
@@ -236,7 +240,10 @@ typedef struct {
  * the same GEMM):
  *     dlogits_iv = dloss_i (exp(logits_iv - lse_i) - [v = t_i]), 0 on ignored rows,
  *     dh = dlogits @ W,   dW = dlogits^T @ h.
- *   in : h, W, targets as in the forward; lse [M] f32 (the forward's); dloss [M] f32.
+ *   in : h, W, targets as in the forward; lse [M] f32 (the forward's); dloss [M] f32;
+ *        logits [M,V] f32, optional: the forward's stored logits (NULL: recomputed by the
+ *        GEMM). Given, a row kernel reads them for dlogits (the same values: the stored
+ *        logits are the recomputing GEMM's accumulators).
  *   out: dlogits [M,V] bf16 (the operand of the two products, written as an output),
  *        dh [M,D] in dh_dtype, dW [V,D] in dW_dtype. No workspace. */
 typedef struct {
@@ -251,6 +258,7 @@ typedef struct {
   void* dW;
   coda_dtype_t dh_dtype;
   coda_dtype_t dW_dtype;
+  const float* logits;
 } coda_ce_bwd_args_t;
 
 /* Operand layouts for coda_gemm. */
@@ -351,7 +359,8 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
  *   op = CODA_OP_CE_FWD, args = coda_ce_fwd_args_t*: the logits h@W^T stored as
  *     fp32 in the workspace ([M, V]) -> a row kernel for lse and loss.
  *   op = CODA_OP_CE_BWD, args = coda_ce_bwd_args_t*: the logits stored as fp32
- *     in the workspace -> a row kernel for dlogits -> the same dh and dW GEMMs. */
+ *     in the workspace -> a row kernel for dlogits -> the same dh and dW GEMMs.
+ *   (Both ignore the structs' optional logits pointer.) */
 coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t ws_bytes, void* stream);
 
 /* SwiGLU forward and backward (see coda_fwd_swiglu_args_t, coda_bwd_swiglu_args_t). */

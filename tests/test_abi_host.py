@@ -50,7 +50,7 @@ int main(void) {
   O(coda_bwd_swiglu_args_t, da_dtype); O(coda_bwd_swiglu_args_t, dW2_dtype);
   O(coda_ce_fwd_args_t, V); O(coda_ce_fwd_args_t, targets); O(coda_ce_fwd_args_t, loss);
   O(coda_ce_bwd_args_t, dloss); O(coda_ce_bwd_args_t, dW); O(coda_ce_bwd_args_t, dh_dtype);
-  O(coda_ce_bwd_args_t, dW_dtype);
+  O(coda_ce_bwd_args_t, dW_dtype); O(coda_ce_fwd_args_t, logits); O(coda_ce_bwd_args_t, logits);
   return 0;
 }
 """
@@ -310,6 +310,14 @@ def test_validate_cross_entropy():
         setattr(c, k, v)
         assert lib.coda_validate_ce_bwd(ctypes.byref(c)) == want, k
         assert lib.coda_ce_bwd(ctypes.byref(c), None) == want, k
+    # the optional stored logits: NULL or 16-byte aligned
+    for S, v, fn in ((L.CeFwdArgs, f, lambda x: lib.coda_validate_ce_fwd(ctypes.byref(x), WS, need)),
+                     (L.CeBwdArgs, b, lambda x: lib.coda_validate_ce_bwd(ctypes.byref(x)))):
+        x = S.from_buffer_copy(v)
+        x.logits = fake(20)
+        assert fn(x) == L.CODA_OK
+        x.logits = ctypes.c_void_p(A + 8)
+        assert fn(x) == L.CODA_ERR_ALIGN
     # the unfused baseline takes the same structs and needs the [M, V] fp32 logits workspace
     un = L.workspace_bytes(L.CODA_OP_UNFUSED_CE_FWD, 300, 256, 1024)
     for op, args in ((L.CODA_OP_CE_FWD, f), (L.CODA_OP_CE_BWD, b)):

@@ -9,7 +9,8 @@ rounding of dlogits before the two products.
 
 The unfused baseline (coda_unfused_ref: fp32 logits stored, then row kernels) is
 held to the same bounds; its logits come from the same mainloop, so its backward
-matches the fused one bit for bit.
+matches the fused one bit for bit. So does the backward from the forward's stored
+logits (coda_ce_fwd with a logits output, coda_ce_bwd reading them).
 """
 import numpy as np
 import pytest
@@ -121,6 +122,17 @@ def test_ce_small_full(name):
     check_fwd(fu, ref, host["targets"])
     for k in ("dlogits", "dh", "dW"):
         assert torch.equal(bu[k], b32[k]), k
+    # the forward storing its fp32 logits, and the backward reading them
+    fs = L.ce_fwd(d["h"], d["W"], d["targets"], store_logits=True)
+    bs = L.ce_bwd(d["h"], d["W"], d["targets"], lse_ref.to(DEV), d["dloss"], dh_dtype=torch.float32,
+                  dW_dtype=torch.float32, logits=fs["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(fs["lse"], f["lse"]) and torch.equal(fs["loss"], f["loss"])
+    e_logits = mt.normwise(fs["logits"], mt.f64(host["h"]) @ mt.f64(host["W"]).T)
+    print(f"  stored logits max|d|/rms={e_logits:.3e}")
+    assert e_logits <= 1e-5
+    for k in ("dlogits", "dh", "dW"):
+        assert torch.equal(bs[k], b32[k]), k
 
 
 def test_ce_forward_then_backward_on_device():
@@ -136,19 +148,20 @@ def test_ce_forward_then_backward_on_device():
     check_bwd(b, host, torch.from_numpy(ref["lse"]).to(torch.float32))
 
 
-@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
-def test_ce_extreme_logits(unfused):
+@pytest.mark.parametrize("mode", ["fused", "unfused", "stored"])
+def test_ce_extreme_logits(mode):
     """Logits of size ~60 (a peaked softmax) and an all-equal row: the tile statistics keep exp in range.
     The ignored row 1 has logits above 88 (exp overflows fp32 there): its gradient is still exactly 0."""
     c = dict(M=32, D=256, V=768)
-    announce(f"coda_ce_fwd / coda_ce_bwd extreme logits {c} unfused={unfused}")
+    announce(f"coda_ce_fwd / coda_ce_bwd extreme logits {c} mode={mode}")
+    unfused = mode == "unfused"
     host = case_inputs(c, seed=2)
     host["W"] = (host["W"].float() * 30).to(torch.bfloat16)   # logits std ~60
     host["h"][5] = 0                                          # all logits 0: lse = log V, loss = log V
     assert host["targets"][1] == -100
     assert (mt.f64(host["h"][1]) @ mt.f64(host["W"]).T).max() > 89.0
     d = {k: v.to(DEV) for k, v in host.items()}
-    f = L.ce_fwd(d["h"], d["W"], d["targets"], unfused=unfused)
+    f = L.ce_fwd(d["h"], d["W"], d["targets"], unfused=unfused, store_logits=mode == "stored")
     torch.cuda.synchronize()
     ref = orc.lm_head_cross_entropy(host["h"], host["W"], host["targets"])
     assert torch.all(torch.isfinite(f["lse"])) and torch.all(torch.isfinite(f["loss"]))
@@ -156,7 +169,7 @@ def test_ce_extreme_logits(unfused):
     check_fwd(f, ref, host["targets"])
     lse_ref = torch.from_numpy(ref["lse"]).to(torch.float32)
     b = L.ce_bwd(d["h"], d["W"], d["targets"], lse_ref.to(DEV), d["dloss"], dh_dtype=torch.float32,
-                 dW_dtype=torch.float32, unfused=unfused)
+                 dW_dtype=torch.float32, unfused=unfused, logits=f.get("logits"))
     torch.cuda.synchronize()
     for k in ("dlogits", "dh", "dW"):
         assert torch.all(torch.isfinite(b[k].float())), k
@@ -204,3 +217,10 @@ def test_ce_llama3_8b_lm_head_sampled():
                  dW_dtype=torch.float32)
     torch.cuda.synchronize()
     check_bwd(b, host, lse_ref, rows=rows, vrows=vrows)
+    # from the forward's stored logits: the same gradients, bit for bit
+    fs = L.ce_fwd(d["h"], d["W"], d["targets"], store_logits=True)
+    bs = L.ce_bwd(d["h"], d["W"], d["targets"], lse_ref.to(DEV), d["dloss"], dh_dtype=torch.float32,
+                  dW_dtype=torch.float32, logits=fs["logits"])
+    torch.cuda.synchronize()
+    for k in ("dlogits", "dh", "dW"):
+        assert torch.equal(bs[k], b[k]), k

@@ -71,13 +71,14 @@ class BwdSwigluArgs(ctypes.Structure):
 
 class CeFwdArgs(ctypes.Structure):
     _fields_ = [("M", c_int64), ("D", c_int64), ("V", c_int64), ("h", c_void_p), ("W", c_void_p),
-                ("targets", c_void_p), ("lse", c_void_p), ("loss", c_void_p)]
+                ("targets", c_void_p), ("lse", c_void_p), ("loss", c_void_p), ("logits", c_void_p)]
 
 
 class CeBwdArgs(ctypes.Structure):
     _fields_ = [("M", c_int64), ("D", c_int64), ("V", c_int64), ("h", c_void_p), ("W", c_void_p),
                 ("targets", c_void_p), ("lse", c_void_p), ("dloss", c_void_p),
-                ("dlogits", c_void_p), ("dh", c_void_p), ("dW", c_void_p), ("dh_dtype", c_int), ("dW_dtype", c_int)]
+                ("dlogits", c_void_p), ("dh", c_void_p), ("dW", c_void_p), ("dh_dtype", c_int), ("dW_dtype", c_int),
+                ("logits", c_void_p)]
 
 
 class CodaError(RuntimeError):
@@ -365,7 +366,7 @@ def bind_bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, out, ws):
                        (dOut, W2, o, y, h, g, r, gamma, W1, out))
 
 
-def _ce_fwd_args(h, W, targets, lse, loss):
+def _ce_fwd_args(h, W, targets, lse, loss, logits=None):
     M, D = h.shape
     V = W.shape[0]
     _want(h, "h", torch.bfloat16, (M, D))
@@ -373,20 +374,26 @@ def _ce_fwd_args(h, W, targets, lse, loss):
     _want(targets, "targets", torch.int64, (M,))
     _want(lse, "lse", torch.float32, (M,))
     _want(loss, "loss", torch.float32, (M,))
-    return CeFwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(loss))
+    if logits is not None:
+        _want(logits, "logits", torch.float32, (M, V))
+    return CeFwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(loss),
+                     None if logits is None else _ptr(logits))
 
 
-def ce_fwd(h, W, targets, ws=None, out=None, unfused=False):
+def ce_fwd(h, W, targets, ws=None, out=None, unfused=False, store_logits=False):
     """Cross-entropy of the LM-head logits h @ W^T against targets (int64; outside [0, V) = ignored).
-    Returns dict(lse, loss), both [M] fp32. unfused: the fp32 logits stored, then a row
-    kernel (coda_unfused_ref)."""
+    Returns dict(lse, loss), both [M] fp32. unfused: the fp32 logits stored in the workspace, then
+    a row kernel (coda_unfused_ref). store_logits: the epilogue also writes the fp32 logits
+    (out["logits"], [M, V]) for ce_bwd(logits=...)."""
     M, D = h.shape
     V = W.shape[0]
     dev = h.device
     if out is None:
         out = {"lse": torch.empty(M, dtype=torch.float32, device=dev),
                "loss": torch.empty(M, dtype=torch.float32, device=dev)}
-    a = _ce_fwd_args(h, W, targets, out["lse"], out["loss"])
+        if store_logits:
+            out["logits"] = torch.empty(M, V, dtype=torch.float32, device=dev)
+    a = _ce_fwd_args(h, W, targets, out["lse"], out["loss"], out.get("logits"))
     if ws is None:
         ws = workspace(CODA_OP_UNFUSED_CE_FWD if unfused else CODA_OP_CE_FWD, M, D, V, dev)
     if unfused:
@@ -397,7 +404,7 @@ def ce_fwd(h, W, targets, ws=None, out=None, unfused=False):
     return out
 
 
-def _ce_bwd_args(h, W, targets, lse, dloss, out):
+def _ce_bwd_args(h, W, targets, lse, dloss, out, logits=None):
     M, D = h.shape
     V = W.shape[0]
     _want(h, "h", torch.bfloat16, (M, D))
@@ -406,14 +413,18 @@ def _ce_bwd_args(h, W, targets, lse, dloss, out):
     _want(lse, "lse", torch.float32, (M,))
     _want(dloss, "dloss", torch.float32, (M,))
     _want(out["dlogits"], "dlogits", torch.bfloat16, (M, V))
+    if logits is not None:
+        _want(logits, "logits", torch.float32, (M, V))
     return CeBwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(dloss), _ptr(out["dlogits"]),
-                     _ptr(out["dh"]), _ptr(out["dW"]), _dt(out["dh"].dtype), _dt(out["dW"].dtype))
+                     _ptr(out["dh"]), _ptr(out["dW"]), _dt(out["dh"].dtype), _dt(out["dW"].dtype),
+                     None if logits is None else _ptr(logits))
 
 
 def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bfloat16, out=None, unfused=False,
-           ws=None):
+           ws=None, logits=None):
     """Backward of sum_i dloss_i loss_i: dict(dlogits [M,V] bf16, dh [M,D], dW [V,D]).
-    unfused: the fp32 logits stored in a workspace, then a dlogits row kernel."""
+    unfused: the fp32 logits stored in a workspace, then a dlogits row kernel. logits: the
+    forward's stored fp32 logits, read instead of recomputed."""
     M, D = h.shape
     V = W.shape[0]
     dev = h.device
@@ -421,7 +432,7 @@ def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bf
         out = {"dlogits": torch.empty(M, V, dtype=torch.bfloat16, device=dev),
                "dh": torch.empty(M, D, dtype=dh_dtype, device=dev),
                "dW": torch.empty(V, D, dtype=dW_dtype, device=dev)}
-    a = _ce_bwd_args(h, W, targets, lse, dloss, out)
+    a = _ce_bwd_args(h, W, targets, lse, dloss, out, logits)
     if unfused:
         if ws is None:
             ws = workspace(CODA_OP_UNFUSED_CE_BWD, M, D, V, dev)
@@ -450,12 +461,13 @@ class BoundCe:
             _check(lib().coda_ce_bwd(ctypes.byref(self.args), stream), "coda_ce_bwd")
 
 
-def bind_ce_fwd(h, W, targets, out, ws):
-    return BoundCe("fwd", _ce_fwd_args(h, W, targets, out["lse"], out["loss"]), ws, (h, W, targets, out))
+def bind_ce_fwd(h, W, targets, out, ws, logits=None):
+    return BoundCe("fwd", _ce_fwd_args(h, W, targets, out["lse"], out["loss"], logits), ws, (h, W, targets, out, logits))
 
 
-def bind_ce_bwd(h, W, targets, lse, dloss, out):
-    return BoundCe("bwd", _ce_bwd_args(h, W, targets, lse, dloss, out), None, (h, W, targets, lse, dloss, out))
+def bind_ce_bwd(h, W, targets, lse, dloss, out, logits=None):
+    return BoundCe("bwd", _ce_bwd_args(h, W, targets, lse, dloss, out, logits), None,
+                   (h, W, targets, lse, dloss, out, logits))
 
 
 class BoundGemm0:

@@ -74,6 +74,7 @@ coda_status_t validate_ce_fwd_common(const coda_ce_fwd_args_t* a) {
   coda_status_t st = check_ptrs(ps, 5);
   if (st != CODA_OK) return st;
   if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V) || !grid_ok(a->M, a->V)) return CODA_ERR_SHAPE;
+  if (a->logits != nullptr && !aligned16(a->logits)) return CODA_ERR_ALIGN;  // optional output
   return CODA_OK;
 }
 
@@ -211,6 +212,7 @@ coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a) {
   if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->V)) return CODA_ERR_SHAPE;
   if (!grid_ok(a->M, a->V) || !grid_ok(a->M, a->D) || !grid_ok(a->V, a->D)) return CODA_ERR_SHAPE;
   if (!dtype_ok(a->dh_dtype) || !dtype_ok(a->dW_dtype)) return CODA_ERR_ARG;
+  if (a->logits != nullptr && !aligned16(a->logits)) return CODA_ERR_ALIGN;  // optional input
   return CODA_OK;
 }
 

@@ -517,11 +517,14 @@ __device__ __forceinline__ bool ce_valid(int64_t t, int64_t V) { return t >= 0 &
 
 // Per (row, wave tile of 64 columns): the running statistics of the row's
 // logits over those columns, m = max and l = sum exp(logit - m) -> Pml[i, nb / 64];
-// the lane that holds column t_i writes the target logit to tgt[i].
+// the lane that holds column t_i writes the target logit to tgt[i]. STORE: the fp32
+// logits are also written to logits[M, V].
+template <bool STORE>
 struct EpiCeStats {
   const int64_t* targets;
   float2* Pml;
   float* tgt;
+  float* logits;
   int64_t M, V, pcols;
   // during the last K step: the wave's 128 targets into aux
   __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
@@ -530,7 +533,7 @@ struct EpiCeStats {
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
                                              lds_char_t*, lds_char_t* aux) const {
     const int li = lane & 15, lg = lane >> 4;
-    wait_vm0();
+    wait_vm0();  // early()'s DMA (before any store: vmcnt counts stores too)
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
       const int64_t i = mb + 16 * tm + li;
@@ -560,6 +563,12 @@ struct EpiCeStats {
           for (int e = 0; e < 4; ++e) v = (16 * tn + 4 * lg + e == c) ? acc[tm][tn][e] : v;
         tgt[i] = v;
       }
+    }
+    if constexpr (STORE) {  // after the statistics (issued first they make the compiler spill)
+#pragma unroll
+      for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < kTN; ++tn) store_f32(logits, V, mb, nb, M, lane, tm, tn, acc[tm][tn]);
     }
   }
 };
@@ -1509,7 +1518,9 @@ coda_status_t coda_ce_fwd(const coda_ce_fwd_args_t* a, void* ws, size_t ws_bytes
   float* tgt = reinterpret_cast<float*>(ws_at(ws, align256(size_t(a->M) * size_t(pcols) * 8)));
   // logits = h @ W^T: A = h [M, D], B(k=d, v) = W[v, d] (both k contiguous)
   const GemmShape p{a->M, a->V, a->D, a->h, a->D, a->W, a->D};
-  hipError_t e = launch_gemm<true, true>(p, EpiCeStats{a->targets, Pml, tgt, a->M, a->V, pcols}, st);
+  hipError_t e = a->logits != nullptr
+                     ? launch_gemm<true, true>(p, EpiCeStats<true>{a->targets, Pml, tgt, a->logits, a->M, a->V, pcols}, st)
+                     : launch_gemm<true, true>(p, EpiCeStats<false>{a->targets, Pml, tgt, nullptr, a->M, a->V, pcols}, st);
   if (e != hipSuccess) return CODA_ERR_HIP;
   hipLaunchKernelGGL(ce_combine_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, (const float2*)Pml, (const float*)tgt,
                      a->targets, a->lse, a->loss, pcols, a->V);
@@ -1520,10 +1531,16 @@ coda_status_t coda_ce_bwd(const coda_ce_bwd_args_t* a, void* stream) {
   coda_status_t v = coda_validate_ce_bwd(a);
   if (v != CODA_OK) return v;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // recomputed logits with the dlogits epilogue
-  const GemmShape p{a->M, a->V, a->D, a->h, a->D, a->W, a->D};
-  hipError_t e = launch_gemm<true, true>(
-      p, EpiCeBwd{a->targets, a->lse, a->dloss, static_cast<uint16_t*>(a->dlogits), a->M, a->V}, st);
+  hipError_t e;
+  if (a->logits != nullptr) {  // the forward's stored logits: a row kernel instead of the GEMM
+    hipLaunchKernelGGL(ce_rows_bwd_kernel, dim3(unsigned(a->M)), dim3(256), 0, st, a->logits, a->targets, a->lse,
+                       a->dloss, static_cast<uint16_t*>(a->dlogits), a->V);
+    e = hipGetLastError();
+  } else {  // recomputed logits with the dlogits epilogue
+    const GemmShape p{a->M, a->V, a->D, a->h, a->D, a->W, a->D};
+    e = launch_gemm<true, true>(
+        p, EpiCeBwd{a->targets, a->lse, a->dloss, static_cast<uint16_t*>(a->dlogits), a->M, a->V}, st);
+  }
   if (e != hipSuccess) return CODA_ERR_HIP;
   return to_status(ce_bwd_products(a, st));
 }
