@@ -938,21 +938,36 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2* Pml, cons
   }
 }
 
-// Unfused cross-entropy rows, one 256-thread block per row of the stored fp32 logits.
+// Rows of stored fp32 logits, one 256-thread block per row; each thread reads its
+// 16-byte chunks v = tid + 256 (u + kCeUnroll q) in rounds of kCeUnroll, all loads of a
+// round issued before any is used.
+constexpr int kCeUnroll = 4;
+
 // Forward: each thread keeps a running (max, sum exp) over its columns in one pass,
 // then the block combines them; lse_i = m + log l, loss_i = lse_i - logit[i, t_i], 0
 // for an ignored row.
 __global__ __launch_bounds__(256) void ce_rows_fwd_kernel(const float* logits, const int64_t* targets, float* lse,
                                                           float* loss, int64_t V) {
   __shared__ float red[4];
-  const int64_t i = blockIdx.x;
+  const int64_t i = blockIdx.x, n4 = V / 4;
   const float4* lv = reinterpret_cast<const float4*>(logits + i * V);
   float m = -INFINITY, l = 0.f;
-  for (int64_t v = threadIdx.x; v < V / 4; v += 256) {
-    const float4 x = lv[v];
-    const float mn = fmaxf(m, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
-    l = l * expf(m - mn) + ((expf(x.x - mn) + expf(x.y - mn)) + (expf(x.z - mn) + expf(x.w - mn)));
-    m = mn;
+  for (int64_t v0 = threadIdx.x; v0 < n4; v0 += 256 * kCeUnroll) {
+    float4 x[kCeUnroll];
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int64_t v = v0 + 256 * u;
+      x[u] = v < n4 ? lv[v] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) mx = fmaxf(mx, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+    // a round always holds a real column (v0 < n4), so mx is finite
+    l *= expf(m - mx);
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u)
+      l += (expf(x[u].x - mx) + expf(x[u].y - mx)) + (expf(x[u].z - mx) + expf(x[u].w - mx));
+    m = mx;
   }
   const float mb = block_max256(m, red);
   const float lb = block_sum256(m == -INFINITY ? 0.f : l * expf(m - mb), red);
@@ -972,15 +987,27 @@ __global__ __launch_bounds__(256) void ce_rows_bwd_kernel(const float* logits, c
   const int64_t t = targets[i];
   const bool ok = ce_valid(t, V);
   const float ls = ok ? lse[i] : INFINITY, dl = ok ? dloss[i] : 0.f;
+  const int64_t n4 = V / 4;
   const float4* lv = reinterpret_cast<const float4*>(logits + i * V);
   uint2* dv = reinterpret_cast<uint2*>(dlogits + i * V);
-  for (int64_t v = threadIdx.x; v < V / 4; v += 256) {
-    const float4 x = lv[v];
-    const float xs[4] = {x.x, x.y, x.z, x.w};
-    float d[4];
+  for (int64_t v0 = threadIdx.x; v0 < n4; v0 += 256 * kCeUnroll) {
+    float4 x[kCeUnroll];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d[e] = dl * (expf(xs[e] - ls) - (4 * v + e == t ? 1.0f : 0.0f));
-    dv[v] = pack4_bf16(d[0], d[1], d[2], d[3]);
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int64_t v = v0 + 256 * u;
+      x[u] = v < n4 ? lv[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kCeUnroll; ++u) {
+      const int64_t v = v0 + 256 * u;
+      if (v < n4) {
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = dl * (expf(xs[e] - ls) - (4 * v + e == t ? 1.0f : 0.0f));
+        dv[v] = pack4_bf16(d[0], d[1], d[2], d[3]);
+      }
+    }
   }
 }
 
