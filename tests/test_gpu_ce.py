@@ -224,3 +224,28 @@ def test_ce_llama3_8b_lm_head_sampled():
     torch.cuda.synchronize()
     for k in ("dlogits", "dh", "dW"):
         assert torch.equal(bs[k], b[k]), k
+
+
+@pytest.mark.parametrize("stored", [False, True], ids=["recompute", "stored_logits"])
+def test_ce_graph_capture(stored):
+    """The LM head's forward and backward captured into one HIP graph (the backward on the
+    forward's lse, with or without the stored logits): every replay reproduces the eager
+    results bit for bit."""
+    from graph_util import assert_replays_match_eager
+    c = SMALL["ragged"]
+    M, D, V = c["M"], c["D"], c["V"]
+    announce(f"graph capture coda_ce_fwd + coda_ce_bwd {c} stored={stored}")
+    d = {k: v.to(DEV) for k, v in case_inputs(c, seed=7).items()}
+    fo = {"lse": torch.empty(M, dtype=torch.float32, device=DEV), "loss": torch.empty(M, dtype=torch.float32, device=DEV)}
+    if stored:
+        fo["logits"] = torch.empty(M, V, dtype=torch.float32, device=DEV)
+    bo = {"dlogits": torch.empty(M, V, dtype=torch.bfloat16, device=DEV),
+          "dh": torch.empty(M, D, dtype=torch.bfloat16, device=DEV),
+          "dW": torch.empty(V, D, dtype=torch.bfloat16, device=DEV)}
+    ws = L.workspace(L.CODA_OP_CE_FWD, M, D, V, DEV)
+
+    def step():
+        L.ce_fwd(d["h"], d["W"], d["targets"], ws=ws, out=fo)
+        L.ce_bwd(d["h"], d["W"], d["targets"], fo["lse"], d["dloss"], out=bo, logits=fo.get("logits"))
+
+    assert_replays_match_eager(step, list(fo.values()) + list(bo.values()))

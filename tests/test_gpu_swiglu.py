@@ -237,3 +237,30 @@ def test_swiglu_llama3_8b_sampled():
     ecols = inputs.sample(c["E"], 256, 0, "dw2_cols").numpy()
     o32, o16 = run_bwd(to_dev(host))
     check_bwd(o32, o16, host, rows=rows, jcols=jcols, ncols=ncols, ecols=ecols)
+
+
+def test_swiglu_graph_capture():
+    """The SwiGLU block's forward and backward captured into one HIP graph: every replay
+    reproduces the eager results bit for bit (the library allocates and clears nothing)."""
+    from graph_util import assert_replays_match_eager
+    c = SMALL["ragged"]
+    M, K0, D, N, E = c["M"], c["K0"], c["D"], c["N"], c["E"]
+    announce(f"graph capture coda_fwd_swiglu + coda_bwd_swiglu {c}")
+    inp = to_dev(inputs.forward_inputs(M, K0, D, N, seed=6))
+    sw = to_dev(inputs.swiglu_inputs(M, N, E, seed=6))
+    bf = torch.bfloat16
+    fo = {"h": torch.empty(M, D, dtype=bf, device=DEV), "g": torch.empty(M, D, dtype=bf, device=DEV),
+          "r": torch.empty(M, dtype=torch.float32, device=DEV), "y": torch.empty(M, N, dtype=bf, device=DEV),
+          "o": torch.empty(M, N // 2, dtype=bf, device=DEV)}
+    bo = {"dY": torch.empty(M, N, dtype=bf, device=DEV), "da": torch.empty(M, D, dtype=bf, device=DEV),
+          "dgamma": torch.empty(D, dtype=torch.float32, device=DEV), "dW1": torch.empty(D, N, dtype=bf, device=DEV),
+          "dW2": torch.empty(N // 2, E, dtype=bf, device=DEV), "s": torch.empty(M, dtype=torch.float32, device=DEV)}
+    fws = L.workspace(L.CODA_OP_FWD_SWIGLU, M, D, N, DEV)
+    bws = L.workspace(L.CODA_OP_BWD_SWIGLU, M, D, N, DEV)
+
+    def step():
+        L.fwd_swiglu(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, ws=fws, out=fo)
+        L.bwd_swiglu(sw["dOut"], sw["W2"], fo["o"], fo["y"], fo["h"], fo["g"], fo["r"], inp["gamma"], inp["W1"],
+                     ws=bws, out=bo)
+
+    assert_replays_match_eager(step, list(fo.values()) + list(bo.values()))
