@@ -98,6 +98,23 @@ def measured_sclk(kernel: str):
     return blob.get("kernels", {}).get(kernel)
 
 
+def measured_mfma_busy(kernel: str):
+    """Fraction of the kernel's active cycles in which the SIMDs' matrix units are busy, from
+    profiles/mfma_busy_llama3_8b.md (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs), or None
+    when that measurement was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "mfma_busy_llama3_8b.md")
+    if not os.path.exists(path):
+        return None
+    try:
+        blob = json.loads(open(path).read().split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if blob.get("source_digest") != kernel_source_digest():
+        return None
+    k = blob.get("kernels", {}).get(kernel)
+    return None if k is None else k["mfma_busy"]
+
+
 def cpu_baseline(host, rows, ncols, total_rows, seed=0):
     """Time the fp64 oracle (as it is) on a sub-batch of sampled rows of the workload."""
     import numpy as np
@@ -252,6 +269,7 @@ def main():
         clk = measured_sclk(dom)   # the power-limited clock the kernel runs at (2.4 GHz is the peak's)
         roof["sclk_ghz"] = clk
         roof["frac_at_sclk"] = None if clk is None else round(ach / (PEAK_BF16_TFLOPS * clk / 2.4), 4)
+        roof["mfma_busy"] = measured_mfma_busy(dom)
     else:
         ach = damount / (per[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
