@@ -11,7 +11,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   value     = algorithmic TFLOP per step / seconds per step (forward 2MK0D + 2MDN,
               backward 4MDN; epilogue arithmetic is not counted),
   roofline  = the longest kernel of the step against the bf16 dense MFMA peak,
-              its duration from HIP events recorded around it on its stream,
+              its duration from HIP events recorded around it on its stream in a
+              second, instrumented pass of the same K steps (the headline steps
+              carry events only at the two ends of the timed region),
   cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -224,10 +226,26 @@ def main():
         B.run(sp)
     torch.cuda.synchronize()
 
+    # The timed region: K whole steps back to back, HIP events only at its two ends (an
+    # event marker between kernels holds the next dispatch back by several microseconds).
     log(f"[bench] timing {args.steps} steps")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    t_a.record(stream)
+    for _ in range(args.steps):
+        F.run(sp)
+        B.run(sp)
+    t_b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t_a.elapsed_time(t_b) / args.steps    # whole timed region / steps
+
+    # The same K steps again, instrumented: an event after every stage gives the per-stage
+    # (per-kernel) durations, the dominant kernel's roofline figures and the per-step spread.
+    log(f"[bench] per-stage timing: {args.steps} more steps with an event after each stage")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for k in range(args.steps):
         e = ev[k]
         e[0].record(stream)
@@ -238,7 +256,6 @@ def main():
             B.stage(i, sp)
             e[1 + F.nstages + i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
     per = {n: 0.0 for n in names}
     step_ms = []
     for e in ev:
@@ -246,9 +263,20 @@ def main():
             per[n] += e[i].elapsed_time(e[i + 1])
         step_ms.append(e[0].elapsed_time(e[-1]))
     per = {n: v / args.steps for n, v in per.items()}          # ms per launch
-    ms_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps    # whole timed region / steps
-    fwd_ms = sum(per[n] for n in L.FWD_STAGE_NAMES)
-    bwd_ms = sum(per[n] for n in L.BWD_STAGE_NAMES)
+    ms_instrumented = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
+
+    # The forward and the backward each alone, K calls with events at the ends only (the
+    # way the unfused baseline is timed below).
+    def clean_ms(obj, **kw):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            obj.run(sp, **kw)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+    fwd_ms, bwd_ms = clean_ms(F), clean_ms(B)
     fwd_flop = 2 * M * K0 * D + 2 * M * D * N
     bwd_flop = 4 * M * D * N
     value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
@@ -476,6 +504,7 @@ def main():
                    "eps": inputs.EPS, "parallelism": "single GPU"},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "step_ms_p10_p50_p90": [round(float(q), 4) for q in _quantiles(step_ms, (0.1, 0.5, 0.9))],
+        "ms_per_step_instrumented": round(ms_instrumented, 4),
         "cold_cache": cold, "dp8_shard": shard,
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / fwd_ms / 1e9, 1),
                 "pct_peak": round(100 * fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)},

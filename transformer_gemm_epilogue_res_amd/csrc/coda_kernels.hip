@@ -714,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
     p.B = static_cast<const char*>(p0.B) + 2 * (B_K ? k0 : k0 * p0.ldb);
   }
   int tile_m, tile_n;
-  map_tile(p.M, p.N, tile_m, tile_n);
+  map_tile(p.M, p.N, p.group_m, tile_m, tile_n);
   const int64_t m0 = int64_t(tile_m) * kBM, n0 = int64_t(tile_n) * kBN;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1288,6 +1288,11 @@ hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, h
   return hipGetLastError();
 }
 
+// Raster of the data-gradient GEMM (both operands k-contiguous, contraction over N): an
+// XCD's 32 concurrent tiles as 8 tile-rows x 4 tile-columns ran it about 1.5 % faster than
+// the 4 x 8 of the other GEMMs, which in turn suits those better.
+constexpr int kDgradGroupM = 8;
+
 // The data gradient with its RMSNorm-backward epilogue; with few rows (dgrad_split) the
 // contraction is split over S block rows into fp32 partials `part` and a row kernel finishes.
 hipError_t bwd_dgrad(const coda_bwd_args_t* a, float* Pg, float* part, hipStream_t st) {
@@ -1307,7 +1312,7 @@ hipError_t bwd_dgrad(const coda_bwd_args_t* a, float* Pg, float* part, hipStream
                          (const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D);
     return hipGetLastError();
   }
-  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
+  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N, 0, kDgradGroupM};
   if (a->da_dtype == CODA_F32)
     return launch_gemm<true, true>(pd, EpiRmsNormBwd<true>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
   return launch_gemm<true, true>(pd, EpiRmsNormBwd<false>{(const uint16_t*)a->h, a->r, a->s, (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D}, st);
@@ -1484,7 +1489,7 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
   float* Pg = reinterpret_cast<float*>(ws_at(ws, 2 * md));
   hipError_t e = bwd_rowstat_rows(a, gr, st);
   if (e != hipSuccess) return CODA_ERR_HIP;
-  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N};
+  const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N, 0, kDgradGroupM};
   if ((e = gemm_plain(pd, true, true, G, a->D, false, st)) != hipSuccess) return CODA_ERR_HIP;
   const dim3 grid(unsigned(ceil_div(a->D, 2048)), unsigned(ceil_div(a->M, kUnfusedBwdRows)));
   if (a->da_dtype == CODA_F32)

@@ -293,17 +293,20 @@ __device__ __forceinline__ void prio_low() { asm volatile("s_setprio 0" ::: "mem
 
 // Block -> output tile. Consecutive logical tiles go to one XCD (the
 // dispatcher deals blocks round-robin over the 8 XCDs); logical tiles are
-// rastered down groups of kGroupM tile-rows.
+// rastered down groups of group_m tile-rows (kGroupM unless the launch names
+// another), so at any time an XCD's 32 CUs hold a group_m x (32 / group_m)
+// block of tiles.
 constexpr int kGroupM = CODA_GROUP_M;
-__device__ __forceinline__ void map_tile(int64_t M, int64_t N, int& tile_m, int& tile_n) {
+__device__ __forceinline__ void map_tile(int64_t M, int64_t N, int group_m, int& tile_m, int& tile_n) {
   const int tiles_m = int(dceil_div(M, kBM));
   const int tiles_n = int(N / kBN);
   const int nb = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + (b / 8) : b;
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (t / per_group) * kGroupM;
-  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int gm = group_m > 0 ? group_m : kGroupM;
+  const int per_group = gm * tiles_n;
+  const int first_m = (t / per_group) * gm;
+  const int gsz = min(tiles_m - first_m, gm);
   const int r = t % per_group;
   tile_m = first_m + r % gsz;
   tile_n = r / gsz;
@@ -316,6 +319,7 @@ struct GemmShape {
   const void* B;    // B_K: [N, ldb] (k contiguous); else [K, ldb] (n contiguous)
   int64_t ldb;
   int64_t kslice;   // split-K: block row blockIdx.y contracts k in [y kslice, (y + 1) kslice); 0 = no split
+  int group_m = 0;  // tile-rows per raster group (map_tile); 0 = kGroupM
 };
 
 // One wave's view of the loop. The A tile of K step s lives in A slot s % 3,
