@@ -84,8 +84,9 @@ inline size_t fwd_ws(int64_t M, int64_t D) {
   const int64_t S = gemm0_split_max(M, D);
   return fwd_ws_p(M, D) + (S > 1 ? align256(size_t(S) * size_t(M) * size_t(D) * 4) : 0);
 }
-// Row group of the split-K reduction kernel (its dgamma partials have ceil(M / 32) rows).
-constexpr int kSplitRows = 32;
+// Row group of the split-K reduction kernel (its dgamma partials have ceil(M / 8) rows):
+// small enough that a shard's rows give the kernel several blocks per CU.
+constexpr int kSplitRows = 8;
 inline int64_t bwd_pg_rows(int64_t M, int64_t D, int64_t N) {
   return dgrad_split(M, D, N).S > 1 ? ceil_div(M, kSplitRows) : dgamma_rows(M);
 }

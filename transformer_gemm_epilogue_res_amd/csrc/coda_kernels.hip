@@ -1028,15 +1028,15 @@ __global__ __launch_bounds__(256) void splitk_rmsnorm_bwd_kernel(const float* pa
   float gm[4], cs[4] = {0.f, 0.f, 0.f, 0.f};
   unpack4_bf16(*reinterpret_cast<const uint2*>(gamma + j), gm);
   for (int64_t i = i0; i < i1; ++i) {
-    float G[4];
-    {
-      const float4 v = *reinterpret_cast<const float4*>(part + i * D + j);
-      G[0] = v.x, G[1] = v.y, G[2] = v.z, G[3] = v.w;
-    }
-    for (int t = 1; t < S; ++t) {
-      const float4 v = *reinterpret_cast<const float4*>(part + t * sstride + i * D + j);
-      G[0] += v.x, G[1] += v.y, G[2] += v.z, G[3] += v.w;
-    }
+    // all S slices' loads of the row in flight before the fixed-order sum (S <= 8)
+    float4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (t < S) v[t] = *reinterpret_cast<const float4*>(part + t * sstride + i * D + j);
+    float G[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+    for (int t = 1; t < 8; ++t)
+      if (t < S) G[0] += v[t].x, G[1] += v[t].y, G[2] += v[t].z, G[3] += v[t].w;
     float hv[4], d[4];
     unpack4_bf16(*reinterpret_cast<const uint2*>(h + i * D + j), hv);
     const float ri = r[i], c2 = s[i] * ri * ri * invD;
