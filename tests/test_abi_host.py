@@ -97,12 +97,12 @@ def test_workspace_sizes():
     def gr_bytes(M, D):  # bf16(r g) transposed, [D, M rounded up to 64]
         return a256(D * math.ceil(M / 64) * 64 * 2)
     assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == (
-        gr_bytes(M, D) + a256(math.ceil(M / 32) * D * 4) + a256(S * M * D * 4))
+        gr_bytes(M, D) + a256(math.ceil(M / 8) * D * 4) + a256(S * M * D * 4))
     assert dgrad_split(8192, 4096, 28672) == (1, 0)  # the Llama-3-8B step: 512 tiles, no split
     assert L.workspace_bytes(L.CODA_OP_BWD, 8192, 4096, 28672) == a256(8192 * 4096 * 2) + a256(64 * 4096 * 4)
     assert dgrad_split(1024, 4096, 28672) == (4, 7168)  # a data-parallel shard: 64 tiles -> 4 slices
     assert L.workspace_bytes(L.CODA_OP_BWD, 1024, 4096, 28672) == (
-        a256(1024 * 4096 * 2) + a256(32 * 4096 * 4) + a256(4 * 1024 * 4096 * 4))
+        a256(1024 * 4096 * 2) + a256(1024 // 8 * 4096 * 4) + a256(4 * 1024 * 4096 * 4))  # dgamma partials of 8-row groups
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD, M, D, N) == 2 * a256(M * D * 2)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD, 0, D, N) == 0
@@ -110,7 +110,7 @@ def test_workspace_sizes():
     N2 = 1024  # SwiGLU needs N % 512 == 0; its backward adds the s partials Ps[M, (N/2)/64]
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
     S2, _ = dgrad_split(M, D, N2)
-    bwd2 = gr_bytes(M, D) + a256(math.ceil(M / (32 if S2 > 1 else 128)) * D * 4) + (a256(S2 * M * D * 4) if S2 > 1 else 0)
+    bwd2 = gr_bytes(M, D) + a256(math.ceil(M / (8 if S2 > 1 else 128)) * D * 4) + (a256(S2 * M * D * 4) if S2 > 1 else 0)
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2 // 64) * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0

@@ -787,9 +787,17 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
 // One 512-thread block per row i: s_i = sum_n dY_in y_in (fp32) and, with GR (the
 // unfused baseline's row layout), gr_i = bf16(r_i g_i). The row is read in rounds of kRowUnroll x 16 bytes per
 // thread of each input, all loads of a round issued before any is used (one
-// round covers an N = 28672 row).
+// round covers an N = 28672 row); dY and y are read non-temporally (about 6 % faster
+// at the 8B shape).
 constexpr int kRowThreads = 512;
 constexpr int kRowUnroll = 7;
+
+// 16 bytes of a stream read once (non-temporal: it need not displace cached data that
+// later kernels read again, e.g. the weights and h of the data-gradient GEMM).
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
 template <bool GR>
 __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY, const uint16_t* y,
                                                               const uint16_t* g, const float* r, float* s,
@@ -818,8 +826,8 @@ __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
       const int64_t v = base + u * kRowThreads;
-      va[u] = v < n8 ? a[v] : make_uint4(0, 0, 0, 0);
-      vb[u] = v < n8 ? b[v] : make_uint4(0, 0, 0, 0);
+      va[u] = v < n8 ? load_once(a + v) : make_uint4(0, 0, 0, 0);
+      vb[u] = v < n8 ? load_once(b + v) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
