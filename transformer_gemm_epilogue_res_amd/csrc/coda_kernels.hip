@@ -74,6 +74,8 @@ struct StageBf16 {
   }
   // Staged rows to rows mb .. mb+127 (those below M) of out, row stride ldb
   // bytes, starting at byte column cb.
+  // NT: non-temporal stores (for an output no kernel reads again soon)
+  template <bool NT = false>
   __device__ __forceinline__ void flush_raw(char* out, int64_t ldb, int64_t mb, int64_t cb, int64_t M) const {
     const int c = lane & 7;
 #pragma unroll
@@ -81,12 +83,17 @@ struct StageBf16 {
       const int row = 8 * q + (lane >> 3);
       const u32x4_t v = *reinterpret_cast<const LDS_AS u32x4_t*>(base + row * 128 + ((c ^ (row & 7)) << 4));
       const int64_t i = mb + row;
-      if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldb + cb + 16 * c) = v;
+      if (i < M) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + i * ldb + cb + 16 * c);
+        if constexpr (NT) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+      }
     }
   }
   // Rows mb .. mb+127 (those below M), columns nb .. nb+63 of out[., ldc].
+  template <bool NT = false>
   __device__ __forceinline__ void flush(uint16_t* out, int64_t ldc, int64_t mb, int64_t nb, int64_t M) const {
-    flush_raw(reinterpret_cast<char*>(out), 2 * ldc, mb, 2 * nb, M);
+    flush_raw<NT>(reinterpret_cast<char*>(out), 2 * ldc, mb, 2 * nb, M);
   }
   // The reverse of flush: rows mb .. mb+127 (0 past M), columns nb .. nb+63 of src[., ldc] into
   // the staging area with whole-row 16-byte loads; get() then returns a lane's four values.
@@ -166,7 +173,7 @@ __device__ __forceinline__ void store_f32(float* out, int64_t ldc, int64_t mb, i
 }
 
 // Writes the wave's block val(tm, tn) as bf16 (staged) or fp32 (direct).
-template <bool F32, class V>
+template <bool F32, bool NT = false, class V>
 __device__ __forceinline__ void store_block(lds_char_t* stage, int lane, void* out, int64_t ldc, int64_t mb,
                                             int64_t nb, int64_t M, V&& val) {
   if constexpr (F32) {
@@ -180,7 +187,7 @@ __device__ __forceinline__ void store_block(lds_char_t* stage, int lane, void* o
     for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < kTN; ++tn) st.put(tm, tn, val(tm, tn));
-    st.flush(static_cast<uint16_t*>(out), ldc, mb, nb, M);
+    st.template flush<NT>(static_cast<uint16_t*>(out), ldc, mb, nb, M);
   }
 }
 
@@ -323,7 +330,9 @@ struct EpiRowScale {
     float rr[kTM];
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
-    store_block<F32>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
+    // y non-temporally: the forward does not read it again, and the backward's row-statistic
+    // pass reads it from HBM faster this way (about 30 us less at the 8B shape)
+    store_block<F32, true>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
       f32x4_t v = acc[tm][tn];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] *= rr[tm];
