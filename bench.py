@@ -226,8 +226,8 @@ def main():
         B.run(sp)
     torch.cuda.synchronize()
 
-    # The timed region: K whole steps back to back, HIP events only at its two ends (an
-    # event marker between kernels holds the next dispatch back by several microseconds).
+    # The timed region: K whole steps back to back, HIP events only at its two ends (no
+    # marker between the step's kernels; under the profiler each one delays the next dispatch).
     log(f"[bench] timing {args.steps} steps")
     t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
