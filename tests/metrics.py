@@ -89,17 +89,23 @@ def bf16_one_ulp(x, ref) -> float:
     return float(np.max(np.abs(x - ref) / (bf16_ulp(ref) + 1e-6 * rms(ref))))
 
 
-def operand_rounding_allowance(g, r, dY, cols=None, dY_rounded=False) -> np.ndarray:
+def operand_rounding_allowance(g, r, dY, cols=None, dY_rounded=False, chunk=65536) -> np.ndarray:
     """[D, C] bound sum_i ulp(r_i g_ij)/2 |dY_in| for the sampled columns n; with
     dY_rounded (dY itself rounded to bf16 before the product, from an exact value)
-    also sum_i |r_i g_ij| ulp(dY_in)/2."""
-    rg = f64(g) * f64(r)[:, None]
-    d = f64(dY)
-    if cols is not None:
-        d = d[:, np.asarray(cols)]
-    allow = (0.5 * bf16_ulp(rg)).T @ np.abs(d)
-    if dY_rounded:
-        allow += np.abs(rg).T @ (0.5 * bf16_ulp(d))
+    also sum_i |r_i g_ij| ulp(dY_in)/2. Accumulated over blocks of rows."""
+    if cols is None:
+        dYc = dY
+    else:
+        idx = np.asarray(cols)
+        dYc = dY[:, idx] if isinstance(dY, np.ndarray) else dY[:, torch.as_tensor(idx)]
+    allow = None
+    for i0 in range(0, g.shape[0], chunk):
+        rg = f64(g[i0:i0 + chunk]) * f64(r[i0:i0 + chunk])[:, None]
+        d = f64(dYc[i0:i0 + chunk])
+        a = (0.5 * bf16_ulp(rg)).T @ np.abs(d)
+        if dY_rounded:
+            a += np.abs(rg).T @ (0.5 * bf16_ulp(d))
+        allow = a if allow is None else allow + a
     return allow
 
 

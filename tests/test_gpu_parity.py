@@ -167,9 +167,10 @@ def run_bwd_both(dev, unfused=False):
     return o32, o16
 
 
-def check_bwd(o32, o16, host, rows=None, jcols=None, ncols=None, unfused=False):
-    ref = orc.backward(host["dY"], host["y"], host["h"], host["g"], host["r"], host["gamma"], host["W1"],
-                       rows=rows, dgamma_cols=jcols, dw1_cols=ncols)
+def check_bwd(o32, o16, host, rows=None, jcols=None, ncols=None, unfused=False, ref=None, allow=None):
+    if ref is None:
+        ref = orc.backward(host["dY"], host["y"], host["h"], host["g"], host["r"], host["gamma"], host["W1"],
+                           rows=rows, dgamma_cols=jcols, dw1_cols=ncols)
 
     def rsel(t):
         return t.cpu() if rows is None else t.index_select(0, torch.as_tensor(rows, device=t.device)).cpu()
@@ -185,7 +186,8 @@ def check_bwd(o32, o16, host, rows=None, jcols=None, ncols=None, unfused=False):
     assert torch.equal(mt.rne_bf16(da).view(torch.int16), rsel(o16["da"]).view(torch.int16))
     assert torch.equal(mt.rne_bf16(dW1).view(torch.int16), csel(o16["dW1"], ncols).view(torch.int16))
     assert torch.equal(rsel(o16["s"]), s) and torch.equal(csel(o16["dgamma"], jcols), dg)
-    allow = mt.operand_rounding_allowance(host["g"], host["r"], host["dY"], ncols)
+    if allow is None:
+        allow = mt.operand_rounding_allowance(host["g"], host["r"], host["dY"], ncols)
     e_w = mt.within_allowance(dW1, ref["dW1"], allow)
     print(f"  dW1 |d| / (1e-2 rms + operand-rounding bound) max = {e_w:.3f}")
     assert e["s"] <= mt.S_TOL
@@ -226,6 +228,63 @@ def test_bwd_llama_shapes_sampled(name):
     ncols = inputs.sample(c["N"], 256, 0, "dw1_cols").numpy()
     o32, o16 = run_bwd_both(to_dev(host))
     check_bwd(o32, o16, host, rows=rows, jcols=jcols, ncols=ncols)
+
+
+# ---------------------------------------------------------- the largest row count
+
+MAX_ROWS = 1 << 22  # the entry points reject more rows (host validation)
+
+
+def test_max_rows_forward_and_backward():
+    """M = 2^22 rows, the largest the entry points accept, at the smallest widths: every launch
+    at its largest grid (one block per row, 65536 row blocks of the transposed operand, 16384
+    tile rows, the unfused kernels' 131072 row groups) and byte offsets past 2^31; forward and
+    backward, fused and unfused. The inputs (2 GB each) are drawn on the device; the forward is
+    checked on 256 sampled rows, the backward (on a saved set drawn directly, since its formulas
+    hold for any saved tensors) on every row where dY is not zero and on every column."""
+    M, K0, D, N = MAX_ROWS, 256, 256, 256
+    announce(f"coda_fwd / coda_bwd M={M} K0={K0} D={D} N={N} seed=0, fused and unfused, sampled")
+    dev = {"x": inputs.device_randn_bf16((M, K0), 0, "x", DEV),
+           "z": inputs.device_randn_bf16((M, D), 0, "z", DEV),
+           "W0": inputs.device_randn_bf16((K0, D), 0, "W0", DEV, scale=K0 ** -0.5),
+           "gamma": inputs.device_randn_bf16((D,), 0, "gamma", DEV, scale=0.1, shift=1.0),
+           "W1": inputs.device_randn_bf16((D, N), 0, "W1", DEV, scale=D ** -0.5)}
+    rows = inputs.sample(M, 256, 0, "rows").numpy()
+    ridx = torch.as_tensor(rows, device=DEV)
+    gamma, W1 = dev["gamma"].cpu(), dev["W1"].cpu()
+    ref = orc.forward(dev["x"].index_select(0, ridx).cpu(), dev["W0"].cpu(), dev["z"].index_select(0, ridx).cpu(),
+                      gamma, W1, EPS)
+    for unfused in (False, True):
+        o32, o16 = run_fwd_both(dev, unfused=unfused)
+        check_fwd(o32, o16, ref, gamma, rows=rows, unfused=unfused)
+        del o32, o16
+    del dev["x"], dev["z"]
+    torch.cuda.empty_cache()
+    # dY is zero outside a seeded set of rows spread over the whole range (and the last 64), so
+    # dgamma and dW1, sums over all rows, are exactly the sums over those rows; the kernels still
+    # run over all 2^22 rows, and on the zero rows s and da must come out exactly 0.
+    R = np.union1d(inputs.sample(M, 4096, 0, "rows").numpy(), np.arange(M - 64, M))
+    Ridx = torch.as_tensor(R, device=DEV)
+    dY = torch.zeros(M, N, dtype=torch.bfloat16, device=DEV)
+    dY.index_copy_(0, Ridx, inputs.device_randn_bf16((len(R), N), 0, "dY", DEV))
+    dev.update(dY=dY,
+               y=inputs.device_randn_bf16((M, N), 0, "y_s", DEV),
+               h=inputs.device_randn_bf16((M, D), 0, "h_s", DEV, scale=2 ** 0.5),
+               g=inputs.device_randn_bf16((M, D), 0, "g_s", DEV, scale=2 ** 0.5),
+               r=inputs.device_uniform_f32((M,), 0, "r_s", DEV, 0.5, 1.0))
+    sub = {k: dev[k].index_select(0, Ridx).cpu() for k in ("dY", "y", "h", "g", "r")}
+    sub.update(gamma=gamma, W1=W1)
+    ref_b = orc.backward(sub["dY"], sub["y"], sub["h"], sub["g"], sub["r"], gamma, W1)
+    allow = mt.operand_rounding_allowance(sub["g"], sub["r"], sub["dY"])
+    zero_rows = torch.as_tensor(np.setdiff1d(inputs.sample(M, 256, 1, "rows").numpy(), R), device=DEV)
+    assert zero_rows.numel() > 200
+    for unfused in (False, True):
+        o32, o16 = run_bwd_both(dev, unfused=unfused)
+        check_bwd(o32, o16, sub, rows=R, unfused=unfused, ref=ref_b, allow=allow)
+        for o in (o32, o16):
+            assert not o["s"].index_select(0, zero_rows).any()
+            assert not o["da"].index_select(0, zero_rows).any()
+        del o32, o16
 
 
 # --------------------------------------------- backward through the first GEMM

@@ -1201,9 +1201,9 @@ template <bool F32>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* G, const uint16_t* h, const float* r,
                                                           const float* s, const uint16_t* gamma, void* da,
                                                           float* Pg, int64_t M, int64_t D) {
-  const int64_t j = int64_t(blockIdx.x) * 2048 + threadIdx.x * 8;
+  const int64_t j = int64_t(blockIdx.y) * 2048 + threadIdx.x * 8;
   if (j >= D) return;
-  const int64_t i0 = int64_t(blockIdx.y) * kUnfusedBwdRows;
+  const int64_t i0 = int64_t(blockIdx.x) * kUnfusedBwdRows;  // row groups on x: up to 2^31 - 1 blocks
   const float invD = 1.0f / float(D);
   float gm[8], cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   unpack8_bf16(*reinterpret_cast<const uint4*>(gamma + j), gm);
@@ -1226,7 +1226,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* G, con
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(da) + i * D + j) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   }
-  float4* o = reinterpret_cast<float4*>(Pg + int64_t(blockIdx.y) * D + j);
+  float4* o = reinterpret_cast<float4*>(Pg + int64_t(blockIdx.x) * D + j);
   o[0] = make_float4(cs[0], cs[1], cs[2], cs[3]);
   o[1] = make_float4(cs[4], cs[5], cs[6], cs[7]);
 }
@@ -1260,7 +1260,7 @@ char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 // s and bf16(r * g), then the weight gradient dW1 = bf16(r g)^T @ dY.
 // bf16(r g) transposed into grT [D, gr_cols(M)] for the weight-gradient GEMM.
 hipError_t gr_transpose(const uint16_t* g, const float* r, uint16_t* grT, int64_t M, int64_t D, hipStream_t st) {
-  const int64_t ldt = gr_cols(M);
+  const int64_t ldt = gr_cols(M);  // ldt / 64 <= 2^22 / 64 = 65536 blocks, the device's grid-y limit
   hipLaunchKernelGGL(gr_transpose_kernel, dim3(unsigned(D / 64), unsigned(ldt / 64)), dim3(256), 0, st, g, r, grT, M, D,
                      ldt);
   return hipGetLastError();
@@ -1508,7 +1508,7 @@ coda_status_t coda_unfused_ref(coda_op_t op, const void* args, void* ws, size_t 
   if (e != hipSuccess) return CODA_ERR_HIP;
   const GemmShape pd{a->M, a->D, a->N, a->dY, a->N, a->W1, a->N, 0, kDgradGroupM};
   if ((e = gemm_plain(pd, true, true, G, a->D, false, st)) != hipSuccess) return CODA_ERR_HIP;
-  const dim3 grid(unsigned(ceil_div(a->D, 2048)), unsigned(ceil_div(a->M, kUnfusedBwdRows)));
+  const dim3 grid(unsigned(ceil_div(a->M, kUnfusedBwdRows)), unsigned(ceil_div(a->D, 2048)));
   if (a->da_dtype == CODA_F32)
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<true>, grid, dim3(256), 0, st, G, (const uint16_t*)a->h, a->r, a->s,
                        (const uint16_t*)a->gamma, a->da, Pg, a->M, a->D);

@@ -35,7 +35,9 @@ EPS = 1e-5
 IDS = {"x": 1, "W0": 2, "z": 3, "gamma": 4, "W1": 5, "dY": 6,
        "rows": 7, "dgamma_cols": 8, "dw1_cols": 9, "dh": 10, "dw0_cols": 11,
        "W2": 12, "dOut": 13, "dw2_cols": 14,
-       "h_lm": 15, "W_lm": 16, "targets": 17, "dloss": 18, "ignored": 19, "dw_lm_rows": 20}
+       "h_lm": 15, "W_lm": 16, "targets": 17, "dloss": 18, "ignored": 19, "dw_lm_rows": 20,
+       # the largest-row-count case: the backward's saved set drawn directly (not from a forward)
+       "h_s": 21, "g_s": 22, "y_s": 23, "r_s": 24}
 
 # name -> (M tokens, K0, D, N = 2 * ffn); the LM head of each model has V = 128256 outputs
 LM_VOCAB = 128256
@@ -53,6 +55,21 @@ def generator(seed: int, name: str) -> torch.Generator:
     g = torch.Generator(device="cpu")
     g.manual_seed(seed * 100 + IDS[name])
     return g
+
+
+def device_randn_bf16(shape, seed: int, name: str, device, scale: float = 1.0, shift: float = 0.0) -> torch.Tensor:
+    """The same recipe drawn by a generator on ``device`` (for tensors too large to draw on the host;
+    its stream differs from the host generator's)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 100 + IDS[name])
+    return (torch.randn(*shape, generator=g, device=device, dtype=torch.float32) * scale + shift).to(torch.bfloat16)
+
+
+def device_uniform_f32(shape, seed: int, name: str, device, lo: float, hi: float) -> torch.Tensor:
+    """Seeded fp32 U(lo, hi) drawn on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 100 + IDS[name])
+    return torch.rand(*shape, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
 
 
 def _randn_bf16(shape, seed, name, scale=1.0, shift=0.0):
