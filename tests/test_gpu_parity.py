@@ -287,6 +287,38 @@ def test_max_rows_forward_and_backward():
         del o32, o16
 
 
+MAX_DIM = 1 << 20  # the entry points reject wider K0, D or N (host validation)
+MAX_WIDTH = {"N": dict(M=256, K0=256, D=256, N=MAX_DIM), "D": dict(M=256, K0=256, D=MAX_DIM, N=256)}
+
+
+@pytest.mark.parametrize("name", list(MAX_WIDTH))
+def test_max_width_forward_and_backward(name):
+    """The widest D or N the entry points accept (2^20): the longest row loops (the row statistics
+    over 2^20 columns, the sums of squares over 16384 partials per row), contractions of 16384 K
+    steps and 4096 tile columns; forward on 16 sampled rows, backward (on a saved set drawn directly)
+    on 16 rows, 8 dgamma columns and 8 dW1 columns."""
+    c = MAX_WIDTH[name]
+    M, K0, D, N = c["M"], c["K0"], c["D"], c["N"]
+    announce(f"coda_fwd / coda_bwd max {name}: M={M} K0={K0} D={D} N={N} seed=0, sampled")
+    inp = inputs.forward_inputs(M, K0, D, N, seed=0)
+    rows = inputs.sample(M, 16, 0, "rows").numpy()
+    dev = to_dev(inp)
+    ref = orc.forward(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, rows=rows)
+    o32, o16 = run_fwd_both(dev)
+    check_fwd(o32, o16, ref, inp["gamma"], rows=rows)
+    del o32, o16, ref
+    host = {"dY": inputs.output_grad(M, N, seed=0),
+            "y": inputs.device_randn_bf16((M, N), 0, "y_s", DEV).cpu(),
+            "h": inputs.device_randn_bf16((M, D), 0, "h_s", DEV, scale=2 ** 0.5).cpu(),
+            "g": inputs.device_randn_bf16((M, D), 0, "g_s", DEV, scale=2 ** 0.5).cpu(),
+            "r": inputs.device_uniform_f32((M,), 0, "r_s", DEV, 0.5, 1.0).cpu(),
+            "gamma": inp["gamma"], "W1": inp["W1"]}
+    jcols = inputs.sample(D, 8, 0, "dgamma_cols").numpy()
+    ncols = inputs.sample(N, 8, 0, "dw1_cols").numpy()
+    o32, o16 = run_bwd_both(to_dev(host))
+    check_bwd(o32, o16, host, rows=rows, jcols=jcols, ncols=ncols)
+
+
 # --------------------------------------------- backward through the first GEMM
 
 BWD0_SMALL = {
