@@ -19,6 +19,9 @@ expectations" paragraph, and the kucoin article, "experimental results"):
 * LM head: h ~ N(0, 1) (a normalised hidden state), W [V, D] ~ N(0, 4/D) (logits
   of standard deviation 2: a peaked softmax), targets uniform in [0, V) with about
   3 % of the rows set to -100 (ignored), dloss ~ N(0, 1) fp32 per row;
+* for the largest row count and the widest D or N, a backward saved set drawn directly
+  (ids h=21, g=22, y=23, r=24): h, g ~ N(0, 2) and y ~ N(0, 1) in bf16, r ~ U(0.5, 1)
+  in fp32; tensors of 2^30 elements are drawn by a seeded generator on the device;
 * eps = 1e-5.
 
 W1's columns are read as interleaved gate/up pairs (column 2f = gate f,
