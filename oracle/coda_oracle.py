@@ -146,11 +146,6 @@ def forward(x, W0, z, gamma, W1, eps: float, rows=None, chunk: int = 1024) -> di
     return {k: np.concatenate(v, axis=0) for k, v in out.items()}
 
 
-def row_statistic(dY, y, rows=None) -> np.ndarray:
-    """s_i = sum over columns of dY_in * y_in for the given rows."""
-    return (_take(dY, rows) * _take(y, rows)).sum(axis=1)
-
-
 def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=None) -> dict:
     """Backward of the chain for the saved set (h, g, y, r).
 

@@ -138,6 +138,50 @@ def test_backward_brute_force_derivative(seed):
     assert _relerr(b["G"], dY @ W1.T) == 0.0
 
 
+# ------------------------------------------------------------- plain product
+
+def _bf16_dyadics(shape, seed):
+    """bf16 tensor of m * 2^e with |m| < 256 (8 significant bits, exact in bf16), e in [-4, 4]."""
+    g = np.random.default_rng(seed)
+    m = g.integers(-255, 256, size=shape).astype(np.float64)
+    e = g.integers(-4, 5, size=shape).astype(np.float64)
+    t = torch.from_numpy(m * 2.0 ** e).to(torch.bfloat16)
+    assert torch.equal(t.double(), torch.from_numpy(m * 2.0 ** e))   # exactly representable
+    return t
+
+
+def _fraction_product(A, B):
+    a = [[Fraction(float(v)) for v in row] for row in A.double().tolist()]
+    b = [[Fraction(float(v)) for v in row] for row in B.double().tolist()]
+    return np.array([[float(sum(a[i][k] * b[k][j] for k in range(len(b)))) for j in range(len(b[0]))]
+                     for i in range(len(a))])
+
+
+@pytest.mark.parametrize("a_col", [False, True], ids=["A_row", "A_col"])
+@pytest.mark.parametrize("b_col", [False, True], ids=["B_row", "B_col"])
+@pytest.mark.parametrize("shape", [(3, 5, 2), (7, 4, 6)])
+def test_gemm_exact_in_every_storage_layout(a_col, b_col, shape):
+    """oracle.gemm (the checker of the plain-mainloop GPU test) is the exact product A @ B of the
+    logical operands, whichever way they are stored: a row-major tensor, or the transposed view of a
+    column-major one. The sizes differ pairwise, so a transposed operand or a wrong contraction axis
+    fails on shape or value; the operands carry 8 significant bits at exponents -4..4, so a widening
+    that drops mantissa bits or sign changes the exact rational result (every partial sum is exact in
+    fp64, so the comparison is equality)."""
+    M, K, N = shape
+    A = _bf16_dyadics((M, K), 100 + M)
+    B = _bf16_dyadics((K, N), 200 + N)
+    A_view = A.t().contiguous().t() if a_col else A          # stored [K, M], read as its transpose
+    B_view = B.t().contiguous().t() if b_col else B          # stored [N, K], read as its transpose
+    assert A_view.is_contiguous() == (not a_col) and B_view.is_contiguous() == (not b_col)
+    want = _fraction_product(A, B)
+    got = orc.gemm(A_view, B_view)
+    assert got.shape == (M, N)
+    assert np.array_equal(got, want)
+    assert np.array_equal(orc.gemm(A.double().numpy(), B.double().numpy()), want)   # ndarray inputs
+    with pytest.raises(ValueError):
+        orc.gemm(A_view, B_view.t())                           # a transposed B cannot multiply
+
+
 # --------------------------------------------------------- library special case
 
 def _rand_problem(M, K0, D, N, seed, eps=1e-5):
