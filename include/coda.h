@@ -58,6 +58,13 @@
 extern "C" {
 #endif
 
+/* Every enum below also names the smallest and largest int32 (the *_RANGE_MIN_ / *_RANGE_MAX_
+ * sentinels, which no function accepts): that fixes each enum's range to all of int32, so any int a C
+ * caller passes (e.g. through ctypes) is a defined value of the type, and the validators reject it
+ * with CODA_ERR_ARG instead of the C++ implementation reading an out-of-range enum. */
+#define CODA_ENUM_MIN_ (-0x7fffffff - 1)
+#define CODA_ENUM_MAX_ 0x7fffffff
+
 typedef enum {
   CODA_OK = 0,
   CODA_ERR_NULL = 1,      /* a required pointer is NULL                      */
@@ -65,10 +72,15 @@ typedef enum {
   CODA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                */
   CODA_ERR_WORKSPACE = 4, /* workspace NULL or smaller than required          */
   CODA_ERR_ARG = 5,       /* bad scalar argument (eps, dtype, op, layout)     */
-  CODA_ERR_HIP = 6        /* a HIP launch failed                              */
+  CODA_ERR_HIP = 6,       /* a HIP launch failed                              */
+  CODA_STATUS_RANGE_MIN_ = CODA_ENUM_MIN_, CODA_STATUS_RANGE_MAX_ = CODA_ENUM_MAX_
 } coda_status_t;
 
-typedef enum { CODA_BF16 = 0, CODA_F32 = 1 } coda_dtype_t;
+typedef enum {
+  CODA_BF16 = 0,
+  CODA_F32 = 1,
+  CODA_DTYPE_RANGE_MIN_ = CODA_ENUM_MIN_, CODA_DTYPE_RANGE_MAX_ = CODA_ENUM_MAX_
+} coda_dtype_t;
 
 /* Operations, for coda_workspace_bytes. */
 typedef enum {
@@ -83,7 +95,8 @@ typedef enum {
   CODA_OP_UNFUSED_FWD_SWIGLU = 8, /* coda_unfused_ref(CODA_OP_FWD_SWIGLU) */
   CODA_OP_UNFUSED_BWD_SWIGLU = 9, /* coda_unfused_ref(CODA_OP_BWD_SWIGLU) */
   CODA_OP_UNFUSED_CE_FWD = 10,    /* coda_unfused_ref(CODA_OP_CE_FWD) (V as N) */
-  CODA_OP_UNFUSED_CE_BWD = 11     /* coda_unfused_ref(CODA_OP_CE_BWD) (V as N) */
+  CODA_OP_UNFUSED_CE_BWD = 11,    /* coda_unfused_ref(CODA_OP_CE_BWD) (V as N) */
+  CODA_OP_RANGE_MIN_ = CODA_ENUM_MIN_, CODA_OP_RANGE_MAX_ = CODA_ENUM_MAX_
 } coda_op_t;
 
 /* Forward arguments.
@@ -264,7 +277,8 @@ typedef struct {
 /* Operand layouts for coda_gemm. */
 typedef enum {
   CODA_ROW = 0, /* A: element (m,k) at A[m*lda + k];  B: element (k,n) at B[k*ldb + n] */
-  CODA_COL = 1  /* A: element (m,k) at A[k*lda + m];  B: element (k,n) at B[n*ldb + k] */
+  CODA_COL = 1, /* A: element (m,k) at A[k*lda + m];  B: element (k,n) at B[n*ldb + k] */
+  CODA_LAYOUT_RANGE_MIN_ = CODA_ENUM_MIN_, CODA_LAYOUT_RANGE_MAX_ = CODA_ENUM_MAX_
 } coda_layout_t;
 
 /* Plain GEMM C[M,N] = A[M,K] @ B[K,N] with bf16 operands and fp32 accumulation,

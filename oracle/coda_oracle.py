@@ -286,6 +286,24 @@ def lm_head_cross_entropy(h, W, targets, rows=None, chunk: int = 512) -> dict:
     return {k: np.concatenate(v) for k, v in out.items()}
 
 
+def lm_head_dlogits(h, W, targets, lse, dloss, rows=None, vcols=None) -> np.ndarray:
+    """dlogits_iv = dloss_i (exp(logits_iv - lse_i) - [v = t_i]) for the given rows i and vocabulary
+    columns v (all when None), 0 on ignored rows, from the logits h @ W^T recomputed in float64 and the
+    saved lse."""
+    Wd = f64(W)
+    t = np.asarray(targets, dtype=np.int64) if not hasattr(targets, "numpy") else targets.numpy().astype(np.int64)
+    lse_d, dl = f64(lse), f64(dloss)
+    V = Wd.shape[0]
+    sel = np.arange(len(t)) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(V) if vcols is None else np.asarray(vcols, dtype=np.int64)
+    L = _take(h, sel) @ Wd[cols].T
+    P = np.exp(L - lse_d[sel, None])
+    tv = t[sel]
+    valid = (tv >= 0) & (tv < V)
+    onehot = (cols[None, :] == tv[:, None]).astype(np.float64)
+    return np.where(valid[:, None], dl[sel, None] * (P - onehot), 0.0)
+
+
 def lm_head_cross_entropy_backward(h, W, targets, lse, dloss, rows=None, dw_rows=None, chunk: int = 512) -> dict:
     """Backward of L = sum_i dloss_i loss_i for the saved lse [M]:
 
@@ -293,27 +311,15 @@ def lm_head_cross_entropy_backward(h, W, targets, lse, dloss, rows=None, dw_rows
     * ``dw_rows``: vocabulary rows v of dW [*, D] (sums over *all* M rows; all when None).
     """
     Wd = f64(W)
-    t = np.asarray(targets, dtype=np.int64) if not hasattr(targets, "numpy") else targets.numpy().astype(np.int64)
-    lse_d, dl = f64(lse), f64(dloss)
-    M, V = len(t), Wd.shape[0]
-
-    def dlogits(sel, vcols=None):
-        Wc = Wd if vcols is None else Wd[vcols]
-        L = _take(h, sel) @ Wc.T
-        P = np.exp(L - lse_d[sel, None])
-        tv = t[sel]
-        valid = (tv >= 0) & (tv < V)
-        cols = np.arange(V) if vcols is None else np.asarray(vcols)
-        onehot = (cols[None, :] == tv[:, None]).astype(np.float64)
-        return np.where(valid[:, None], dl[sel, None] * (P - onehot), 0.0)
-
+    M, V = len(targets), Wd.shape[0]
     idx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
-    dL = np.concatenate([dlogits(idx[c0:c0 + chunk]) for c0 in range(0, len(idx), chunk)])
+    dL = np.concatenate([lm_head_dlogits(h, Wd, targets, lse, dloss, rows=idx[c0:c0 + chunk])
+                         for c0 in range(0, len(idx), chunk)])
     out = {"dlogits": dL, "dh": dL @ Wd}
     vc = np.arange(V) if dw_rows is None else np.asarray(dw_rows, dtype=np.int64)
     dW = np.zeros((len(vc), Wd.shape[1]))
     for c0 in range(0, M, chunk):
         blk = np.arange(c0, min(M, c0 + chunk))
-        dW += dlogits(blk, vc).T @ _take(h, blk)
+        dW += lm_head_dlogits(h, Wd, targets, lse, dloss, rows=blk, vcols=vc).T @ _take(h, blk)
     out["dW"] = dW
     return out

@@ -17,8 +17,8 @@ reports:
 
 Control flow is followed with a fixed-point iteration over branch targets.
 
-Usage: python -m transformer_gemm_epilogue_res_amd.check_lds_waits [file.s]
-(without a file it compiles csrc/coda_kernels.hip to assembly first).
+Usage: python tests/check_lds_waits.py [file.s]
+(without a file it compiles the library's coda_kernels.hip to assembly first).
 """
 from __future__ import annotations
 
@@ -201,11 +201,13 @@ def merge(a, b):
 
 
 def device_asm(src=None, extra_flags=()) -> str:
-    here = os.path.dirname(os.path.abspath(__file__))
-    src = src or os.path.join(here, "csrc", "coda_kernels.hip")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    from transformer_gemm_epilogue_res_amd.build import CSRC, FLAGS, HIPCC
+    src = src or os.path.join(CSRC, "coda_kernels.hip")
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
-        from .build import FLAGS, HIPCC
         flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
         subprocess.run([HIPCC, *flags, *extra_flags, "--cuda-device-only", "-S", src, "-o", out], check=True,
                        capture_output=True)

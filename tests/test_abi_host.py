@@ -354,3 +354,38 @@ def test_python_binding_checks_dtypes(name):
             L.fwd(x, x, x, x[0], x, 1e-5)
         else:
             L.bwd(x, x, x, x, x[:, 0], x[0], x)
+
+
+def test_python_binding_rejects_host_tensors_before_any_call():
+    """A CPU (host) tensor anywhere -- input, output or workspace -- is refused by the binding with a
+    ValueError before the library is called: its pointer would be a host address to the kernels."""
+    import torch
+    bf = torch.bfloat16
+    M, K0, D, N = 4, 256, 256, 256
+    x, W0, z, g, W1 = (torch.zeros(M, K0, dtype=bf), torch.zeros(K0, D, dtype=bf), torch.zeros(M, D, dtype=bf),
+                       torch.zeros(D, dtype=bf), torch.zeros(D, N, dtype=bf))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.fwd(x, W0, z, g, W1, 1e-5)
+    dY, y = torch.zeros(M, N, dtype=bf), torch.zeros(M, N, dtype=bf)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.bwd(dY, y, z, z, torch.zeros(M), g, W1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.bwd_gemm0(z, x, W0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.gemm(x, W0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.ce_fwd(z, torch.zeros(512, D, dtype=bf), torch.zeros(M, dtype=torch.int64))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L._ws_bytes(torch.zeros(16, dtype=torch.uint8), "cpu")
+    with pytest.raises(TypeError):
+        L._want([1, 2], "x", bf)
+
+
+def test_python_binding_counts_workspace_bytes_not_elements():
+    """A workspace of any dtype is passed to the library as its size in bytes (checked through the meta
+    device, which has sizes but no storage)."""
+    import torch
+    ws = torch.empty(10, dtype=torch.float32, device="meta")
+    assert ws.numel() * ws.element_size() == 40
+    with pytest.raises(ValueError):          # and a non-GPU workspace is refused
+        L._ws_bytes(ws, "meta")

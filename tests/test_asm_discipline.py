@@ -5,7 +5,7 @@ waits for those loads nor pads MFMA result reads; the check compiles the
 kernels to gfx950 assembly and verifies both by static analysis."""
 import pytest
 
-from transformer_gemm_epilogue_res_amd import check_lds_waits as chk
+import check_lds_waits as chk
 
 
 @pytest.fixture(scope="module")

@@ -68,7 +68,8 @@ def check_bwd(out, host, lse_ref, rows=None, vrows=None):
     # need dlogits[:, v] over all M rows
     a_dh = mt.bf16_ulp(ref["dlogits"]) @ np.abs(mt.f64(W))
     vcols = np.arange(W.shape[0]) if vrows is None else np.asarray(vrows)
-    dLv = _dlogits_cols(h, W, t, lse_ref, dloss, vcols)
+    dLv = np.concatenate([orc.lm_head_dlogits(h, W, t, lse_ref, dloss, rows=np.arange(c0, min(h.shape[0], c0 + 512)), vcols=vcols)
+                          for c0 in range(0, h.shape[0], 512)])
     a_dW = mt.bf16_ulp(dLv).T @ np.abs(mt.f64(h))
     e = {"dlogits": mt.bf16_faithful(dL, ref["dlogits"], TOL),
          "dh": mt.within_allowance(dh, ref["dh"], a_dh, TOL), "dW": mt.within_allowance(dW, ref["dW"], a_dW, TOL)}
@@ -77,21 +78,6 @@ def check_bwd(out, host, lse_ref, rows=None, vrows=None):
     ign = torch.as_tensor(~((rsel(t, rows) >= 0) & (rsel(t, rows) < W.shape[0])))
     assert torch.all(dL[ign] == 0)
     assert e["dlogits"] <= 1.0 and e["dh"] <= 1.0 and e["dW"] <= 1.0
-
-
-def _dlogits_cols(h, W, t, lse, dloss, vcols, chunk=512):
-    """dlogits[:, vcols] for every row, from the oracle's definition (for the dW bound)."""
-    Wd = orc.f64(W)[vcols]
-    tt, ls, dl = t.numpy(), orc.f64(lse), orc.f64(dloss)
-    V = W.shape[0]
-    out = []
-    for c0 in range(0, h.shape[0], chunk):
-        sel = np.arange(c0, min(h.shape[0], c0 + chunk))
-        P = np.exp(orc.f64(h[sel]) @ Wd.T - ls[sel, None])
-        onehot = (np.asarray(vcols)[None, :] == tt[sel, None]).astype(np.float64)
-        valid = (tt[sel] >= 0) & (tt[sel] < V)
-        out.append(np.where(valid[:, None], dl[sel, None] * (P - onehot), 0.0))
-    return np.concatenate(out)
 
 
 @pytest.mark.parametrize("name", list(SMALL))

@@ -501,3 +501,35 @@ def test_binding_reports_errors_without_launch():
     with pytest.raises(L.CodaError) as e:
         L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], 0.0)
     assert e.value.status == L.CODA_ERR_ARG
+
+
+def test_binding_checks_outputs_and_workspace_bytes():
+    """Outputs of the wrong shape or on the host are refused before any launch; a workspace is measured
+    in bytes whatever its dtype (a float32 workspace of exactly the needed bytes works; one byte short of
+    it is rejected by the library's own check)."""
+    c = FWD_SMALL["ragged"]
+    M, D, N = c["M"], c["D"], c["N"]
+    announce(f"binding misuse checks {c}")
+    inp = to_dev(inputs.forward_inputs(**c, seed=0))
+    args = (inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
+
+    def outs(**over):
+        o = {"h": torch.empty(M, D, dtype=torch.bfloat16, device=DEV), "g": torch.empty(M, D, dtype=torch.bfloat16, device=DEV),
+             "r": torch.empty(M, dtype=torch.float32, device=DEV), "y": torch.empty(M, N, dtype=torch.float32, device=DEV)}
+        o.update(over)
+        return o
+    with pytest.raises(ValueError):
+        L.fwd(*args, out=outs(y=torch.empty(M, N - 256, dtype=torch.float32, device=DEV)))
+    with pytest.raises(ValueError):
+        L.fwd(*args, out=outs(h=torch.empty(M, D, dtype=torch.bfloat16)))
+    with pytest.raises(TypeError):
+        L.fwd(*args, out=outs(r=torch.empty(M, dtype=torch.bfloat16, device=DEV)))
+    need = L.workspace_bytes(L.CODA_OP_FWD, M, D, N)
+    assert need % 4 == 0
+    ref = L.fwd(*args, torch.float32)
+    got = L.fwd(*args, ws=torch.empty(need // 4, dtype=torch.float32, device=DEV), out=outs())
+    torch.cuda.synchronize()
+    assert torch.equal(ref["y"], got["y"]) and torch.equal(ref["r"], got["r"])
+    with pytest.raises(L.CodaError) as e:
+        L.fwd(*args, ws=torch.empty(need - 1, dtype=torch.uint8, device=DEV), out=outs())
+    assert e.value.status == L.CODA_ERR_WORKSPACE

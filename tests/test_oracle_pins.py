@@ -445,6 +445,10 @@ def test_cross_entropy_backward_finite_differences_and_subsets():
     assert np.allclose(bs["dh"], b["dh"][rows], rtol=0, atol=1e-15)
     assert np.allclose(bs["dlogits"], b["dlogits"][rows], rtol=0, atol=1e-15)
     assert np.allclose(bs["dW"], b["dW"][vr], rtol=0, atol=1e-14)
+    # dlogits on a (row, vocabulary-column) block equals that block of the full backward's dlogits,
+    # whose dh and dW pass the finite differences above
+    blk = orc.lm_head_dlogits(h, W, t, f["lse"], dloss, rows=rows, vcols=vr)
+    assert np.allclose(blk, b["dlogits"][np.ix_(rows, vr)], rtol=0, atol=1e-15)
 
 
 def test_backward_finite_differences():

@@ -155,13 +155,36 @@ def _dt(dtype) -> int:
     raise ValueError(f"unsupported output dtype {dtype}")
 
 
-def _want(t, name, dtype, shape=None):
-    if t.dtype != dtype:
-        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+def _want(t, name, dtype, shape=None, device=None):
+    """t must be a contiguous GPU tensor of `dtype` (or one of a tuple of dtypes), `shape` and, when
+    given, on `device`: every pointer handed to the library is then device memory of the stated size."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name}: expected {' or '.join(map(str, dts))}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (got one on {t.device})")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name}: on {t.device}, the other tensors are on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+OUT_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def _ws_bytes(ws, device) -> int:
+    """Byte size of a workspace tensor (any dtype), after checking it is contiguous GPU memory on device."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"ws: expected a torch.Tensor, got {type(ws).__name__}")
+    if not ws.is_cuda or ws.device != torch.device(device):
+        raise ValueError(f"ws: must be a GPU tensor on {device} (got one on {ws.device})")
+    if not ws.is_contiguous():
+        raise ValueError("ws: must be contiguous")
+    return ws.numel() * ws.element_size()
 
 
 def _stream(device) -> c_void_p:
@@ -177,13 +200,21 @@ def workspace(op: int, M: int, D: int, N: int, device) -> torch.Tensor:
 
 
 def _fwd_args(x, W0, z, gamma, W1, eps, h, g, r, y):
+    _want(x, "x", torch.bfloat16)
+    _want(W1, "W1", torch.bfloat16)
     M, K0 = x.shape
     D, N = W1.shape
-    _want(x, "x", torch.bfloat16, (M, K0))
-    _want(W0, "W0", torch.bfloat16, (K0, D))
-    _want(z, "z", torch.bfloat16, (M, D))
-    _want(gamma, "gamma", torch.bfloat16, (D,))
-    _want(W1, "W1", torch.bfloat16, (D, N))
+    dev = x.device
+    _want(x, "x", torch.bfloat16, (M, K0), dev)
+    _want(W0, "W0", torch.bfloat16, (K0, D), dev)
+    _want(z, "z", torch.bfloat16, (M, D), dev)
+    _want(gamma, "gamma", torch.bfloat16, (D,), dev)
+    _want(W1, "W1", torch.bfloat16, (D, N), dev)
+    _want(h, "h", torch.bfloat16, (M, D), dev)
+    if g is not None:
+        _want(g, "g", torch.bfloat16, (M, D), dev)
+    _want(r, "r", torch.float32, (M,), dev)
+    _want(y, "y", OUT_DTYPES, (M, N), dev)
     return FwdArgs(M, K0, D, N, float(eps), _ptr(x), _ptr(W0), _ptr(z), _ptr(gamma), _ptr(W1),
                    _ptr(h), _ptr(g), _ptr(r), _ptr(y), _dt(y.dtype))
 
@@ -202,23 +233,30 @@ def fwd(x, W0, z, gamma, W1, eps, y_dtype=torch.bfloat16, ws=None, out=None, unf
     if ws is None:
         ws = workspace(op, M, D, N, dev)
     if unfused:
-        st = lib().coda_unfused_ref(CODA_OP_FWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+        st = lib().coda_unfused_ref(CODA_OP_FWD, ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev))
     else:
-        st = lib().coda_fwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+        st = lib().coda_fwd(ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev))
     _check(st, "coda_unfused_ref(fwd)" if unfused else "coda_fwd")
     return out
 
 
 def _bwd_args(dY, y, h, g, r, gamma, W1, da, dgamma, dW1, s):
+    _want(dY, "dY", torch.bfloat16)
+    _want(W1, "W1", torch.bfloat16)
     M, N = dY.shape
     D = W1.shape[0]
-    _want(dY, "dY", torch.bfloat16, (M, N))
-    _want(y, "y", torch.bfloat16, (M, N))
-    _want(h, "h", torch.bfloat16, (M, D))
-    _want(g, "g", torch.bfloat16, (M, D))
-    _want(r, "r", torch.float32, (M,))
-    _want(gamma, "gamma", torch.bfloat16, (D,))
-    _want(W1, "W1", torch.bfloat16, (D, N))
+    dev = dY.device
+    _want(dY, "dY", torch.bfloat16, (M, N), dev)
+    _want(y, "y", torch.bfloat16, (M, N), dev)
+    _want(h, "h", torch.bfloat16, (M, D), dev)
+    _want(g, "g", torch.bfloat16, (M, D), dev)
+    _want(r, "r", torch.float32, (M,), dev)
+    _want(gamma, "gamma", torch.bfloat16, (D,), dev)
+    _want(W1, "W1", torch.bfloat16, (D, N), dev)
+    _want(da, "da", OUT_DTYPES, (M, D), dev)
+    _want(dgamma, "dgamma", torch.float32, (D,), dev)
+    _want(dW1, "dW1", OUT_DTYPES, (D, N), dev)
+    _want(s, "s", torch.float32, (M,), dev)
     return BwdArgs(M, D, N, _ptr(dY), _ptr(y), _ptr(h), _ptr(g), _ptr(r), _ptr(gamma), _ptr(W1),
                    _ptr(da), _ptr(dgamma), _ptr(dW1), _ptr(s), _dt(da.dtype), _dt(dW1.dtype))
 
@@ -239,19 +277,24 @@ def bwd(dY, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_dtype=torch.bflo
     if ws is None:
         ws = workspace(op, M, D, N, dev)
     if unfused:
-        st = lib().coda_unfused_ref(CODA_OP_BWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+        st = lib().coda_unfused_ref(CODA_OP_BWD, ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev))
     else:
-        st = lib().coda_bwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev))
+        st = lib().coda_bwd(ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev))
     _check(st, "coda_unfused_ref(bwd)" if unfused else "coda_bwd")
     return out
 
 
 def _bwd_gemm0_args(dh, x, W0, dx, dW0):
+    _want(dh, "dh", torch.bfloat16)
+    _want(x, "x", torch.bfloat16)
     M, D = dh.shape
     K0 = x.shape[1]
-    _want(dh, "dh", torch.bfloat16, (M, D))
-    _want(x, "x", torch.bfloat16, (M, K0))
-    _want(W0, "W0", torch.bfloat16, (K0, D))
+    dev = dh.device
+    _want(dh, "dh", torch.bfloat16, (M, D), dev)
+    _want(x, "x", torch.bfloat16, (M, K0), dev)
+    _want(W0, "W0", torch.bfloat16, (K0, D), dev)
+    _want(dx, "dx", OUT_DTYPES, (M, K0), dev)
+    _want(dW0, "dW0", OUT_DTYPES, (K0, D), dev)
     return BwdGemm0Args(M, K0, D, _ptr(dh), _ptr(x), _ptr(W0), _ptr(dx), _ptr(dW0), _dt(dx.dtype), _dt(dW0.dtype))
 
 
@@ -269,6 +312,7 @@ def bwd_gemm0(dh, x, W0, dx_dtype=torch.bfloat16, dW0_dtype=torch.bfloat16, out=
 
 
 def _fwd_swiglu_args(x, W0, z, gamma, W1, eps, out):
+    _want(out["o"], "o", OUT_DTYPES, (x.shape[0], W1.shape[1] // 2), x.device)
     return FwdSwigluArgs(_fwd_args(x, W0, z, gamma, W1, eps, out["h"], out["g"], out["r"], out["y"]),
                          _ptr(out["o"]), _dt(out["o"].dtype))
 
@@ -289,26 +333,36 @@ def fwd_swiglu(x, W0, z, gamma, W1, eps, o_dtype=torch.bfloat16, ws=None, out=No
     if ws is None:
         ws = workspace(CODA_OP_UNFUSED_FWD_SWIGLU if unfused else CODA_OP_FWD_SWIGLU, M, D, N, dev)
     if unfused:
-        _check(lib().coda_unfused_ref(CODA_OP_FWD_SWIGLU, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+        _check(lib().coda_unfused_ref(CODA_OP_FWD_SWIGLU, ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)),
                "coda_unfused_ref(fwd_swiglu)")
     else:
-        _check(lib().coda_fwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_fwd_swiglu")
+        _check(lib().coda_fwd_swiglu(ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)), "coda_fwd_swiglu")
     return out
 
 
 def _bwd_swiglu_args(dOut, W2, o, y, h, g, r, gamma, W1, out):
+    _want(dOut, "dOut", torch.bfloat16)
+    _want(W1, "W1", torch.bfloat16)
+    _want(W2, "W2", torch.bfloat16)
     M, E = dOut.shape
     D, N = W1.shape
     F = W2.shape[0]
-    _want(dOut, "dOut", torch.bfloat16, (M, E))
-    _want(W2, "W2", torch.bfloat16, (N // 2, E))
-    _want(o, "o", torch.bfloat16, (M, F))
-    _want(y, "y", torch.bfloat16, (M, N))
-    _want(h, "h", torch.bfloat16, (M, D))
-    _want(g, "g", torch.bfloat16, (M, D))
-    _want(r, "r", torch.float32, (M,))
-    _want(gamma, "gamma", torch.bfloat16, (D,))
-    _want(W1, "W1", torch.bfloat16, (D, N))
+    dev = dOut.device
+    _want(dOut, "dOut", torch.bfloat16, (M, E), dev)
+    _want(W2, "W2", torch.bfloat16, (N // 2, E), dev)
+    _want(o, "o", torch.bfloat16, (M, F), dev)
+    _want(y, "y", torch.bfloat16, (M, N), dev)
+    _want(h, "h", torch.bfloat16, (M, D), dev)
+    _want(g, "g", torch.bfloat16, (M, D), dev)
+    _want(r, "r", torch.float32, (M,), dev)
+    _want(gamma, "gamma", torch.bfloat16, (D,), dev)
+    _want(W1, "W1", torch.bfloat16, (D, N), dev)
+    _want(out["dY"], "dY", torch.bfloat16, (M, N), dev)
+    _want(out["da"], "da", OUT_DTYPES, (M, D), dev)
+    _want(out["dgamma"], "dgamma", torch.float32, (D,), dev)
+    _want(out["dW1"], "dW1", OUT_DTYPES, (D, N), dev)
+    _want(out["dW2"], "dW2", OUT_DTYPES, (F, E), dev)
+    _want(out["s"], "s", torch.float32, (M,), dev)
     return BwdSwigluArgs(M, D, N, E, _ptr(dOut), _ptr(W2), _ptr(o), _ptr(y), _ptr(h), _ptr(g), _ptr(r),
                          _ptr(gamma), _ptr(W1), _ptr(out["dY"]), _ptr(out["da"]), _ptr(out["dgamma"]),
                          _ptr(out["dW1"]), _ptr(out["dW2"]), _ptr(out["s"]),
@@ -334,10 +388,10 @@ def bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, da_dtype=torch.bfloat16, dW1_
     if ws is None:
         ws = workspace(CODA_OP_UNFUSED_BWD_SWIGLU if unfused else CODA_OP_BWD_SWIGLU, M, D, N, dev)
     if unfused:
-        _check(lib().coda_unfused_ref(CODA_OP_BWD_SWIGLU, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+        _check(lib().coda_unfused_ref(CODA_OP_BWD_SWIGLU, ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)),
                "coda_unfused_ref(bwd_swiglu)")
     else:
-        _check(lib().coda_bwd_swiglu(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_bwd_swiglu")
+        _check(lib().coda_bwd_swiglu(ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)), "coda_bwd_swiglu")
     return out
 
 
@@ -350,11 +404,11 @@ class BoundSwiglu:
     def run(self, stream, unfused=False):
         if unfused:
             op = CODA_OP_FWD_SWIGLU if self.kind == "fwd" else CODA_OP_BWD_SWIGLU
-            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream),
+            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(self.ws), _ws_bytes(self.ws, self.ws.device), stream),
                    f"coda_unfused_ref({self.kind}_swiglu)")
             return
         fn = lib().coda_fwd_swiglu if self.kind == "fwd" else lib().coda_bwd_swiglu
-        _check(fn(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}_swiglu")
+        _check(fn(ctypes.byref(self.args), _ptr(self.ws), _ws_bytes(self.ws, self.ws.device), stream), f"coda_{self.kind}_swiglu")
 
 
 def bind_fwd_swiglu(x, W0, z, gamma, W1, eps, out, ws):
@@ -367,15 +421,18 @@ def bind_bwd_swiglu(dOut, W2, o, y, h, g, r, gamma, W1, out, ws):
 
 
 def _ce_fwd_args(h, W, targets, lse, loss, logits=None):
+    _want(h, "h", torch.bfloat16)
+    _want(W, "W", torch.bfloat16)
     M, D = h.shape
     V = W.shape[0]
-    _want(h, "h", torch.bfloat16, (M, D))
-    _want(W, "W", torch.bfloat16, (V, D))
-    _want(targets, "targets", torch.int64, (M,))
-    _want(lse, "lse", torch.float32, (M,))
-    _want(loss, "loss", torch.float32, (M,))
+    dev = h.device
+    _want(h, "h", torch.bfloat16, (M, D), dev)
+    _want(W, "W", torch.bfloat16, (V, D), dev)
+    _want(targets, "targets", torch.int64, (M,), dev)
+    _want(lse, "lse", torch.float32, (M,), dev)
+    _want(loss, "loss", torch.float32, (M,), dev)
     if logits is not None:
-        _want(logits, "logits", torch.float32, (M, V))
+        _want(logits, "logits", torch.float32, (M, V), dev)
     return CeFwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(loss),
                      None if logits is None else _ptr(logits))
 
@@ -397,24 +454,29 @@ def ce_fwd(h, W, targets, ws=None, out=None, unfused=False, store_logits=False):
     if ws is None:
         ws = workspace(CODA_OP_UNFUSED_CE_FWD if unfused else CODA_OP_CE_FWD, M, D, V, dev)
     if unfused:
-        _check(lib().coda_unfused_ref(CODA_OP_CE_FWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+        _check(lib().coda_unfused_ref(CODA_OP_CE_FWD, ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)),
                "coda_unfused_ref(ce_fwd)")
     else:
-        _check(lib().coda_ce_fwd(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)), "coda_ce_fwd")
+        _check(lib().coda_ce_fwd(ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)), "coda_ce_fwd")
     return out
 
 
 def _ce_bwd_args(h, W, targets, lse, dloss, out, logits=None):
+    _want(h, "h", torch.bfloat16)
+    _want(W, "W", torch.bfloat16)
     M, D = h.shape
     V = W.shape[0]
-    _want(h, "h", torch.bfloat16, (M, D))
-    _want(W, "W", torch.bfloat16, (V, D))
-    _want(targets, "targets", torch.int64, (M,))
-    _want(lse, "lse", torch.float32, (M,))
-    _want(dloss, "dloss", torch.float32, (M,))
-    _want(out["dlogits"], "dlogits", torch.bfloat16, (M, V))
+    dev = h.device
+    _want(h, "h", torch.bfloat16, (M, D), dev)
+    _want(W, "W", torch.bfloat16, (V, D), dev)
+    _want(targets, "targets", torch.int64, (M,), dev)
+    _want(lse, "lse", torch.float32, (M,), dev)
+    _want(dloss, "dloss", torch.float32, (M,), dev)
+    _want(out["dlogits"], "dlogits", torch.bfloat16, (M, V), dev)
+    _want(out["dh"], "dh", OUT_DTYPES, (M, D), dev)
+    _want(out["dW"], "dW", OUT_DTYPES, (V, D), dev)
     if logits is not None:
-        _want(logits, "logits", torch.float32, (M, V))
+        _want(logits, "logits", torch.float32, (M, V), dev)
     return CeBwdArgs(M, D, V, _ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(dloss), _ptr(out["dlogits"]),
                      _ptr(out["dh"]), _ptr(out["dW"]), _dt(out["dh"].dtype), _dt(out["dW"].dtype),
                      None if logits is None else _ptr(logits))
@@ -436,7 +498,7 @@ def ce_bwd(h, W, targets, lse, dloss, dh_dtype=torch.bfloat16, dW_dtype=torch.bf
     if unfused:
         if ws is None:
             ws = workspace(CODA_OP_UNFUSED_CE_BWD, M, D, V, dev)
-        _check(lib().coda_unfused_ref(CODA_OP_CE_BWD, ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)),
+        _check(lib().coda_unfused_ref(CODA_OP_CE_BWD, ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)),
                "coda_unfused_ref(ce_bwd)")
     else:
         _check(lib().coda_ce_bwd(ctypes.byref(a), _stream(dev)), "coda_ce_bwd")
@@ -453,10 +515,10 @@ class BoundCe:
         """unfused_ws: run coda_unfused_ref (stored fp32 logits) in that workspace instead."""
         if unfused_ws is not None:
             op = CODA_OP_CE_FWD if self.kind == "fwd" else CODA_OP_CE_BWD
-            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(unfused_ws), unfused_ws.numel(), stream),
+            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(unfused_ws), _ws_bytes(unfused_ws, unfused_ws.device), stream),
                    f"coda_unfused_ref(ce_{self.kind})")
         elif self.kind == "fwd":
-            _check(lib().coda_ce_fwd(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), "coda_ce_fwd")
+            _check(lib().coda_ce_fwd(ctypes.byref(self.args), _ptr(self.ws), _ws_bytes(self.ws, self.ws.device), stream), "coda_ce_fwd")
         else:
             _check(lib().coda_ce_bwd(ctypes.byref(self.args), stream), "coda_ce_bwd")
 
@@ -490,16 +552,16 @@ class Bound:
 
     def stage(self, i, stream):
         fn = lib().coda_fwd_stage if self.kind == "fwd" else lib().coda_bwd_stage
-        _check(fn(i, ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}_stage({i})")
+        _check(fn(i, ctypes.byref(self.args), _ptr(self.ws), _ws_bytes(self.ws, self.ws.device), stream), f"coda_{self.kind}_stage({i})")
 
     def run(self, stream, unfused=False):
         if unfused:
             op = CODA_OP_FWD if self.kind == "fwd" else CODA_OP_BWD
-            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream),
+            _check(lib().coda_unfused_ref(op, ctypes.byref(self.args), _ptr(self.ws), _ws_bytes(self.ws, self.ws.device), stream),
                    "coda_unfused_ref")
         else:
             fn = lib().coda_fwd if self.kind == "fwd" else lib().coda_bwd
-            _check(fn(ctypes.byref(self.args), _ptr(self.ws), self.ws.numel(), stream), f"coda_{self.kind}")
+            _check(fn(ctypes.byref(self.args), _ptr(self.ws), _ws_bytes(self.ws, self.ws.device), stream), f"coda_{self.kind}")
 
 
 def bind_fwd(x, W0, z, gamma, W1, eps, out, ws):
@@ -519,11 +581,18 @@ def current_stream(device="cuda:0") -> c_void_p:
 def gemm(A, B, a_layout=CODA_ROW, b_layout=CODA_ROW, out_dtype=torch.float32, M=None, N=None, K=None):
     """C[M,N] = A @ B with the shared mainloop. Layouts as in coda_layout_t."""
     _want(A, "A", torch.bfloat16)
-    _want(B, "B", torch.bfloat16)
+    _want(B, "B", torch.bfloat16, device=A.device)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
     if M is None:
         M, K = (A.shape[0], A.shape[1]) if a_layout == CODA_ROW else (A.shape[1], A.shape[0])
     if N is None:
         N = B.shape[1] if b_layout == CODA_ROW else B.shape[0]
+    # the logical [M, K] and [K, N] operands must lie inside the stored tensors
+    a_ext = (M, K) if a_layout == CODA_ROW else (K, M)
+    b_ext = (K, N) if b_layout == CODA_ROW else (N, K)
+    if A.shape[0] < a_ext[0] or A.shape[1] < a_ext[1] or B.shape[0] < b_ext[0] or B.shape[1] < b_ext[1]:
+        raise ValueError(f"gemm: M={M}, N={N}, K={K} exceed A {tuple(A.shape)} or B {tuple(B.shape)}")
     C = torch.empty(M, N, dtype=out_dtype, device=A.device)
     a = GemmArgs(M, N, K, _ptr(A), A.shape[1], a_layout, _ptr(B), B.shape[1], b_layout, _ptr(C), N, _dt(out_dtype))
     _check(lib().coda_gemm(ctypes.byref(a), _stream(A.device)), "coda_gemm")

@@ -110,6 +110,7 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_UNFUSED_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? unfused_bwd_swiglu_ws(M, D, N) : 0;
     case CODA_OP_UNFUSED_CE_FWD:
     case CODA_OP_UNFUSED_CE_BWD: return dim_ok(N) ? unfused_ce_ws(M, N) : 0;
+    default: break;
   }
   return 0;
 }
@@ -236,6 +237,7 @@ const char* coda_status_string(coda_status_t s) {
     case CODA_ERR_WORKSPACE: return "workspace missing or too small";
     case CODA_ERR_ARG: return "bad scalar argument";
     case CODA_ERR_HIP: return "HIP launch failed";
+    default: break;
   }
   return "unknown status";
 }
