@@ -330,6 +330,23 @@ coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* 
  * row-statistic combine (r) -> GEMM1 + epilogue (row scale r). */
 coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
+/* The fused forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels as coda_fwd, with the
+ * sum-of-squares partials kept in a device array of the library's own, CODA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB), which every GPU the library runs on holds until the process ends; no workspace argument,
+ * and no allocation or free of any kind. GEMM0 is never split over its contraction here (coda_fwd
+ * splits it when its tiles cannot fill the chip), so the partials need only M * (D / 64) * 4 bytes.
+ *   - Returns CODA_ERR_WORKSPACE, launching nothing, when M * (D / 64) * 4 exceeds the 16 MiB
+ *     (e.g. M > 65536 rows at D = 4096); every other check and status is coda_fwd's.
+ *   - All calls on one GPU share that GPU's array: calls that may overlap on one GPU (on different
+ *     streams, or from several threads) race and must be ordered by the caller. A call needs nothing
+ *     from the previous one (its partials are written in full before they are read).
+ *   - The first call on a device looks the array's device address up (hipGetSymbolAddress with
+ *     that device current) and keeps it; a failed lookup returns CODA_ERR_HIP. */
+#define CODA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+coda_status_t coda_validate_fwd_noalloc(const coda_fwd_args_t* a);
+coda_status_t coda_fwd_noalloc(const coda_fwd_args_t* a, void* stream);
+
 /* Fused backward: row statistic s and bf16(r*g) (transposed, so the dW1
  * GEMM's left operand is contiguous along its contraction) -> G = dY@W1^T with the
  * RMSNorm-backward epilogue (da, dgamma column partials) -> dW1 = bf16(r*g)^T @ dY,

@@ -90,6 +90,11 @@ int main() {
       a = good_fwd(); a.eps = e;
       expect("fwd bad eps", coda_validate_fwd(&a, fake(20), big_ws), CODA_ERR_ARG);
     }
+    a = good_fwd();
+    expect("fwd_noalloc ok", coda_validate_fwd_noalloc(&a), CODA_OK);
+    a.M = int64_t(1) << 22; a.D = 4096;     // partials of 2^22 x 64 fp32 = 1 GiB > the 16 MiB scratch
+    expect("fwd_noalloc too large", coda_validate_fwd_noalloc(&a), CODA_ERR_WORKSPACE);
+    expect("fwd_noalloc null", coda_validate_fwd_noalloc(nullptr), CODA_ERR_NULL);
     for (int t : {-1, 2, 7, 1 << 30}) {
       a = good_fwd(); a.y_dtype = raw<coda_dtype_t>(t);
       expect("fwd bad dtype", coda_validate_fwd(&a, fake(20), big_ws), CODA_ERR_ARG);

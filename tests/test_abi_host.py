@@ -389,3 +389,16 @@ def test_python_binding_counts_workspace_bytes_not_elements():
     assert ws.numel() * ws.element_size() == 40
     with pytest.raises(ValueError):          # and a non-GPU workspace is refused
         L._ws_bytes(ws, "meta")
+
+
+def test_validate_fwd_noalloc_limit():
+    """The no-allocation forward accepts what coda_fwd accepts while its partials, M * (D / 64) * 4
+    bytes, fit the library's 16 MiB device scratch, and returns CODA_ERR_WORKSPACE beyond that."""
+    lib = L.lib()
+    assert L.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd())) == L.CODA_OK
+    rows = (16 << 20) // ((4096 // 64) * 4)           # 65536 rows at D = 4096 fill it exactly
+    assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd(M=rows, D=4096))) == L.CODA_OK
+    assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd(M=rows + 1, D=4096))) == L.CODA_ERR_WORKSPACE
+    assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd(eps=0.0))) == L.CODA_ERR_ARG
+    assert lib.coda_validate_fwd_noalloc(None) == L.CODA_ERR_NULL

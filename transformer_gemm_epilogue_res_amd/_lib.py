@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
                            ("coda_validate_gemm", [POINTER(GemmArgs)]),
                            ("coda_validate_unfused", [c_int, c_void_p, c_void_p, c_size_t]),
                            ("coda_fwd", [POINTER(FwdArgs), c_void_p, c_size_t, c_void_p]),
+                           ("coda_validate_fwd_noalloc", [POINTER(FwdArgs)]),
+                           ("coda_fwd_noalloc", [POINTER(FwdArgs), c_void_p]),
                            ("coda_bwd", [POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
                            ("coda_unfused_ref", [c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
                            ("coda_fwd_stage", [c_int, POINTER(FwdArgs), c_void_p, c_size_t, c_void_p]),
@@ -237,6 +239,24 @@ def fwd(x, W0, z, gamma, W1, eps, y_dtype=torch.bfloat16, ws=None, out=None, unf
     else:
         st = lib().coda_fwd(ctypes.byref(a), _ptr(ws), _ws_bytes(ws, dev), _stream(dev))
     _check(st, "coda_unfused_ref(fwd)" if unfused else "coda_fwd")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fwd_noalloc(x, W0, z, gamma, W1, eps, y_dtype=torch.bfloat16, out=None):
+    """coda_fwd_noalloc: the fused forward with its partials in the library's own device scratch (no
+    workspace argument; the outputs in `out` are the caller's). Returns dict(h, g, r, y)."""
+    M, D, N = x.shape[0], W1.shape[0], W1.shape[1]
+    dev = x.device
+    if out is None:
+        out = {"h": torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+               "g": torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+               "r": torch.empty(M, dtype=torch.float32, device=dev),
+               "y": torch.empty(M, N, dtype=y_dtype, device=dev)}
+    a = _fwd_args(x, W0, z, gamma, W1, eps, out["h"], out["g"], out["r"], out["y"])
+    _check(lib().coda_fwd_noalloc(ctypes.byref(a), _stream(dev)), "coda_fwd_noalloc")
     return out
 
 

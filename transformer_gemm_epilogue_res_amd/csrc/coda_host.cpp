@@ -121,6 +121,12 @@ coda_status_t coda_validate_fwd(const coda_fwd_args_t* a, const void* ws, size_t
   return check_ws(ws, ws_bytes, fwd_ws(a->M, a->D));
 }
 
+coda_status_t coda_validate_fwd_noalloc(const coda_fwd_args_t* a) {
+  coda_status_t st = validate_fwd_common(a, true);
+  if (st != CODA_OK) return st;
+  return fwd_ws_p(a->M, a->D) <= kNoAllocScratchBytes ? CODA_OK : CODA_ERR_WORKSPACE;
+}
+
 coda_status_t coda_validate_bwd(const coda_bwd_args_t* a, const void* ws, size_t ws_bytes) {
   coda_status_t st = validate_bwd_common(a);
   if (st != CODA_OK) return st;

@@ -77,6 +77,8 @@ inline KSplit gemm0_split(int64_t M, int64_t K0, int64_t D) {
   const int64_t kslice = ceil_div(ceil_div(K0, S), kBK) * kBK;
   return {ceil_div(K0, kslice), kslice};
 }
+// Device scratch of the no-allocation forward (coda_fwd_noalloc): its partials P [M, D / 64] fp32.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 // Fused forward workspace: the sums of squares P [M, D / 64], then (split-K only) the
 // fp32 partial products [S_max, M, D].
 inline size_t fwd_ws_p(int64_t M, int64_t D) { return align256(size_t(M) * size_t(ssq_cols(D)) * 4); }

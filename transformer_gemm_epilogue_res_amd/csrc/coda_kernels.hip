@@ -11,6 +11,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1360,6 +1362,77 @@ hipError_t ce_bwd_products(const coda_ce_bwd_args_t* a, hipStream_t st) {
   return gemm_plain(pw, false, false, a->dW, a->D, a->dW_dtype == CODA_F32, st);
 }
 
+// Stage `stage` of the fused forward (0 GEMM0 + epilogue, 1 r combine, 2 GEMM1 + row scale) with the
+// sum-of-squares partials P [M, D / 64]; part: room for GEMM0's split-K partial products when its tiles
+// cannot fill the chip, or nullptr to never split (the no-allocation entry point).
+hipError_t fwd_stage(int stage, const coda_fwd_args_t* a, float* P, float* part, hipStream_t st) {
+  const int64_t pcols = ssq_cols(a->D);
+  if (stage == 0) {  // GEMM0 x @ W0 with the residual / h / g / sum-of-squares epilogue
+    const KSplit ks = part != nullptr ? gemm0_split(a->M, a->K0, a->D) : KSplit{1, 0};
+    if (ks.S > 1) {  // few rows: split the contraction, then a row kernel does the epilogue's work
+      const int64_t sstride = a->M * a->D;
+      const GemmShape pp{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D, ks.kslice};
+      hipError_t e = launch_gemm<true, false>(pp, EpiPartialF32{part, a->D, a->M, sstride}, st);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(splitk_residual_kernel, dim3(unsigned(ceil_div(a->D, 1024)), unsigned(a->M)), dim3(256), 0, st,
+                         (const float*)part, int(ks.S), sstride, (const uint16_t*)a->z, (const uint16_t*)a->gamma,
+                         (uint16_t*)a->h, (uint16_t*)a->g, P, a->D, pcols);
+      return hipGetLastError();
+    }
+    const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
+    return launch_gemm<true, false>(
+        p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st);
+  }
+  if (stage == 1) {  // partial sums of squares -> r
+    hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, kCombineRows))), dim3(256), 0, st, P, a->r, a->M,
+                       pcols, float(a->D), a->eps);
+    return hipGetLastError();
+  }
+  // GEMM1 g @ W1 with the row-scale epilogue
+  const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
+  if (a->y_dtype == CODA_F32) return launch_gemm<true, false>(p1, EpiRowScale<true>{a->r, a->y, a->M, a->N}, st);
+  return launch_gemm<true, false>(p1, EpiRowScale<false>{a->r, a->y, a->M, a->N}, st);
+}
+
+// ------------------------------------------------- no-allocation forward
+// coda_fwd_noalloc keeps its partials P in this file-scope device array (one copy per GPU, held until
+// the process ends) instead of a caller's workspace. In host code `scratch` names a host-side stand-in,
+// not the device memory: every use goes through the address hipGetSymbolAddress returns for the
+// device that runs the call, looked up once per device and kept.
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the device that `st` belongs to.
+hipError_t scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = st == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = 0;
+      if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;   // the lookup is per current device
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace coda
 
 using namespace coda;
@@ -1370,35 +1443,8 @@ coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size
   coda_status_t v = coda_validate_fwd(a, ws, ws_bytes);
   if (v != CODA_OK) return v;
   if (stage < 0 || stage >= CODA_FWD_STAGES) return CODA_ERR_ARG;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* P = reinterpret_cast<float*>(ws);
-  const int64_t pcols = ssq_cols(a->D);
-  if (stage == 0) {  // GEMM0 x @ W0 with the residual / h / g / sum-of-squares epilogue
-    const KSplit ks = gemm0_split(a->M, a->K0, a->D);
-    if (ks.S > 1) {  // few rows: split the contraction, then a row kernel does the epilogue's work
-      float* part = reinterpret_cast<float*>(ws_at(ws, fwd_ws_p(a->M, a->D)));
-      const int64_t sstride = a->M * a->D;
-      const GemmShape pp{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D, ks.kslice};
-      hipError_t e = launch_gemm<true, false>(pp, EpiPartialF32{part, a->D, a->M, sstride}, st);
-      if (e != hipSuccess) return CODA_ERR_HIP;
-      hipLaunchKernelGGL(splitk_residual_kernel, dim3(unsigned(ceil_div(a->D, 1024)), unsigned(a->M)), dim3(256), 0, st,
-                         (const float*)part, int(ks.S), sstride, (const uint16_t*)a->z, (const uint16_t*)a->gamma,
-                         (uint16_t*)a->h, (uint16_t*)a->g, P, a->D, pcols);
-      return to_status(hipGetLastError());
-    }
-    const GemmShape p0{a->M, a->D, a->K0, a->x, a->K0, a->W0, a->D};
-    return to_status(launch_gemm<true, false>(
-        p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st));
-  }
-  if (stage == 1) {  // partial sums of squares -> r
-    hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, kCombineRows))), dim3(256), 0, st, P, a->r, a->M,
-                       pcols, float(a->D), a->eps);
-    return to_status(hipGetLastError());
-  }
-  // GEMM1 g @ W1 with the row-scale epilogue
-  const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
-  if (a->y_dtype == CODA_F32) return to_status(launch_gemm<true, false>(p1, EpiRowScale<true>{a->r, a->y, a->M, a->N}, st));
-  return to_status(launch_gemm<true, false>(p1, EpiRowScale<false>{a->r, a->y, a->M, a->N}, st));
+  float* part = reinterpret_cast<float*>(ws_at(ws, fwd_ws_p(a->M, a->D)));
+  return to_status(fwd_stage(stage, a, reinterpret_cast<float*>(ws), part, static_cast<hipStream_t>(stream)));
 }
 
 coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {
@@ -1406,6 +1452,19 @@ coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void
     const coda_status_t v = coda_fwd_stage(s, a, ws, ws_bytes, stream);
     if (v != CODA_OK) return v;
   }
+  return CODA_OK;
+}
+
+coda_status_t coda_fwd_noalloc(const coda_fwd_args_t* a, void* stream) {
+  coda_status_t v = coda_validate_fwd_noalloc(a);
+  if (v != CODA_OK) return v;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* P = nullptr;
+  if (scratch_address(st, &P) != hipSuccess) return CODA_ERR_HIP;
+  // P is written in full (every row's D / 64 partials) by stage 0 before stage 1 reads it, so the
+  // previous call's contents need no clearing
+  for (int s = 0; s < CODA_FWD_STAGES; ++s)
+    if (fwd_stage(s, a, static_cast<float*>(P), nullptr, st) != hipSuccess) return CODA_ERR_HIP;
   return CODA_OK;
 }
 
