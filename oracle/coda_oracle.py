@@ -86,6 +86,12 @@ and for L = sum_i dloss_i loss_i:
 The max shift is the textbook way to write log-sum-exp (exact in real
 arithmetic); the oracle takes it over the whole row, with no tiling.
 
+Rounded operands. Where a kernel must round an operand to bf16 before a contraction (the weight
+gradient's r_i g_ij, which carries r on its contraction index; a gradient produced in fp32 and stored
+in bf16 before the next product), ``bf16_round`` gives that operand (fp32, then bf16 round-to-nearest-
+even) and ``backward(round_rg=True, s=...)`` the backward on it, so a test can check the contraction
+itself on the very operand the kernel uses, beside the exact definition above.
+
 Matrix products use numpy's float64 matmul as a library primitive. Row subsets
 (``rows``) and column subsets are supported because rows of the forward are
 independent and the large configurations are checked on seeded samples.
@@ -117,6 +123,17 @@ def _take(t, rows=None, cols=None) -> np.ndarray:
     return f64(a)
 
 
+def bf16_round(x) -> np.ndarray:
+    """The bf16 value a kernel stores for x when it computes x in fp32: x rounded to fp32, then to the
+    nearest bf16 with ties to even (the top 16 bits of the fp32 word after adding 0x7fff plus the
+    lowest kept bit); NaN stays NaN and +-inf stays +-inf. Returned widened to float64."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    nan = np.isnan(x32)
+    u = np.where(nan, np.uint64(0x7FC00000), x32.view(np.uint32).astype(np.uint64))
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return np.where(nan, np.nan, r.view(np.float32).astype(np.float64))
+
+
 def gemm(A, B) -> np.ndarray:
     """Plain product C = A @ B in float64."""
     return f64(A) @ f64(B)
@@ -146,12 +163,18 @@ def forward(x, W0, z, gamma, W1, eps: float, rows=None, chunk: int = 1024) -> di
     return {k: np.concatenate(v, axis=0) for k, v in out.items()}
 
 
-def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=None) -> dict:
+def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=None, s=None,
+             round_rg=False) -> dict:
     """Backward of the chain for the saved set (h, g, y, r).
 
     * ``rows``: rows i for which s_i, G_i and da_i are returned (all when None).
     * ``dgamma_cols``: columns j of dgamma (sums over *all* M rows; all when None).
     * ``dw1_cols``: columns n of dW1 (all D rows of each; all when None).
+    * ``s``: the row statistic [M] to use instead of sum_n dY_in y_in (for a dY that is itself a
+      rounded copy of the gradient s was taken from, as when dY is produced in fp32 and stored in bf16).
+    * ``round_rg``: dW1 from the operand r_i g_ij rounded once to bf16 (``bf16_round`` of the fp32
+      product), the form the weight gradient takes when r lies on its contraction index; otherwise
+      the exact r_i g_ij.
     """
     W1d, gd, rd = f64(W1), f64(gamma), f64(r)
     M, N = dY.shape
@@ -161,7 +184,7 @@ def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=No
 
     # rows: s, G, da
     dYr, yr, hr = _take(dY, ridx), _take(y, ridx), _take(h, ridx)
-    s = (dYr * yr).sum(axis=1)
+    s = (dYr * yr).sum(axis=1) if s is None else f64(s)[ridx]
     G = dYr @ W1d.T
     rr = rd[ridx]
     da = (rr[:, None] * gd[None, :]) * G - ((s * rr * rr) / D)[:, None] * hr
@@ -182,7 +205,10 @@ def backward(dY, y, h, g, r, gamma, W1, rows=None, dgamma_cols=None, dw1_cols=No
     dW1 = np.zeros((D, len(nc)))
     for c0 in range(0, M, 2048):
         blk = np.arange(c0, min(M, c0 + 2048))
-        gr = _take(g, blk) * rd[blk, None]
+        if round_rg:   # the fp32 product of the fp32 r and the bf16 g, rounded to bf16
+            gr = bf16_round(rd[blk, None].astype(np.float32) * _take(g, blk).astype(np.float32))
+        else:
+            gr = _take(g, blk) * rd[blk, None]
         dW1 += gr.T @ _take(dY, blk, nc)
     out["dW1"] = dW1
     return out

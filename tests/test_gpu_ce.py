@@ -4,8 +4,8 @@ oracle on one MI355X.
 Forward: lse and loss at fp32-level agreement (the logits are fp32 accumulations
 of exact bf16 products and never rounded); ignored rows have loss exactly 0.
 Backward, fed the oracle's lse: dlogits faithfully rounded to bf16 (within one
-ulp, +1e-4 rms); dh and dW within 1e-4 rms plus the first-order effect of that
-rounding of dlogits before the two products.
+ulp, +1e-4 rms); dh and dW within 1e-4 rms plus a statistical bound
+(metrics.SIGMA_K sigma) of that rounding of dlogits before the two products.
 
 The unfused baseline (coda_unfused_ref: fp32 logits stored, then row kernels) is
 held to the same bounds; its logits come from the same mainloop, so its backward
@@ -64,15 +64,15 @@ def check_bwd(out, host, lse_ref, rows=None, vrows=None):
     dL = rsel(out["dlogits"], rows)
     dh = rsel(out["dh"], rows)
     dW = out["dW"].cpu() if vrows is None else out["dW"].index_select(0, torch.as_tensor(vrows, device=DEV)).cpu()
-    # first-order bounds of rounding dlogits to bf16 before the products; dW's rows v
-    # need dlogits[:, v] over all M rows
-    a_dh = mt.bf16_ulp(ref["dlogits"]) @ np.abs(mt.f64(W))
+    # statistical bounds (metrics.SIGMA_K sigma) of rounding dlogits to bf16 before the products; dW's
+    # rows v need dlogits[:, v] over all M rows
+    s_dh = mt.rounding_sigma(mt.half_ulp_sq_over_3(ref["dlogits"]), W)
     vcols = np.arange(W.shape[0]) if vrows is None else np.asarray(vrows)
     dLv = np.concatenate([orc.lm_head_dlogits(h, W, t, lse_ref, dloss, rows=np.arange(c0, min(h.shape[0], c0 + 512)), vcols=vcols)
                           for c0 in range(0, h.shape[0], 512)])
-    a_dW = mt.bf16_ulp(dLv).T @ np.abs(mt.f64(h))
+    s_dW = mt.rounding_sigma(mt.half_ulp_sq_over_3(dLv).T, h)
     e = {"dlogits": mt.bf16_faithful(dL, ref["dlogits"], TOL),
-         "dh": mt.within_allowance(dh, ref["dh"], a_dh, TOL), "dW": mt.within_allowance(dW, ref["dW"], a_dW, TOL)}
+         "dh": mt.within_sigma(dh, ref["dh"], s_dh, TOL), "dW": mt.within_sigma(dW, ref["dW"], s_dW, TOL)}
     print("  " + "  ".join(f"{k} |d|/bound={v:.3e}" for k, v in e.items()) +
           f"  (dh max|d|/rms={mt.normwise(dh, ref['dh']):.3e}, dW max|d|/rms={mt.normwise(dW, ref['dW']):.3e})")
     ign = torch.as_tensor(~((rsel(t, rows) >= 0) & (rsel(t, rows) < W.shape[0])))

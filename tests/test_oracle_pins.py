@@ -182,6 +182,66 @@ def test_gemm_exact_in_every_storage_layout(a_col, b_col, shape):
         orc.gemm(A_view, B_view.t())                           # a transposed B cannot multiply
 
 
+# ----------------------------------------------------------- bf16 rounding
+
+def test_bf16_round_matches_torch_conversion():
+    """bf16_round against torch's float32 -> bfloat16 conversion (a separate implementation) on random
+    values over the whole exponent range, exact ties with an even and an odd kept bit, subnormals,
+    +-0, +-inf, NaN and the largest floats (which round to inf); float64 inputs go through float32
+    first, as a kernel's fp32 value does."""
+    g = np.random.default_rng(0)
+    bits = g.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    ties = (g.integers(0, 2 ** 16, size=4000, dtype=np.uint64).astype(np.uint32) << 16) | np.uint32(0x8000)
+    special = np.array([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000,
+                        0x00000001, 0x00008000, 0x00018000, 0x007FFFFF, 0x3F808000, 0x3F818000], dtype=np.uint32)
+    x32 = np.concatenate([bits, ties, special]).view(np.float32)
+    want = torch.from_numpy(x32.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.bf16_round(x32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    x64 = g.standard_normal(100000) * 10.0 ** g.integers(-30, 30, size=100000)
+    want64 = torch.from_numpy(x64).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.bf16_round(x64), want64)
+
+
+def test_backward_rounded_operand_and_given_s():
+    """The backward's two options: round_rg (dW1 from bf16(r g)) equals the exact dW1 when r g is a bf16
+    value already (r a power of two), and otherwise differs from it by exactly (bf16(r g) - r g)^T dY,
+    with the rounding computed by torch (within the first-order bound sum_i ulp(r g)/2 |dY|); a given s
+    equal to sum dY y changes nothing, and da is affine in s with slope -r^2 h / D."""
+    M, D, N = 40, 16, 24
+    gen = torch.Generator().manual_seed(3)
+    bf = torch.bfloat16
+    dY, y = torch.randn(M, N, generator=gen).to(bf), torch.randn(M, N, generator=gen).to(bf)
+    h = torch.randn(M, D, generator=gen).to(bf)
+    gamma = (1 + 0.1 * torch.randn(D, generator=gen)).to(bf)
+    g = (h.double() * gamma.double()).to(bf)
+    W1 = (torch.randn(D, N, generator=gen) / 4).to(bf)
+    r2 = torch.full((M,), 0.5, dtype=torch.float32)
+    a = orc.backward(dY, y, h, g, r2, gamma, W1)
+    b = orc.backward(dY, y, h, g, r2, gamma, W1, round_rg=True)
+    assert np.array_equal(a["dW1"], b["dW1"])
+    r = (0.5 + torch.rand(M, generator=gen)).to(torch.float32)
+    a = orc.backward(dY, y, h, g, r, gamma, W1)
+    b = orc.backward(dY, y, h, g, r, gamma, W1, round_rg=True)
+    rg32 = r[:, None] * g.float()                       # torch's fp32 product
+    delta = (rg32.to(bf).double() - r.double()[:, None] * g.double()).numpy()
+    assert np.allclose(b["dW1"] - a["dW1"], delta.T @ dY.double().numpy(), rtol=0, atol=1e-12)
+    rg = (r.double()[:, None] * g.double()).abs().numpy()
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(rg, 2.0 ** -126))) - 7)
+    assert np.all(np.abs(b["dW1"] - a["dW1"]) <= (0.5 * ulp).T @ np.abs(dY.double().numpy()) + 1e-12)
+    assert np.abs(b["dW1"] - a["dW1"]).max() > 0
+    c = orc.backward(dY, y, h, g, r, gamma, W1, s=a["s"])
+    for k in ("s", "G", "da", "dgamma", "dW1"):
+        assert np.array_equal(c[k], a[k]), k
+    s2 = a["s"] + np.arange(M)
+    d = orc.backward(dY, y, h, g, r, gamma, W1, s=s2)
+    assert np.allclose(d["da"] - a["da"], -(np.arange(M) * r.double().numpy() ** 2)[:, None] * h.double().numpy() / D,
+                       rtol=0, atol=1e-12)
+    assert np.array_equal(d["dgamma"], a["dgamma"]) and np.array_equal(d["dW1"], a["dW1"])
+
+
 # --------------------------------------------------------- library special case
 
 def _rand_problem(M, K0, D, N, seed, eps=1e-5):
@@ -571,7 +631,12 @@ def test_subsets_match_full_computation():
 
 # ---------------------------------------------------------------- hand-worked
 
-@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
 def test_golden_hand_worked(case):
     a = {k: np.array(v, dtype=np.float64) for k, v in case.items() if isinstance(v, list)}
     o = orc.forward(a["x"], a["W0"], a["z"], a["gamma"], a["W1"], case["eps"])
