@@ -37,7 +37,8 @@
  *     Calls on one stream with distinct outputs/workspaces are independent; the
  *     library keeps no global state.
  *   - Shapes: 1 <= M <= 2^22 (any value; the last row tile is masked); K0, D
- *     and N are multiples of 256 in [256, 2^20]; and every GEMM of the call has
+ *     and N are multiples of 64 in [64, 2^20] (a last column tile narrower than
+ *     256 is masked per 64 columns); and every GEMM of the call has
  *     at most 2^23 output tiles of 256 x 256 (its launch stays within 2^32
  *     work-items). Anything else returns CODA_ERR_SHAPE.
  *   - eps must be finite and > 0.
@@ -155,7 +156,7 @@ typedef struct {
  *   in : dh [M,D] bf16, x [M,K0] bf16, W0 [K0,D] bf16.
  *   out: dx [M,K0] in dx_dtype, dW0 [K0,D] in dW0_dtype.
  * Two launches of the shared mainloop with store-only epilogues; no workspace.
- * Shapes as for coda_fwd (K0 and D multiples of 256, any M >= 1). */
+ * Shapes as for coda_fwd (K0 and D multiples of 64, any M >= 1). */
 typedef struct {
   int64_t M, K0, D;
   const void* dh;
@@ -174,7 +175,7 @@ typedef struct {
  *     o_if = silu(y_i,2f) * y_i,2f+1,   silu(v) = v / (1 + exp(-v)).
  * The forward is coda_fwd with GEMM1's epilogue also emitting o (from the fp32
  * y; y itself is still stored, in bf16 as the backward takes it: chain.y_dtype
- * must be CODA_BF16). N must be a multiple of 512. Workspace: as coda_fwd
+ * must be CODA_BF16). N must be a multiple of 128. Workspace: as coda_fwd
  * (coda_workspace_bytes(CODA_OP_FWD_SWIGLU, ...)). */
 typedef struct {
   coda_fwd_args_t chain; /* as for coda_fwd */
@@ -197,7 +198,7 @@ typedef struct {
  *        gamma [D] bf16; W1 [D,N] bf16.
  *   out: dY [M,N] bf16, da [M,D] in da_dtype, dgamma [D] f32, dW1 [D,N] in
  *        dW1_dtype, dW2 [F,E] in dW2_dtype, s [M] f32.
- * N a multiple of 512, E a multiple of 256 in [256, 2^20]. */
+ * N a multiple of 128, E a multiple of 64 in [64, 2^20]. */
 typedef struct {
   int64_t M, D, N, E;
   const void* dOut;
@@ -230,7 +231,7 @@ typedef struct {
  * The logits GEMM's epilogue reduces each (row, 64-column) tile to its max m and
  * sum exp(logit - m) and picks out the target logit; a row kernel combines the
  * tile statistics in a fixed order. A target outside [0, V) marks an ignored row:
- * its loss is 0 (lse is still written). D and V multiples of 256 in [256, 2^20]
+ * its loss is 0 (lse is still written). D and V multiples of 64 in [64, 2^20]
  * (Llama-3's V = 128256 = 501 * 256).
  *   in : h [M,D] bf16, W [V,D] bf16, targets [M] int64.
  *   out: lse [M] f32, loss [M] f32 (per row; a mean is the caller's sum / count);
@@ -284,7 +285,7 @@ typedef enum {
 /* Plain GEMM C[M,N] = A[M,K] @ B[K,N] with bf16 operands and fp32 accumulation,
  * output in c_dtype with leading dimension ldc. This is the mainloop every
  * fused kernel shares, with a store-only epilogue; the unfused baseline is
- * built from it. M >= 1, N and K multiples of 256, lda/ldb/ldc >= the
+ * built from it. M >= 1, N and K multiples of 64, lda/ldb/ldc >= the
  * contiguous extent and multiples of 8. */
 typedef struct {
   int64_t M, N, K;
@@ -304,11 +305,12 @@ typedef struct {
  * fused backward holds bf16(r*g) transposed, [D, M rounded up to 64], and the dgamma column partials (the
  * SwiGLU backward also the partial sums of s); the unfused baseline also holds
  * its materialised intermediates. When the backward's data-gradient GEMM has
- * fewer than 192 tiles of 256 x 256 (few rows M, e.g. a data-parallel shard),
+ * fewer than 192 tiles of 256 x 256 (tiles = ceil(M/256) * ceil(D/256); few rows M, e.g. a
+ * data-parallel shard),
  * its contraction over N is split into S = min(ceil(256 / tiles), 8, N / 256)
  * slices and the workspace also holds their fp32 partial products [S, M, D]
- * (the dgamma partials then have ceil(M / 32) rows instead of ceil(M / 128)).
- * The forward splits GEMM0 by the same rule (tiles = ceil(M/256) * D/256); its
+ * (the dgamma partials then have ceil(M / 8) rows instead of ceil(M / 128)).
+ * The forward splits GEMM0 by the same rule (tiles = ceil(M/256) * ceil(D/256)); its
  * workspace, sized without K0, then also holds min(ceil(256 / tiles), 8) fp32
  * partial products [., M, D]. */
 size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N);

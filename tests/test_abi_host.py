@@ -86,7 +86,7 @@ def test_workspace_sizes():
         return (v + 255) // 256 * 256
     M, D, N = 300, 512, 768
     def fwd_ws(M, D):  # P [M, D/64], and min(ceil(256 / tiles), 8) split-K partials when GEMM0 has < 192 tiles
-        tiles = math.ceil(M / 256) * (D // 256)
+        tiles = math.ceil(M / 256) * math.ceil(D / 256)
         S = 1 if tiles >= 192 else min(math.ceil(256 / tiles), 8)
         return a256(M * (D // 64) * 4) + (a256(S * M * D * 4) if S > 1 else 0)
     assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == fwd_ws(M, D) == a256(M * 8 * 4) + a256(8 * M * D * 4)
@@ -107,13 +107,16 @@ def test_workspace_sizes():
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD, 0, D, N) == 0
     assert L.workspace_bytes(L.CODA_OP_FWD, M, 100, N) == 0
-    N2 = 1024  # SwiGLU needs N % 512 == 0; its backward adds the s partials Ps[M, (N/2)/64]
+    N2 = 1024  # SwiGLU needs N % 128 == 0; its backward adds the s partials Ps[M, (N/2)/64]
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
     S2, _ = dgrad_split(M, D, N2)
     bwd2 = gr_bytes(M, D) + a256(math.ceil(M / (8 if S2 > 1 else 128)) * D * 4) + (a256(S2 * M * D * 4) if S2 > 1 else 0)
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2 // 64) * 4)
-    assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, N) == 0
-    assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N) == 0
+    assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, 832) == 0      # 13 x 64: not a multiple of 128
+    assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, 832) == 0
+    # multiples of 64 (not of 256): P [M, 5] for D = 320, and a ragged column tile
+    assert L.workspace_bytes(L.CODA_OP_FWD, 8192, 320, 576) == a256(8192 * 5 * 4) + a256(4 * 8192 * 320 * 4)  # 64 tiles: 4 slices
+    assert L.workspace_bytes(L.CODA_OP_FWD, 65536, 320, 576) == a256(65536 * 5 * 4) # 256 x 2 tiles: no split
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2) * 2)
     V = 128256  # cross-entropy: tile statistics (m, l) [M, V/64] and the target logits [M]
@@ -128,7 +131,7 @@ def test_workspace_sizes():
 
 def dgrad_split(M, D, N):
     """The documented split-K rule of the backward's data-gradient GEMM: (slices, columns per slice)."""
-    tiles = math.ceil(M / 256) * (D // 256)
+    tiles = math.ceil(M / 256) * math.ceil(D / 256)
     S = min(math.ceil(256 / tiles), 8, N // 64 // 4)
     if tiles >= 192 or S < 2:
         return 1, 0
@@ -168,7 +171,9 @@ def test_validate_fwd_ok_and_errors():
     for f in ("x", "W0", "z", "gamma", "W1", "h", "g", "r", "y"):
         assert vfwd(_fwd(**{f: None})) == L.CODA_ERR_NULL, f
         assert vfwd(_fwd(**{f: ctypes.c_void_p(A + 8)})) == L.CODA_ERR_ALIGN, f
-    for k, v in (("M", 0), ("M", -5), ("M", (1 << 22) + 1), ("K0", 128), ("D", 300), ("N", 0), ("N", 1 << 21)):
+    assert vfwd(_fwd(K0=192, D=320, N=576)) == L.CODA_OK   # multiples of 64
+    for k, v in (("M", 0), ("M", -5), ("M", (1 << 22) + 1), ("K0", 100), ("K0", 32), ("D", 300), ("N", 0),
+                 ("N", 1 << 21), ("N", 96)):
         assert vfwd(_fwd(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
     # every GEMM's launch stays within 2^32 work-items: 2^14 row tiles x 2^12 column tiles x 512 is too many
     assert vfwd(_fwd(M=1 << 22, N=1 << 20)) == L.CODA_ERR_SHAPE
@@ -189,7 +194,8 @@ def test_validate_bwd_ok_and_errors():
     for f in ("dY", "y", "h", "g", "r", "gamma", "W1", "da", "dgamma", "dW1", "s"):
         assert vbwd(_bwd(**{f: None})) == L.CODA_ERR_NULL, f
         assert vbwd(_bwd(**{f: ctypes.c_void_p(A + 2)})) == L.CODA_ERR_ALIGN, f
-    for k, v in (("M", 0), ("D", 64), ("N", 1000)):
+    assert vbwd(_bwd(D=64, N=320)) == L.CODA_OK
+    for k, v in (("M", 0), ("D", 96), ("N", 1000)):
         assert vbwd(_bwd(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
     assert vbwd(_bwd(da_dtype=2)) == L.CODA_ERR_ARG
     assert vbwd(_bwd(dW1_dtype=-1)) == L.CODA_ERR_ARG
@@ -257,7 +263,8 @@ def test_validate_swiglu():
     assert vf(_fsw(o=None)) == L.CODA_ERR_NULL
     assert vf(_fsw(o=ctypes.c_void_p(A + 4))) == L.CODA_ERR_ALIGN
     assert vf(_fsw(o_dtype=5)) == L.CODA_ERR_ARG
-    assert vf(_fsw(chain=_fwd(N=768))) == L.CODA_ERR_SHAPE        # N not a multiple of 512
+    assert vf(_fsw(chain=_fwd(N=832))) == L.CODA_ERR_SHAPE        # N not a multiple of 128
+    assert vf(_fsw(chain=_fwd(N=640))) == L.CODA_OK
     assert vf(_fsw(chain=_fwd(N=1024, y_dtype=L.CODA_F32))) == L.CODA_ERR_ARG  # y is saved in bf16
     assert vf(_fsw(chain=_fwd(N=1024, eps=0.0))) == L.CODA_ERR_ARG
     need = L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, 64, 256, 1024)
@@ -269,7 +276,7 @@ def test_validate_swiglu():
     for f in ("dOut", "W2", "o", "y", "h", "g", "r", "gamma", "W1", "dY", "da", "dgamma", "dW1", "dW2", "s"):
         assert vb(_bsw(**{f: None})) == L.CODA_ERR_NULL, f
         assert vb(_bsw(**{f: ctypes.c_void_p(A + 8)})) == L.CODA_ERR_ALIGN, f
-    for k, v in (("M", 0), ("N", 768), ("N", 256), ("E", 300), ("E", 0), ("D", 128)):
+    for k, v in (("M", 0), ("N", 832), ("N", 320), ("E", 300), ("E", 0), ("D", 160)):
         assert vb(_bsw(**{k: v})) == L.CODA_ERR_SHAPE, (k, v)
     for k in ("da_dtype", "dW1_dtype", "dW2_dtype"):
         assert vb(_bsw(**{k: 4})) == L.CODA_ERR_ARG, k
@@ -280,7 +287,7 @@ def test_validate_swiglu():
     un = L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, 300, 256, 1024)
     assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw()), WS, un) == L.CODA_OK
     assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw()), WS, un - 1) == L.CODA_ERR_WORKSPACE
-    assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw(N=768)), WS, un) == L.CODA_ERR_SHAPE
+    assert lib.coda_validate_unfused(L.CODA_OP_BWD_SWIGLU, ctypes.byref(_bsw(N=832)), WS, un) == L.CODA_ERR_SHAPE
     assert lib.coda_validate_unfused(L.CODA_OP_FWD_SWIGLU, ctypes.byref(_fsw()), WS, 1 << 30) == L.CODA_OK
     assert lib.coda_unfused_ref(L.CODA_OP_FWD_SWIGLU, ctypes.byref(_fsw(o=None)), WS, 1 << 30, None) == L.CODA_ERR_NULL
     # rejected before any launch
@@ -295,7 +302,7 @@ def test_validate_cross_entropy():
     assert lib.coda_validate_ce_fwd(ctypes.byref(f), WS, need) == L.CODA_OK
     assert lib.coda_validate_ce_fwd(ctypes.byref(f), WS, need - 1) == L.CODA_ERR_WORKSPACE
     assert lib.coda_validate_ce_fwd(None, WS, need) == L.CODA_ERR_NULL
-    for k, v, want in (("M", 0, L.CODA_ERR_SHAPE), ("V", 1000, L.CODA_ERR_SHAPE), ("D", 128, L.CODA_ERR_SHAPE),
+    for k, v, want in (("M", 0, L.CODA_ERR_SHAPE), ("V", 1000, L.CODA_ERR_SHAPE), ("D", 160, L.CODA_ERR_SHAPE),
                        ("targets", None, L.CODA_ERR_NULL), ("loss", ctypes.c_void_p(A + 4), L.CODA_ERR_ALIGN)):
         g = L.CeFwdArgs.from_buffer_copy(f)
         setattr(g, k, v)

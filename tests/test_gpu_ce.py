@@ -30,6 +30,7 @@ SMALL = {
     "ragged": dict(M=300, D=512, V=1280),
     "one_row": dict(M=1, D=256, V=256),
     "llama_vocab": dict(M=64, D=256, V=inputs.LM_VOCAB),
+    "dims64": dict(M=300, D=320, V=576),                  # sizes in multiples of 64
 }
 
 

@@ -33,9 +33,8 @@ def to_dev(d):
 
 @pytest.mark.parametrize("a_layout", [L.CODA_ROW, L.CODA_COL], ids=["A_row", "A_col"])
 @pytest.mark.parametrize("b_layout", [L.CODA_ROW, L.CODA_COL], ids=["B_row", "B_col"])
-@pytest.mark.parametrize("M", [320, 1])
-def test_gemm_mainloop_layouts(a_layout, b_layout, M):
-    N, K = 512, 768
+@pytest.mark.parametrize("M,N,K", [(320, 512, 768), (1, 512, 768), (320, 576, 448)])
+def test_gemm_mainloop_layouts(a_layout, b_layout, M, N, K):
     announce(f"coda_gemm M={M} N={N} K={K} a_layout={a_layout} b_layout={b_layout}")
     g = torch.Generator().manual_seed(11)
     Am = torch.randn(M, K, generator=g).to(torch.bfloat16)     # logical A [M, K]
@@ -63,6 +62,10 @@ FWD_SMALL = {
     "one_row": dict(M=1, K0=256, D=256, N=256),
     "k0_ne_d": dict(M=130, K0=768, D=256, N=512),
     "deep_k0": dict(M=64, K0=1024, D=256, N=512),     # GEMM0 split over K0 into 4 slices
+    # sizes in multiples of 64: a last column tile of 64 (D) or 64 (N) live columns, K0 of 3 K steps
+    "dims64": dict(M=300, K0=192, D=320, N=576),
+    "dims64_split": dict(M=64, K0=1088, D=320, N=576),      # GEMM0 in 4 slices, the last one 2 K steps
+    "dims64_rows": dict(M=24576, K0=192, D=320, N=576),     # 192 GEMM0 tiles: the fused epilogue, unsplit
 }
 
 
@@ -208,6 +211,8 @@ BWD_SMALL = {
     "ragged": dict(M=300, K0=256, D=512, N=768),
     "one_row": dict(M=1, K0=256, D=256, N=256),
     "two_k_steps": dict(M=100, K0=256, D=256, N=512),  # dW1 contracts over two K steps (rows padded to 128)
+    "dims64": dict(M=300, K0=192, D=320, N=576),          # the data gradient split in 2 slices
+    "dims64_rows": dict(M=24576, K0=192, D=320, N=576),   # unsplit: the last column tile has one live wave
 }
 
 
@@ -334,6 +339,7 @@ BWD0_SMALL = {
     "tiny": dict(M=64, K0=256, D=256),
     "ragged": dict(M=300, K0=512, D=256),
     "one_row": dict(M=1, K0=256, D=512),
+    "dims64": dict(M=300, K0=192, D=320),
 }
 
 
@@ -437,9 +443,9 @@ def guards_intact(buf):
     return bool(torch.all(g == 0x5A).item())
 
 
-@pytest.mark.parametrize("M", [300, 1])
-def test_no_writes_outside_outputs(M):
-    c = dict(FWD_SMALL["ragged"], M=M)
+@pytest.mark.parametrize("name,M", [("ragged", 300), ("ragged", 1), ("dims64", 300), ("dims64_rows", 24576)])
+def test_no_writes_outside_outputs(name, M):
+    c = dict(FWD_SMALL[name], M=M)
     announce(f"canaries coda_fwd/coda_bwd {c}")
     inp = to_dev(inputs.forward_inputs(**c, seed=2))
     D, N = c["D"], c["N"]

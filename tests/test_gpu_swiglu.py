@@ -26,6 +26,7 @@ SMALL = {
     "tiny": dict(M=64, K0=256, D=256, N=512, E=256),
     "ragged": dict(M=300, K0=256, D=512, N=1024, E=768),
     "one_row": dict(M=1, K0=256, D=256, N=512, E=256),
+    "dims64": dict(M=300, K0=192, D=320, N=640, E=192),   # sizes in multiples of 64 (N of 128)
 }
 
 

@@ -16,7 +16,7 @@ bool dim_ok(int64_t v) { return v >= kDimQuantum && v <= kMaxDim && v % kDimQuan
 bool rows_ok(int64_t M) { return M >= 1 && M <= kMaxRows; }
 
 // A GEMM's grid (one 512-thread block per 256 x 256 output tile) fits a launch: at most 2^32 - 1 work-items.
-bool grid_ok(int64_t rows, int64_t cols) { return ceil_div(rows, kBM) * (cols / kBN) * kThreads <= 0xFFFFFFFFll; }
+bool grid_ok(int64_t rows, int64_t cols) { return ceil_div(rows, kBM) * ceil_div(cols, kBN) * kThreads <= 0xFFFFFFFFll; }
 
 bool dtype_ok(coda_dtype_t t) { return t == CODA_BF16 || t == CODA_F32; }
 
@@ -84,7 +84,7 @@ coda_status_t validate_bwd_swiglu_common(const coda_bwd_swiglu_args_t* a) {
                       a->dW1, a->dW2, a->s};
   coda_status_t st = check_ptrs(ps, 15);
   if (st != CODA_OK) return st;
-  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 512) return CODA_ERR_SHAPE;
+  if (!rows_ok(a->M) || !dim_ok(a->D) || !dim_ok(a->N) || !dim_ok(a->E) || a->N % 128) return CODA_ERR_SHAPE;
   if (!grid_ok(a->M, a->D) || !grid_ok(a->D, a->N) || !grid_ok(a->M, a->N / 2) || !grid_ok(a->N / 2, a->E))
     return CODA_ERR_SHAPE;
   if (!dtype_ok(a->da_dtype) || !dtype_ok(a->dW1_dtype) || !dtype_ok(a->dW2_dtype)) return CODA_ERR_ARG;
@@ -102,12 +102,12 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
     case CODA_OP_BWD: return dim_ok(N) ? bwd_ws(M, D, N) : 0;
     case CODA_OP_UNFUSED_FWD: return unfused_fwd_ws(M, D);
     case CODA_OP_UNFUSED_BWD: return unfused_bwd_ws(M, D);
-    case CODA_OP_FWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? fwd_ws(M, D) : 0;
-    case CODA_OP_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? bwd_swiglu_ws(M, D, N) : 0;
+    case CODA_OP_FWD_SWIGLU: return (dim_ok(N) && N % 128 == 0) ? fwd_ws(M, D) : 0;
+    case CODA_OP_BWD_SWIGLU: return (dim_ok(N) && N % 128 == 0) ? bwd_swiglu_ws(M, D, N) : 0;
     case CODA_OP_CE_FWD: return dim_ok(N) ? ce_fwd_ws(M, N) : 0;
     case CODA_OP_CE_BWD: return 0;
-    case CODA_OP_UNFUSED_FWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? fwd_ws(M, D) : 0;
-    case CODA_OP_UNFUSED_BWD_SWIGLU: return (dim_ok(N) && N % 512 == 0) ? unfused_bwd_swiglu_ws(M, D, N) : 0;
+    case CODA_OP_UNFUSED_FWD_SWIGLU: return (dim_ok(N) && N % 128 == 0) ? fwd_ws(M, D) : 0;
+    case CODA_OP_UNFUSED_BWD_SWIGLU: return (dim_ok(N) && N % 128 == 0) ? unfused_bwd_swiglu_ws(M, D, N) : 0;
     case CODA_OP_UNFUSED_CE_FWD:
     case CODA_OP_UNFUSED_CE_BWD: return dim_ok(N) ? unfused_ce_ws(M, N) : 0;
     default: break;
@@ -194,7 +194,7 @@ coda_status_t coda_validate_fwd_swiglu(const coda_fwd_swiglu_args_t* a, const vo
   if (st != CODA_OK) return st;
   const void* ps[] = {a->o};
   if ((st = check_ptrs(ps, 1)) != CODA_OK) return st;
-  if (a->chain.N % 512) return CODA_ERR_SHAPE;
+  if (a->chain.N % 128) return CODA_ERR_SHAPE;
   if (a->chain.y_dtype != CODA_BF16 || !dtype_ok(a->o_dtype)) return CODA_ERR_ARG;
   return CODA_OK;
 }

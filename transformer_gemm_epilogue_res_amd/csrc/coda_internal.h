@@ -16,8 +16,9 @@ constexpr int kWaveTileM = 128;
 constexpr int kWaveTileN = 64;
 constexpr int kThreads = 512;
 
-// K0, D and N must be multiples of this.
-constexpr int64_t kDimQuantum = 256;
+// K0, D and N must be multiples of this: the K step (every contraction runs whole K steps) and the
+// wave tile width (each wave's 64 output columns lie wholly inside or wholly past the last column).
+constexpr int64_t kDimQuantum = 64;
 // Largest accepted K0 / D / N and M (keeps every per-tile buffer offset < 2^31 and a
 // one-block-per-row launch of 512-thread blocks within 2^32 work-items); each GEMM's
 // grid is also checked against that limit.
@@ -53,7 +54,7 @@ struct KSplit {
   int64_t S, kslice;
 };
 inline KSplit dgrad_split(int64_t M, int64_t D, int64_t N) {
-  const int64_t tiles = ceil_div(M, kBM) * (D / kBN);
+  const int64_t tiles = ceil_div(M, kBM) * ceil_div(D, kBN);
   int64_t S = ceil_div(256, tiles);
   if (S > 8) S = 8;
   if (S > N / kBK / 4) S = N / kBK / 4;
@@ -65,7 +66,7 @@ inline KSplit dgrad_split(int64_t M, int64_t D, int64_t N) {
 // without K0 for S_max = min(ceil(256 / tiles), 8) slices; a call uses
 // S = min(S_max, K0 / 256) of them (at least four K steps each).
 inline int64_t gemm0_split_max(int64_t M, int64_t D) {
-  const int64_t tiles = ceil_div(M, kBM) * (D / kBN);
+  const int64_t tiles = ceil_div(M, kBM) * ceil_div(D, kBN);
   if (tiles >= 192) return 1;
   const int64_t S = ceil_div(256, tiles);
   return S > 8 ? 8 : S;

@@ -733,26 +733,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
   lds_char_t *stage, *aux;
   epi_regions(smem, wave, int(dceil_div(p.K, kBK)), stage, aux);
   f32x4_t acc[kTM][kTN];
+  // N is a multiple of the wave tile width (64), so a wave's columns lie wholly inside or wholly past
+  // N: in the last column tile, a wave past N runs the mainloop (its loads read zeros or other rows'
+  // values, in bounds) but writes nothing -- no output, no partial statistics.
+  const bool cols_in = nb < p.N;
   if (wave < 4) {
     mainloop<A_K, B_K, 0>(p, m0, n0, smem, acc, [&] {
       if constexpr (HasEarly<Epi>::value) epi.early(stage, aux, m0, nb, lane);
     });
-    if constexpr (HasEarly<Epi>::value) epi(acc, m0, nb, lane, stage, aux);
-    else epi(acc, m0, nb, lane, stage);
+    if (!cols_in) {
+      wait_vm0();
+    } else if constexpr (HasEarly<Epi>::value) {
+      epi(acc, m0, nb, lane, stage, aux);
+    } else {
+      epi(acc, m0, nb, lane, stage);
+    }
   } else {
     mainloop<A_K, B_K, 1>(p, m0, n0, smem, acc, [&] {
       if constexpr (HasEarly<Epi>::value) epi.early(stage, aux, m0 + kWaveTileM, nb, lane);
     });
-    if constexpr (HasEarly<Epi>::value) epi(acc, m0 + kWaveTileM, nb, lane, stage, aux);
-    else epi(acc, m0 + kWaveTileM, nb, lane, stage);
+    if (!cols_in) {
+      wait_vm0();
+    } else if constexpr (HasEarly<Epi>::value) {
+      epi(acc, m0 + kWaveTileM, nb, lane, stage, aux);
+    } else {
+      epi(acc, m0 + kWaveTileM, nb, lane, stage);
+    }
   }
 }
 
 // ------------------------------------------------------- small kernels
 
 // r_i = 1 / sqrt(sum_t P[i, t] / D + eps). Sixteen lanes per row, each summing
-// a strided quarter of the row's partials as float4 loads, then a fixed
-// butterfly over the 16 lanes: the summation order depends only on pcols.
+// a strided share of the row's partials (as float4 loads when the rows are
+// 16-byte aligned), then a fixed butterfly over the 16 lanes: the summation
+// order depends only on pcols.
 constexpr int kCombineRows = 16;  // rows per 256-thread block
 __global__ __launch_bounds__(256) void rms_combine_kernel(const float* P, float* r, int64_t M, int64_t pcols,
                                                           float D, float eps) {
@@ -760,10 +775,15 @@ __global__ __launch_bounds__(256) void rms_combine_kernel(const float* P, float*
   const int l = threadIdx.x & 15;
   float acc = 0.f;
   if (i < M) {
-    const float4* row = reinterpret_cast<const float4*>(P + i * pcols);
-    for (int64_t t = l; t < pcols / 4; t += 16) {
-      const float4 v = row[t];
-      acc += (v.x + v.y) + (v.z + v.w);
+    const float* row = P + i * pcols;
+    if ((pcols & 3) == 0) {  // D a multiple of 256: 16-byte rows
+      const float4* row4 = reinterpret_cast<const float4*>(row);
+      for (int64_t t = l; t < pcols / 4; t += 16) {
+        const float4 v = row4[t];
+        acc += (v.x + v.y) + (v.z + v.w);
+      }
+    } else {
+      for (int64_t t = l; t < pcols; t += 16) acc += row[t];
     }
   }
 #pragma unroll
@@ -1079,7 +1099,7 @@ __global__ __launch_bounds__(256) void splitk_residual_kernel(const float* part,
                                                               uint16_t* g, float* P, int64_t D, int64_t pcols) {
   const int64_t i = blockIdx.y;
   const int64_t j = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  const bool ok = j < D;  // uniform over each 16-thread chunk group (D is a multiple of 256)
+  const bool ok = j < D;  // uniform over each 16-thread chunk group (64 columns; D is a multiple of 64)
   float ssq = 0.f;
   if (ok) {
     float hv[4], zz[4], gm[4];
@@ -1237,7 +1257,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* G, con
 
 template <bool A_K, bool B_K, class Epi>
 hipError_t launch_gemm(const GemmShape& p, const Epi& epi, hipStream_t st) {
-  const int64_t blocks = ceil_div(p.M, kBM) * (p.N / kBN);
+  const int64_t blocks = ceil_div(p.M, kBM) * ceil_div(p.N, kBN);
   const int64_t slices = p.kslice > 0 ? ceil_div(p.K, p.kslice) : 1;
   hipLaunchKernelGGL((gemm_kernel<A_K, B_K, Epi>), dim3(unsigned(blocks), unsigned(slices)), dim3(kThreads), 0, st, p,
                      epi);

@@ -299,7 +299,7 @@ __device__ __forceinline__ void prio_low() { asm volatile("s_setprio 0" ::: "mem
 constexpr int kGroupM = CODA_GROUP_M;
 __device__ __forceinline__ void map_tile(int64_t M, int64_t N, int group_m, int& tile_m, int& tile_n) {
   const int tiles_m = int(dceil_div(M, kBM));
-  const int tiles_n = int(N / kBN);
+  const int tiles_n = int(dceil_div(N, kBN));
   const int nb = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + (b / 8) : b;
