@@ -14,7 +14,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
               its duration from HIP events recorded around it on its stream in a
               second, instrumented pass of the same K steps (the headline steps
               carry events only at the two ends of the timed region),
-  cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload.
+  cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload,
+  unfused, configs = each fused pass against its unfused baseline (and the tiny,
+              Llama-3 1B and 70B forwards), the two timed in alternating blocks so
+              that both run at the same power-limited clock.
 """
 from __future__ import annotations
 
@@ -145,16 +148,45 @@ def cpu_baseline(host, rows, ncols, total_rows, seed=0):
     t2 = time.perf_counter()
     orc.backward(host["dY"], y_s, h_s, g_s, r_s, host["gamma"], host["W1"], dgamma_cols=jc, dw1_cols=nc)
     t3 = time.perf_counter()
-    # forward; s, G, da of every row; dgamma (G recomputed on its columns) and dW1 on their columns
-    flops = 2 * R * (K0 * D + D * N) + 2 * R * N * D + 2 * R * N + 2 * R * N * cj + 2 * R * D * cn
+    # priced at the step's algorithmic work on this sub-batch (forward 2RK0D + 2RDN, backward 4RDN, the
+    # same count as the GPU value), not at the oracle's own arithmetic (it recomputes G for dgamma)
+    executed = 2 * R * (K0 * D + D * N) + 2 * R * N * D + 2 * R * N + 2 * R * N * cj + 2 * R * D * cn
+    flops = 2 * R * (K0 * D + D * N) + 4 * R * D * N if ncols <= 0 else executed
     secs = (t1 - t0) + (t3 - t2)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     what = "all" if ncols <= 0 else f"{ncols} sampled"
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"fp64 numpy oracle on {R} of the 8B workload's {total_rows} rows: forward of those rows, then "
                        f"the backward of that {R}-row batch (s, G, da for every row; dgamma and dW1 on "
-                       f"{what} columns); {flops / 1e9:.1f} GFLOP in {secs:.2f} s"),
-            "seconds": secs, "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+                       f"{what} columns); {flops / 1e9:.1f} GFLOP of the step's algorithmic work "
+                       f"({executed / 1e9:.1f} GFLOP executed) in {secs:.2f} s"),
+            "seconds": secs, "algorithmic_gflop": flops / 1e9, "executed_gflop": executed / 1e9,
+            "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+
+
+def oracle_configs(gpu, rows_per_cfg=256):
+    """The oracle's forward timed on each configuration's seeded row sample (every row of the tiny one): rows/s
+    and the extrapolated full-M time (rows are independent), and the GPU forward's error on those rows (its fp32
+    y against the oracle's y: max|d| / rms; r: max relative)."""
+    import numpy as np
+    import torch
+
+    from oracle import coda_oracle as orc
+    from transformer_gemm_epilogue_res_amd import inputs
+
+    out = {}
+    for name, g in gpu.items():
+        host, rows, M = g["host"], g["rows"], g["M"]
+        t0 = time.perf_counter()
+        f = orc.forward(host["x"], host["W0"], host["z"], host["gamma"], host["W1"], inputs.EPS)
+        secs = time.perf_counter() - t0
+        y = g["y32"].double().numpy()
+        e_y = float(np.abs(y - f["y"]).max() / np.sqrt((f["y"] ** 2).mean()))
+        e_r = float(np.abs(g["r"].double().numpy() / f["r"] - 1).max())
+        R = len(rows)
+        out[name] = {"rows": R, "seconds": round(secs, 4), "rows_per_s": round(R / secs, 1),
+                     "extrapolated_full_s": round(secs * M / R, 3), "y_err_max_over_rms": e_y, "r_err_max_rel": e_r}
+    return out
 
 
 def main():
@@ -170,6 +202,8 @@ def main():
     ap.add_argument("--no-ce", action="store_true", help="skip timing the cross-entropy LM head")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache variant of the step")
     ap.add_argument("--no-shard", action="store_true", help="skip the data-parallel shard (M / 8) step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, Llama-3 1B and Llama-3 70B forward configurations")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many bytes (a reference kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -210,6 +244,27 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = L.current_stream(dev)
     names = list(L.FWD_STAGE_NAMES) + list(L.BWD_STAGE_NAMES)
+
+    def paired_ms(a, b, calls, rounds=5):
+        """Mean ms per call of a() and of b(), timed in alternating blocks of calls / rounds calls each
+        (events at the block ends only), so that both run in the same power and thermal state: under
+        the socket power cap the clock a kernel gets depends on what ran before it, and timing one
+        chain after another section of the bench would compare two different clocks."""
+        reps = max(1, -(-calls // rounds))
+        for f in (a, b, a, b):
+            f()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(rounds)]
+        for e in ev:
+            e[0].record(stream)
+            for _ in range(reps):
+                a()
+            e[1].record(stream)
+            for _ in range(reps):
+                b()
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        return (sum(e[0].elapsed_time(e[1]) for e in ev) / (rounds * reps),
+                sum(e[1].elapsed_time(e[2]) for e in ev) / (rounds * reps))
 
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -265,18 +320,25 @@ def main():
     per = {n: v / args.steps for n, v in per.items()}          # ms per launch
     ms_instrumented = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
 
-    # The forward and the backward each alone, K calls with events at the ends only (the
-    # way the unfused baseline is timed below).
-    def clean_ms(obj, **kw):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(args.steps):
-            obj.run(sp, **kw)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-    fwd_ms, bwd_ms = clean_ms(F), clean_ms(B)
+    # The forward and the backward each alone (events at block ends only), each paired with the unfused
+    # baseline of the same pass: the unfused forward writes the same h, r, y (no g) and the unfused
+    # backward reads the fused forward's saved set.
+    unfused = None
+    if args.no_unfused:
+        fwd_ms = paired_ms(lambda: F.run(sp), lambda: None, args.steps)[0]
+        bwd_ms = paired_ms(lambda: B.run(sp), lambda: None, args.steps)[0]
+    else:
+        log("[bench] timing the fused forward and backward, each alternating with the unfused baseline")
+        uF = L.bind_fwd(x, W0, z, gamma, W1, inputs.EPS, dict(fo, g=None),
+                        L.workspace(L.CODA_OP_UNFUSED_FWD, M, D, N, dev))
+        uB = L.bind_bwd(dY, fo["y"], fo["h"], fo["g"], fo["r"], gamma, W1, bo,
+                        L.workspace(L.CODA_OP_UNFUSED_BWD, M, D, N, dev))
+        fwd_ms, ufwd_ms = paired_ms(lambda: F.run(sp), lambda: uF.run(sp, unfused=True), args.steps)
+        bwd_ms, ubwd_ms = paired_ms(lambda: B.run(sp), lambda: uB.run(sp, unfused=True), args.steps)
+        unfused = {"fwd_ms": round(ufwd_ms, 4), "bwd_ms": round(ubwd_ms, 4),
+                   "fused_fwd_speedup": round(ufwd_ms / fwd_ms, 3), "fused_bwd_speedup": round(ubwd_ms / bwd_ms, 3)}
+        log(f"[bench] unfused fwd {ufwd_ms:.3f} ms, bwd {ubwd_ms:.3f} ms")
+        del uF, uB
     fwd_flop = 2 * M * K0 * D + 2 * M * D * N
     bwd_flop = 4 * M * D * N
     value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
@@ -388,27 +450,20 @@ def main():
         USB = L.bind_bwd_swiglu(dOut, W2, so["o"], so["y"], so["h"], so["g"], so["r"], gamma, W1, sbo,
                                 L.workspace(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N, dev))
         t = {}
-        for name, obj, unf in (("fwd", SF, False), ("bwd", SB, False), ("ufwd", SF, True), ("ubwd", USB, True)):
-            for _ in range(2):
-                obj.run(sp, unfused=unf)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                obj.run(sp, unfused=unf)
-            b.record(stream)
-            torch.cuda.synchronize()
-            t[name] = a.elapsed_time(b) / args.steps
+        t["fwd"], t["ufwd"] = paired_ms(lambda: SF.run(sp), lambda: SF.run(sp, unfused=True), args.steps)
+        t["bwd"], t["ubwd"] = paired_ms(lambda: SB.run(sp), lambda: USB.run(sp, unfused=True), args.steps)
         s_bwd_flop = bwd_flop + 2 * 2 * M * Fh * E   # + dO = dOut W2^T and dW2 = o^T dOut
         swiglu = {"E": E, "fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
                   "fwd_tflops": round(fwd_flop / t["fwd"] / 1e9, 1),
                   "bwd_tflops": round(s_bwd_flop / t["bwd"] / 1e9, 1),
                   "tflops": round((fwd_flop + s_bwd_flop) / (t["fwd"] + t["bwd"]) / 1e9, 1)}
         swiglu["pct_peak"] = round(100 * swiglu["tflops"] / PEAK_BF16_TFLOPS, 2)
-        swiglu["unfused"] = {"fwd_ms": round(t["ufwd"], 4), "bwd_ms": round(t["ubwd"], 4),
-                             "fused_fwd_speedup": round(t["ufwd"] / t["fwd"], 3),
-                             "fused_bwd_speedup": round(t["ubwd"] / t["bwd"], 3)}
+        # the baseline unfuses only the activation step (the chain under it is the fused one)
+        swiglu["activation_unfused"] = {"fwd_ms": round(t["ufwd"], 4), "bwd_ms": round(t["ubwd"], 4),
+                                        "fused_fwd_speedup": round(t["ufwd"] / t["fwd"], 3),
+                                        "fused_bwd_speedup": round(t["ubwd"] / t["bwd"], 3)}
         log(f"[bench] SwiGLU block: fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms, {swiglu['tflops']} TFLOP/s; "
-            f"unfused SwiGLU step: fwd {t['ufwd']:.3f} ms, bwd {t['ubwd']:.3f} ms")
+            f"with the activation step unfused: fwd {t['ufwd']:.3f} ms, bwd {t['ubwd']:.3f} ms")
         del W2, dOut, so, sbo, SF, SB, USB
 
     # Cross-entropy on the Llama-3-8B LM head (coda_ce_fwd / coda_ce_bwd, V = 128256):
@@ -433,19 +488,14 @@ def main():
         # the unfused baseline stores the fp32 logits [M, V] in its workspace
         uws = None if args.no_unfused else L.workspace(L.CODA_OP_UNFUSED_CE_FWD, M, D, V, dev)
         t = {}
-        runs = [("fwd", CF, None), ("bwd", CB, None), ("sfwd", CFS, None), ("sbwd", CBS, None)]
+        # each variant alternating with the fused (recomputing) pass: fwd / bwd pair with stored logits,
+        # then with the unfused baseline; the fused times are the mean of their pairings
+        t["fwd"], t["sfwd"] = paired_ms(lambda: CF.run(sp), lambda: CFS.run(sp), args.steps)
+        t["bwd"], t["sbwd"] = paired_ms(lambda: CB.run(sp), lambda: CBS.run(sp), args.steps)
         if uws is not None:
-            runs += [("ufwd", CF, uws), ("ubwd", CB, uws)]
-        for name, obj, w in runs:
-            for _ in range(2):
-                obj.run(sp, unfused_ws=w)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                obj.run(sp, unfused_ws=w)
-            b.record(stream)
-            torch.cuda.synchronize()
-            t[name] = a.elapsed_time(b) / args.steps
+            f2, t["ufwd"] = paired_ms(lambda: CF.run(sp), lambda: CF.run(sp, unfused_ws=uws), args.steps)
+            b2, t["ubwd"] = paired_ms(lambda: CB.run(sp), lambda: CB.run(sp, unfused_ws=uws), args.steps)
+            t["fwd"], t["bwd"] = (t["fwd"] + f2) / 2, (t["bwd"] + b2) / 2
         ce_f, ce_b = 2 * M * D * V, 3 * 2 * M * D * V   # logits; recomputed logits, dh, dW
         ce = {"V": V, "fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
               "fwd_tflops": round(ce_f / t["fwd"] / 1e9, 1), "bwd_tflops": round(ce_b / t["bwd"] / 1e9, 1),
@@ -465,29 +515,57 @@ def main():
                 f"bwd {t['ubwd']:.3f} ms")
         del hl, Wl, tg, dloss, cfo, cbo, CF, CB, uws, lg, cso, CFS, CBS
 
-    unfused = None
-    if not args.no_unfused:
-        log("[bench] timing the unfused baseline")
-        ufo = dict(fo, g=None)
-        uF = L.bind_fwd(x, W0, z, gamma, W1, inputs.EPS, ufo, L.workspace(L.CODA_OP_UNFUSED_FWD, M, D, N, dev))
-        uB = L.bind_bwd(dY, fo["y"], fo["h"], fo["g"], fo["r"], gamma, W1, bo,
-                        L.workspace(L.CODA_OP_UNFUSED_BWD, M, D, N, dev))
-        t = {}
-        for name, obj in (("fwd", uF), ("bwd", uB)):
-            for _ in range(2):
-                obj.run(sp, unfused=True)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                obj.run(sp, unfused=True)
-            b.record(stream)
-            torch.cuda.synchronize()
-            t[name] = a.elapsed_time(b) / args.steps
-        unfused = {"fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
-                   "fused_fwd_speedup": round(t["fwd"] / fwd_ms, 3), "fused_bwd_speedup": round(t["bwd"] / bwd_ms, 3)}
-        log(f"[bench] unfused fwd {t['fwd']:.3f} ms, bwd {t['bwd']:.3f} ms")
+    # The other forward configurations (tiny, Llama-3 1B, Llama-3 70B), fused against the unfused baseline,
+    # reported beside the headline; one fp32-y forward per configuration gives its error on sampled rows.
+    configs, cfg_gpu = None, {}
+    if not args.no_configs:
+        configs = {}
+        for name in ("tiny", "llama3_1b", "llama3_70b"):
+            cc = inputs.CONFIGS[name]
+            Mc, K0c, Dc, Nc = cc["M"], cc["K0"], cc["D"], cc["N"]
+            gc = torch.Generator(device=dev)
+            gc.manual_seed(1)
+
+            def rndc(*shape, scale=1.0, shift=0.0):
+                return (torch.randn(*shape, generator=gc, device=dev) * scale + shift).to(bf)
+
+            xc, W0c, zc = rndc(Mc, K0c), rndc(K0c, Dc, scale=K0c ** -0.5), rndc(Mc, Dc)
+            gmc, W1c = rndc(Dc, scale=0.1, shift=1.0), rndc(Dc, Nc, scale=Dc ** -0.5)
+            foc = {"h": torch.empty(Mc, Dc, dtype=bf, device=dev), "g": torch.empty(Mc, Dc, dtype=bf, device=dev),
+                   "r": torch.empty(Mc, dtype=torch.float32, device=dev), "y": torch.empty(Mc, Nc, dtype=bf, device=dev)}
+            FC = L.bind_fwd(xc, W0c, zc, gmc, W1c, inputs.EPS, foc, L.workspace(L.CODA_OP_FWD, Mc, Dc, Nc, dev))
+            UC = L.bind_fwd(xc, W0c, zc, gmc, W1c, inputs.EPS, dict(foc, g=None),
+                            L.workspace(L.CODA_OP_UNFUSED_FWD, Mc, Dc, Nc, dev))
+            reps = args.steps if Mc * Nc * Dc > 1 << 30 else 200   # the tiny one: enough calls to time
+            tc = {}
+            tc["fused"], tc["unfused"] = paired_ms(lambda: FC.run(sp), lambda: UC.run(sp, unfused=True), reps)
+            flc = 2 * Mc * K0c * Dc + 2 * Mc * Dc * Nc
+            configs[name] = {"M": Mc, "K0": K0c, "D": Dc, "N": Nc, "gflop": round(flc / 1e9, 3),
+                             "fused_ms": round(tc["fused"], 5), "unfused_ms": round(tc["unfused"], 5),
+                             "fused_tflops": round(flc / tc["fused"] / 1e9, 1),
+                             "pct_peak": round(100 * flc / tc["fused"] / 1e9 / PEAK_BF16_TFLOPS, 2),
+                             "unfused_tflops": round(flc / tc["unfused"] / 1e9, 1),
+                             "fused_vs_unfused": round(tc["unfused"] / tc["fused"], 3)}
+            log(f"[bench] {name} forward: fused {tc['fused'] * 1e3:.1f} us ({configs[name]['fused_tflops']} TFLOP/s), "
+                f"unfused {tc['unfused'] * 1e3:.1f} us")
+            if args.cpu_rows > 0:   # one fp32-y forward for the error on the oracle's rows (cpu_baseline leg)
+                rows = torch.arange(Mc) if Mc <= 256 else inputs.sample(Mc, 256, 0, "rows")
+                y32 = L.fwd(xc, W0c, zc, gmc, W1c, inputs.EPS, torch.float32)
+                ri = rows.to(dev)
+                cfg_gpu[name] = {"M": Mc, "rows": rows.numpy(), "y32": y32["y"].index_select(0, ri).cpu(),
+                                 "r": y32["r"].index_select(0, ri).cpu(),
+                                 "host": {"x": xc.index_select(0, ri).cpu(), "z": zc.index_select(0, ri).cpu(),
+                                          "W0": W0c.cpu(), "gamma": gmc.cpu(), "W1": W1c.cpu()}}
+                del y32
+            del xc, W0c, zc, gmc, W1c, foc, FC, UC
+            torch.cuda.empty_cache()
 
     cpu = None
+    if args.cpu_rows > 0 and configs is not None:
+        log("[bench] oracle forward on each configuration's row sample")
+        for name, o in oracle_configs(cfg_gpu).items():
+            configs[name]["oracle"] = o
+            log(f"[bench]   {name}: {o}")
     if args.cpu_rows > 0:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
         rows = inputs.sample(M, args.cpu_rows, 0, "rows").to(dev)
@@ -511,7 +589,7 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
                 "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
-        "bwd_gemm0": bwd_gemm0, "swiglu": swiglu, "cross_entropy": ce,
+        "configs": configs, "bwd_gemm0": bwd_gemm0, "swiglu": swiglu, "cross_entropy": ce,
         "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }
