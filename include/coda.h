@@ -328,8 +328,13 @@ coda_status_t coda_validate_ce_bwd(const coda_ce_bwd_args_t* a);
  * CODA_OP_BWD_SWIGLU, CODA_OP_CE_FWD or CODA_OP_CE_BWD). */
 coda_status_t coda_validate_unfused(coda_op_t op, const void* args, const void* ws, size_t ws_bytes);
 
-/* Fused forward: GEMM0 + epilogue (residual, h, g, sum-of-squares partials) ->
- * row-statistic combine (r) -> GEMM1 + epilogue (row scale r). */
+/* Fused forward: GEMM0 + epilogue (residual, h, g, one sum-of-squares partial per row and
+ * 256-column tile, its four waves' sums added in the block) -> row-statistic combine (r) ->
+ * GEMM1 + epilogue (row scale r). The combine is the light auxiliary reduction between the two
+ * epilogues (hotdry blog, section "GEMM-Residual-RMSNorm-GEMM 重参数化", step 2); GEMM1's epilogue does it
+ * itself, with no kernel of its own, when ceil(D / 256) <= 32 and GEMM1 has at most 512 tiles of
+ * 256 x 256 (ceil(M / 256) * ceil(N / 256)): every tile repeats it, which costs more than a
+ * separate launch once GEMM1 runs more than two waves of tiles. */
 coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
 /* The fused forward for callers that cannot allocate device memory (code under HIP graph capture,
@@ -337,9 +342,9 @@ coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void
  * sum-of-squares partials kept in a device array of the library's own, CODA_NOALLOC_SCRATCH_BYTES
  * (16 MiB), which every GPU the library runs on holds until the process ends; no workspace argument,
  * and no allocation or free of any kind. GEMM0 is never split over its contraction here (coda_fwd
- * splits it when its tiles cannot fill the chip), so the partials need only M * (D / 64) * 4 bytes.
- *   - Returns CODA_ERR_WORKSPACE, launching nothing, when M * (D / 64) * 4 exceeds the 16 MiB
- *     (e.g. M > 65536 rows at D = 4096); every other check and status is coda_fwd's.
+ * splits it when its tiles cannot fill the chip), so the partials need only M * ceil(D / 256) * 4 bytes.
+ *   - Returns CODA_ERR_WORKSPACE, launching nothing, when M * ceil(D / 256) * 4 exceeds the 16 MiB
+ *     (e.g. M > 262144 rows at D = 4096); every other check and status is coda_fwd's.
  *   - All calls on one GPU share that GPU's array: calls that may overlap on one GPU (on different
  *     streams, or from several threads) race and must be ordered by the caller. A call needs nothing
  *     from the previous one (its partials are written in full before they are read).
@@ -364,7 +369,8 @@ coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void
  * over its contraction -- see coda_workspace_bytes -- launches the GEMM and a row
  * kernel that finishes its epilogue.) Each call validates the
  * whole argument set; a stage index out of range returns CODA_ERR_ARG.
- *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine,
+ *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine (launches
+ *             nothing where GEMM1's epilogue combines r itself, see coda_fwd),
  *             2 GEMM1 + row-scale epilogue
  *   backward: 0 s, then bf16(r*g) transposed for the dW1 GEMM (two kernels),
  *             1 G = dY@W1^T + RMSNorm-backward epilogue, 2 dW1 GEMM, whose blocks

@@ -85,12 +85,12 @@ def test_workspace_sizes():
     def a256(v):
         return (v + 255) // 256 * 256
     M, D, N = 300, 512, 768
-    def fwd_ws(M, D):  # P [M, D/64], and min(ceil(256 / tiles), 8) split-K partials when GEMM0 has < 192 tiles
+    def fwd_ws(M, D):  # P [M, ceil(D/256)], and min(ceil(256 / tiles), 8) split-K partials when GEMM0 has < 192 tiles
         tiles = math.ceil(M / 256) * math.ceil(D / 256)
         S = 1 if tiles >= 192 else min(math.ceil(256 / tiles), 8)
-        return a256(M * (D // 64) * 4) + (a256(S * M * D * 4) if S > 1 else 0)
-    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == fwd_ws(M, D) == a256(M * 8 * 4) + a256(8 * M * D * 4)
-    assert L.workspace_bytes(L.CODA_OP_FWD, 8192, 4096, 28672) == a256(8192 * 64 * 4)   # 512 tiles: no split
+        return a256(M * math.ceil(D / 256) * 4) + (a256(S * M * D * 4) if S > 1 else 0)
+    assert L.workspace_bytes(L.CODA_OP_FWD, M, D, N) == fwd_ws(M, D) == a256(M * 2 * 4) + a256(8 * M * D * 4)
+    assert L.workspace_bytes(L.CODA_OP_FWD, 8192, 4096, 28672) == a256(8192 * 16 * 4)   # 512 tiles: no split
     # the backward splits the data-gradient contraction when its tiles cannot fill the chip (few rows)
     S, ks = dgrad_split(M, D, N)
     assert (S, ks) == (3, 256)                      # 4 tiles; 12 K steps of 64 -> 3 slices of 4 steps
@@ -114,9 +114,9 @@ def test_workspace_sizes():
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2 // 64) * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD_SWIGLU, M, D, 832) == 0      # 13 x 64: not a multiple of 128
     assert L.workspace_bytes(L.CODA_OP_BWD_SWIGLU, M, D, 832) == 0
-    # multiples of 64 (not of 256): P [M, 5] for D = 320, and a ragged column tile
-    assert L.workspace_bytes(L.CODA_OP_FWD, 8192, 320, 576) == a256(8192 * 5 * 4) + a256(4 * 8192 * 320 * 4)  # 64 tiles: 4 slices
-    assert L.workspace_bytes(L.CODA_OP_FWD, 65536, 320, 576) == a256(65536 * 5 * 4) # 256 x 2 tiles: no split
+    # multiples of 64 (not of 256): P [M, 2] for D = 320 (a ragged column tile)
+    assert L.workspace_bytes(L.CODA_OP_FWD, 8192, 320, 576) == a256(8192 * 2 * 4) + a256(4 * 8192 * 320 * 4)  # 64 tiles: 4 slices
+    assert L.workspace_bytes(L.CODA_OP_FWD, 65536, 320, 576) == a256(65536 * 2 * 4) # 256 x 2 tiles: no split
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD_SWIGLU, M, D, N2) == fwd_ws(M, D)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD_SWIGLU, M, D, N2) == bwd2 + a256(M * (N2 // 2) * 2)
     V = 128256  # cross-entropy: tile statistics (m, l) [M, V/64] and the target logits [M]
@@ -399,12 +399,12 @@ def test_python_binding_counts_workspace_bytes_not_elements():
 
 
 def test_validate_fwd_noalloc_limit():
-    """The no-allocation forward accepts what coda_fwd accepts while its partials, M * (D / 64) * 4
+    """The no-allocation forward accepts what coda_fwd accepts while its partials, M * ceil(D / 256) * 4
     bytes, fit the library's 16 MiB device scratch, and returns CODA_ERR_WORKSPACE beyond that."""
     lib = L.lib()
     assert L.NOALLOC_SCRATCH_BYTES == 16 << 20
     assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd())) == L.CODA_OK
-    rows = (16 << 20) // ((4096 // 64) * 4)           # 65536 rows at D = 4096 fill it exactly
+    rows = (16 << 20) // ((4096 // 256) * 4)          # 262144 rows at D = 4096 fill it exactly
     assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd(M=rows, D=4096))) == L.CODA_OK
     assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd(M=rows + 1, D=4096))) == L.CODA_ERR_WORKSPACE
     assert lib.coda_validate_fwd_noalloc(ctypes.byref(_fwd(eps=0.0))) == L.CODA_ERR_ARG

@@ -66,6 +66,11 @@ FWD_SMALL = {
     "dims64": dict(M=300, K0=192, D=320, N=576),
     "dims64_split": dict(M=64, K0=1088, D=320, N=576),      # GEMM0 in 4 slices, the last one 2 K steps
     "dims64_rows": dict(M=24576, K0=192, D=320, N=576),     # 192 GEMM0 tiles: the fused epilogue, unsplit
+    # GEMM1 combines r itself while its 128-row blocks of partials fit 16 KB (ceil(D / 256) <= 32) and it has
+    # at most 512 tiles (every case above); else a separate kernel does: the two edges of that rule
+    "folded_widest": dict(M=64, K0=256, D=8192, N=256),     # 32 partials per row: the whole staging area
+    "unfolded_wide": dict(M=64, K0=256, D=8256, N=256),     # 33 partials per row
+    "unfolded_tiles": dict(M=2048, K0=128, D=128, N=16640),  # 8 x 65 = 520 GEMM1 tiles
 }
 
 

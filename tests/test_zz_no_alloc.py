@@ -54,7 +54,7 @@ def test_no_alloc_forward_matches_coda_fwd_on_consecutive_calls():
 
 
 def test_no_alloc_forward_rejects_sizes_beyond_its_scratch():
-    M, D = (16 << 20) // ((4096 // 64) * 4) + 1, 4096
+    M, D = (16 << 20) // ((4096 // 256) * 4) + 1, 4096   # partials M * ceil(D / 256) * 4 bytes: one row past 16 MiB
     x = torch.empty(M, 256, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(L.CodaError) as e:
         L.fwd_noalloc(x, torch.empty(256, D, dtype=torch.bfloat16, device=DEV),

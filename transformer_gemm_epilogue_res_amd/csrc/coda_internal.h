@@ -31,8 +31,19 @@ constexpr int kUnfusedBwdRows = 32;
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Column count of the forward's sum-of-squares partials P[M, D / kWaveTileN].
-inline int64_t ssq_cols(int64_t D) { return D / kWaveTileN; }
+// Column count of the forward's sum-of-squares partials P[M, ceil(D / kBN)]: one per row and
+// 256-column tile of GEMM0 (its four waves' 64-column sums added in the block).
+inline int64_t ssq_cols(int64_t D) { return ceil_div(D, kBN); }
+// GEMM1's epilogue combines r from P itself, with no separate combine launch, when
+//   * a wave's 128 rows of partials fit its 16 KB LDS staging area: at most 32 per row, D <= 8192;
+//   * GEMM1 has at most two waves of tiles on the 256 CUs: each tile pays the partials' DMA and the
+//     combine again (measured at the 8B shape: about 2.7 us per wave of tiles, against about 1 us for
+//     the separate launch in stream), so larger GEMMs keep the separate kernel.
+constexpr int64_t kFoldedCombineMaxCols = 32;
+constexpr int64_t kFoldedCombineMaxTiles = 512;
+inline bool fwd_folds_combine(int64_t M, int64_t D, int64_t N) {
+  return ssq_cols(D) <= kFoldedCombineMaxCols && ceil_div(M, kBM) * ceil_div(N, kBN) <= kFoldedCombineMaxTiles;
+}
 // Column count of the SwiGLU backward's s partials Ps[M, (N / 2) / kWaveTileN].
 inline int64_t swiglu_s_cols(int64_t N) { return (N / 2) / kWaveTileN; }
 // Column count of the cross-entropy tile statistics Pml[M, V / kWaveTileN] (float2).
@@ -78,9 +89,9 @@ inline KSplit gemm0_split(int64_t M, int64_t K0, int64_t D) {
   const int64_t kslice = ceil_div(ceil_div(K0, S), kBK) * kBK;
   return {ceil_div(K0, kslice), kslice};
 }
-// Device scratch of the no-allocation forward (coda_fwd_noalloc): its partials P [M, D / 64] fp32.
+// Device scratch of the no-allocation forward (coda_fwd_noalloc): its partials P [M, ceil(D / 256)] fp32.
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
-// Fused forward workspace: the sums of squares P [M, D / 64], then (split-K only) the
+// Fused forward workspace: the sums of squares P [M, ceil(D / 256)], then (split-K only) the
 // fp32 partial products [S_max, M, D].
 inline size_t fwd_ws_p(int64_t M, int64_t D) { return align256(size_t(M) * size_t(ssq_cols(D)) * 4); }
 inline size_t fwd_ws(int64_t M, int64_t D) {

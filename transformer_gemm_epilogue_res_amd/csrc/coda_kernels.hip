@@ -262,8 +262,10 @@ struct EpiStoreDgamma {
 };
 
 // GEMM0 epilogue: h = acc + z (fp32) -> store bf16 h; g = bf16(h * gamma) from
-// the fp32 h; per-row sum of squares of the fp32 h over the wave's 64 columns
-// -> P[i, nb / 64].
+// the fp32 h; per-row sum of squares of the fp32 h over the wave's 64 columns,
+// left in the wave's auxiliary LDS; after a block barrier finish() adds the four
+// waves' sums of each row (in wave order) -> P[i, n0 / 256], the tile's partial.
+constexpr int kSsqAuxOffset = 256;  // the 128 row sums follow the 64 gamma values (256 bytes of DMA) in aux
 struct EpiResidualSsq {
   const uint16_t* z;
   const uint16_t* gamma;
@@ -287,8 +289,6 @@ struct EpiResidualSsq {
     const StageBf16 zs{stage, lane};
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
-      const int64_t i = mb + 16 * tm + li;
-      const bool ok = i < M;
       float ssq = 0.f;
 #pragma unroll
       for (int tn = 0; tn < kTN; ++tn) {
@@ -303,7 +303,7 @@ struct EpiResidualSsq {
       // the 4 lanes l % 16 == li hold the rest of row i's 64 columns
       ssq += shfl_xor(ssq, 16);
       ssq += shfl_xor(ssq, 32);
-      if (lane < 16 && ok) P[i * pcols + nb / kWaveTileN] = ssq;
+      if (lane < 16) *reinterpret_cast<LDS_AS float*>(aux + kSsqAuxOffset + (16 * tm + li) * 4) = ssq;
     }
     store_block<false>(stage, lane, h, D, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
     store_block<false>(stage, lane, g, D, mb, nb, M, [&](int tm, int tn) {
@@ -313,28 +313,97 @@ struct EpiResidualSsq {
       return v;
     });
   }
+  // After the block barrier, all waves: wave p of a group adds rows 32 p .. 32 p + 31 of its group's
+  // 128 (first row mb) over the group's waves whose columns lie below D (aux0: the group's first wave's
+  // auxiliary area) and writes P[i, n0 / 256].
+  __device__ __forceinline__ void finish(const lds_char_t* aux0, int64_t mb, int64_t n0, int p, int lane) const {
+    const int64_t left = (D - n0) / kWaveTileN;
+    const int nvalid = left < 4 ? int(left) : 4;
+    if (lane < 32) {
+      const int row = 32 * p + lane;
+      float s = lds_f32(aux0 + kSsqAuxOffset + row * 4);
+      for (int w = 1; w < nvalid; ++w) s += lds_f32(aux0 + w * kAuxWaveBytes + kSsqAuxOffset + row * 4);
+      const int64_t i = mb + row;
+      if (i < M) P[i * pcols + n0 / kBN] = s;
+    }
+  }
 };
+
+// The row scales of GEMM1's epilogues, r_i = 1 / sqrt(sum_t P[i, t] / D + eps) (the deferred RMSNorm
+// factor). With P set, each wave combines them itself from the sums of squares P [M, pcols] of its 128
+// rows, brought into its staging area by DMA during the last K step (and read before the staging
+// area is reused): the four lanes of a row each add a strided share of its partials, then two
+// butterfly steps add the shares -- a fixed order that depends only on pcols, so every tile of a row
+// gets the same bits -- and the waves of tile column 0 write r. Without P (too many partials for the
+// staging area: a separate kernel combined them), r is an input, moved into aux.
+struct RowScaleSrc {
+  float* r;
+  const float* P;
+  int64_t M, pcols;
+  float D, eps;
+  __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int lane) const {
+    if (P == nullptr) {
+      dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
+      return;
+    }
+    // rows mb .. mb + 127 of P: 512 pcols contiguous bytes (0 past row M - 1)
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + mb * pcols, (M - mb) * pcols * 4);
+    if ((pcols & 3) == 0) {  // 16 bytes per lane: the rows are 16-byte multiples, so no chunk straddles row M
+#pragma unroll 1
+      for (int q = 0; q < pcols / 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(stage + q * 1024), 16, uint32_t(q * 1024 + lane * 16), 0, 0, 0);
+    } else {  // 4 bytes per lane (exact to the element)
+#pragma unroll 1
+      for (int q = 0; q < 2 * pcols; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(stage + q * 256), 4, uint32_t(q * 256 + lane * 4), 0, 0, 0);
+    }
+  }
+  // rr[tm]: the scale of row mb + 16 tm + l % 16 (after early()'s DMA has landed)
+  __device__ __forceinline__ void scales(float (&rr)[kTM], const lds_char_t* stage, const lds_char_t* aux, int64_t mb,
+                                         int64_t nb, int lane) const {
+    const int li = lane & 15, lg = lane >> 4;
+    if (P == nullptr) {
+#pragma unroll
+      for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
+      return;
+    }
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+      const int row = 16 * tm + li;
+      float s = 0.f;
+      for (int64_t q = lg; q < pcols; q += 4) s += lds_f32(stage + (row * pcols + q) * 4);
+      s += shfl_xor(s, 16);
+      s += shfl_xor(s, 32);
+      rr[tm] = 1.0f / sqrtf(s / D + eps);
+    }
+    if (nb == 0 && lg == 0) {
+#pragma unroll
+      for (int tm = 0; tm < kTM; ++tm) {
+        const int64_t i = mb + 16 * tm + li;
+        if (i < M) r[i] = rr[tm];
+      }
+    }
+  }
+};
+static_assert(kWaveTileM * 4 * kFoldedCombineMaxCols <= kEpiWaveBytes, "a wave's partials fit its staging area");
 
 // GEMM1 epilogue: y = r_i * acc (the deferred RMSNorm row scale).
 template <bool F32>
 struct EpiRowScale {
-  const float* r;
+  RowScaleSrc rs;
   void* y;
-  int64_t M, N;
-  // during the last K step: the wave's 128 row scales into aux (0 past M)
-  __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
-    dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
+  int64_t N;
+  __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
+    rs.early(stage, aux, mb, lane);
   }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
                                              lds_char_t* stage, lds_char_t* aux) const {
-    const int li = lane & 15;
     wait_vm0();
     float rr[kTM];
-#pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
+    rs.scales(rr, stage, aux, mb, nb, lane);
     // y non-temporally: the forward does not read it again, and the backward's row-statistic
     // pass reads it from HBM faster this way (about 30 us less at the 8B shape)
-    store_block<F32, true>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
+    store_block<F32, true>(stage, lane, y, N, mb, nb, rs.M, [&](int tm, int tn) {
       f32x4_t v = acc[tm][tn];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] *= rr[tm];
@@ -379,20 +448,19 @@ struct StageBf16Half {
 // stored in fp32 (F32) or bf16.
 template <bool F32>
 struct EpiRowScaleSwiglu {
-  const float* r;
+  RowScaleSrc rs;
   void* y;
   void* o;
-  int64_t M, N;  // o has N / 2 columns
-  __device__ __forceinline__ void early(lds_char_t*, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
-    dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
+  int64_t N;  // o has N / 2 columns
+  __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
+    rs.early(stage, aux, mb, lane);
   }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
                                              lds_char_t* stage, lds_char_t* aux) const {
-    const int li = lane & 15;
+    const int64_t M = rs.M;
     wait_vm0();
     float rr[kTM];
-#pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
+    rs.scales(rr, stage, aux, mb, nb, lane);
     store_block<false>(stage, lane, y, N, mb, nb, M, [&](int tm, int tn) {
       f32x4_t v = acc[tm][tn];
 #pragma unroll
@@ -712,6 +780,14 @@ struct HasEarly : std::false_type {};
 template <class Epi>
 struct HasEarly<Epi, decltype(std::declval<const Epi&>().early(nullptr, nullptr, 0, 0, 0), void())> : std::true_type {};
 
+// ... and block-level work after the epilogue (finish(aux0, mb, n0, p, lane), every wave, after a block
+// barrier that every wave reaches, including waves whose columns lie past N; aux0 is the auxiliary
+// area of the wave's group's first wave, mb the group's first row, p the wave's index in the group).
+template <class Epi, class = void>
+struct HasFinish : std::false_type {};
+template <class Epi>
+struct HasFinish<Epi, decltype(std::declval<const Epi&>().finish(nullptr, 0, 0, 0, 0), void())> : std::true_type {};
+
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, const Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
@@ -759,6 +835,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
     } else {
       epi(acc, m0 + kWaveTileM, nb, lane, stage);
     }
+  }
+  if constexpr (HasFinish<Epi>::value) {
+    wait_lgkm0();  // this wave's LDS writes for finish()
+    block_barrier();
+    epi.finish(aux - (wave & 3) * kAuxWaveBytes, m0 + (wave >> 2) * kWaveTileM, n0, wave & 3, lane);
   }
 }
 
@@ -1091,15 +1172,15 @@ __global__ __launch_bounds__(256) void splitk_rmsnorm_bwd_kernel(const float* pa
 }
 
 // Split-K GEMM0: h = the slices' fp32 partial products summed in order + z (fp32), stored
-// bf16; g = bf16(h gamma) from the fp32 h; P[i, j / 64] = the sum of squares of the fp32 h
-// over each 64-column chunk -- what the fused epilogue computes. A block covers 1024 columns
-// (4 per thread; 16 threads per chunk) of one row.
+// bf16; g = bf16(h gamma) from the fp32 h; P[i, j / 256] = the sum of squares of the fp32 h
+// over each 256-column tile -- what the fused epilogue computes. A block covers 1024 columns
+// (4 per thread; one wave per tile) of one row.
 __global__ __launch_bounds__(256) void splitk_residual_kernel(const float* part, int S, int64_t sstride,
                                                               const uint16_t* z, const uint16_t* gamma, uint16_t* h,
                                                               uint16_t* g, float* P, int64_t D, int64_t pcols) {
   const int64_t i = blockIdx.y;
   const int64_t j = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  const bool ok = j < D;  // uniform over each 16-thread chunk group (64 columns; D is a multiple of 64)
+  const bool ok = j < D;  // uniform over each 16-thread group (64 columns; D is a multiple of 64)
   float ssq = 0.f;
   if (ok) {
     float hv[4], zz[4], gm[4];
@@ -1121,11 +1202,10 @@ __global__ __launch_bounds__(256) void splitk_residual_kernel(const float* part,
     *reinterpret_cast<uint2*>(h + i * D + j) = pack4_bf16(hv[0], hv[1], hv[2], hv[3]);
     *reinterpret_cast<uint2*>(g + i * D + j) = pack4_bf16(hv[0] * gm[0], hv[1] * gm[1], hv[2] * gm[2], hv[3] * gm[3]);
   }
-  ssq += shfl_xor(ssq, 1);
-  ssq += shfl_xor(ssq, 2);
-  ssq += shfl_xor(ssq, 4);
-  ssq += shfl_xor(ssq, 8);
-  if (ok && (threadIdx.x & 15) == 0) P[i * pcols + j / kWaveTileN] = ssq;
+  // a wave's 64 threads cover one 256-column tile: its partial P[i, j / 256]
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ssq += shfl_xor(ssq, m);
+  if (ok && (threadIdx.x & 63) == 0) P[i * pcols + j / kBN] = ssq;
 }
 
 // Unfused SwiGLU: o = silu(gate) * up from the stored bf16 y, four pairs (16 bytes
@@ -1382,8 +1462,13 @@ hipError_t ce_bwd_products(const coda_ce_bwd_args_t* a, hipStream_t st) {
   return gemm_plain(pw, false, false, a->dW, a->D, a->dW_dtype == CODA_F32, st);
 }
 
+// GEMM1's row scales for the forward with partials P: combined in its epilogue, or read from r.
+RowScaleSrc row_scale_src(const coda_fwd_args_t* a, const float* P) {
+  return RowScaleSrc{a->r, fwd_folds_combine(a->M, a->D, a->N) ? P : nullptr, a->M, ssq_cols(a->D), float(a->D), a->eps};
+}
+
 // Stage `stage` of the fused forward (0 GEMM0 + epilogue, 1 r combine, 2 GEMM1 + row scale) with the
-// sum-of-squares partials P [M, D / 64]; part: room for GEMM0's split-K partial products when its tiles
+// sum-of-squares partials P [M, ceil(D / 256)]; part: room for GEMM0's split-K partial products when its tiles
 // cannot fill the chip, or nullptr to never split (the no-allocation entry point).
 hipError_t fwd_stage(int stage, const coda_fwd_args_t* a, float* P, float* part, hipStream_t st) {
   const int64_t pcols = ssq_cols(a->D);
@@ -1403,15 +1488,17 @@ hipError_t fwd_stage(int stage, const coda_fwd_args_t* a, float* P, float* part,
     return launch_gemm<true, false>(
         p0, EpiResidualSsq{(const uint16_t*)a->z, (const uint16_t*)a->gamma, (uint16_t*)a->h, (uint16_t*)a->g, P, a->M, a->D, pcols}, st);
   }
-  if (stage == 1) {  // partial sums of squares -> r
+  if (stage == 1) {  // partial sums of squares -> r, unless GEMM1's epilogue combines them itself
+    if (fwd_folds_combine(a->M, a->D, a->N)) return hipSuccess;
     hipLaunchKernelGGL(rms_combine_kernel, dim3(unsigned(ceil_div(a->M, kCombineRows))), dim3(256), 0, st, P, a->r, a->M,
                        pcols, float(a->D), a->eps);
     return hipGetLastError();
   }
   // GEMM1 g @ W1 with the row-scale epilogue
   const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
-  if (a->y_dtype == CODA_F32) return launch_gemm<true, false>(p1, EpiRowScale<true>{a->r, a->y, a->M, a->N}, st);
-  return launch_gemm<true, false>(p1, EpiRowScale<false>{a->r, a->y, a->M, a->N}, st);
+  const RowScaleSrc rs = row_scale_src(a, P);
+  if (a->y_dtype == CODA_F32) return launch_gemm<true, false>(p1, EpiRowScale<true>{rs, a->y, a->N}, st);
+  return launch_gemm<true, false>(p1, EpiRowScale<false>{rs, a->y, a->N}, st);
 }
 
 // ------------------------------------------------- no-allocation forward
@@ -1481,7 +1568,7 @@ coda_status_t coda_fwd_noalloc(const coda_fwd_args_t* a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* P = nullptr;
   if (scratch_address(st, &P) != hipSuccess) return CODA_ERR_HIP;
-  // P is written in full (every row's D / 64 partials) by stage 0 before stage 1 reads it, so the
+  // P is written in full (every row's ceil(D / 256) partials) by stage 0 before any later stage reads it, so the
   // previous call's contents need no clearing
   for (int s = 0; s < CODA_FWD_STAGES; ++s)
     if (fwd_stage(s, a, static_cast<float*>(P), nullptr, st) != hipSuccess) return CODA_ERR_HIP;
@@ -1607,9 +1694,10 @@ coda_status_t coda_fwd_swiglu(const coda_fwd_swiglu_args_t* a, void* ws, size_t 
     if ((v = coda_fwd_stage(s, c, ws, ws_bytes, stream)) != CODA_OK) return v;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const GemmShape p1{c->M, c->N, c->D, c->g, c->D, c->W1, c->N};
+  const RowScaleSrc rs = row_scale_src(c, static_cast<const float*>(ws));  // P leads the workspace
   if (a->o_dtype == CODA_F32)
-    return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<true>{c->r, c->y, a->o, c->M, c->N}, st));
-  return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<false>{c->r, c->y, a->o, c->M, c->N}, st));
+    return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<true>{rs, c->y, a->o, c->N}, st));
+  return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<false>{rs, c->y, a->o, c->N}, st));
 }
 
 coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream) {
