@@ -357,13 +357,18 @@ struct Loop {
   }
 };
 
-// C(k): 64 MFMAs, slab 0 then slab 1, row-tile major; after(I) runs after MFMA I.
+// C(k): 64 MFMAs, slab 0 then slab 1, row-tile major, the column tiles in reverse order on odd row
+// tiles (serpentine), so that every MFMA of a slab shares one operand fragment with the one before it.
+// On this power-limited part fewer operand changes between consecutive MFMAs mean less switching in
+// the matrix core: the serpentine order measured about 1 % faster per step than plain row-major.
+// The last 16 MFMAs are still those of row tiles 4..7 (what mfma_drain pads). after(I) runs after MFMA I.
 template <bool FIRST, class F>
 __device__ __forceinline__ void compute(f32x4_t (&acc)[kTM][kTN], const Frag (&a)[2][kTM], const Frag (&b)[2][kTN],
                                         F&& after) {
   sfor<2 * kTM * kTN>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    constexpr int kk = i / (kTM * kTN), tm = (i / kTN) % kTM, tn = i % kTN;
+    constexpr int kk = i / (kTM * kTN), tm = (i / kTN) % kTM;
+    constexpr int tn = (tm & 1) ? kTN - 1 - i % kTN : i % kTN;
     mfma_16x16x32<FIRST && kk == 0>(acc[tm][tn], b[kk][tn], a[kk][tm]);
     after(I);
   });
