@@ -380,7 +380,9 @@ coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void
 coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
-/* Unfused baseline with the same mainloop and separate row kernels.
+/* Unfused baseline with the same mainloop and separate row kernels: the conventional chain the
+ * fusion is measured against, three operators in series with the intermediate written to device
+ * memory and read back between them (kucoin page, section "CODA：「尾声」に隠された宝物").
  *   op = CODA_OP_FWD, args = coda_fwd_args_t*: t = x@W0 (bf16, workspace) ->
  *     add+RMSNorm row kernel (h, r, n = bf16(r*h*gamma) into the workspace) ->
  *     y = n@W1. Writes h, r and y; g is not written (this chain feeds n, not g,
