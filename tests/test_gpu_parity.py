@@ -432,6 +432,51 @@ def test_run_to_run_bitwise_determinism():
         assert torch.equal(p[k], q[k]), k
 
 
+@pytest.mark.parametrize("name", ["ragged", "unfolded_wide"])
+def test_stages_match_whole_call(name):
+    """coda_fwd_stage / coda_bwd_stage 0..n-1 in order give the whole call's results bit for bit, whether
+    GEMM1 combines r itself (ragged: stage 1 launches nothing) or a separate kernel does (unfolded_wide)."""
+    c = FWD_SMALL[name]
+    announce(f"stages vs whole call {name} {c}")
+    M, D, N = c["M"], c["D"], c["N"]
+    inp = to_dev(inputs.forward_inputs(**c, seed=5))
+    dY = inputs.output_grad(M, N, seed=5).to(DEV)
+    sp = L.current_stream(DEV)
+
+    def fwd_out():
+        return {"h": torch.empty(M, D, dtype=torch.bfloat16, device=DEV),
+                "g": torch.empty(M, D, dtype=torch.bfloat16, device=DEV),
+                "r": torch.empty(M, dtype=torch.float32, device=DEV),
+                "y": torch.empty(M, N, dtype=torch.bfloat16, device=DEV)}
+
+    def bwd_out():
+        return {"da": torch.empty(M, D, dtype=torch.bfloat16, device=DEV),
+                "dgamma": torch.empty(D, dtype=torch.float32, device=DEV),
+                "dW1": torch.empty(D, N, dtype=torch.bfloat16, device=DEV),
+                "s": torch.empty(M, dtype=torch.float32, device=DEV)}
+
+    res = []
+    for staged in (False, True):
+        fo, bo = fwd_out(), bwd_out()
+        for t in list(fo.values()) + list(bo.values()):
+            t.fill_(float("nan"))
+        F = L.bind_fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS, fo,
+                       L.workspace(L.CODA_OP_FWD, M, D, N, DEV))
+        B = L.bind_bwd(dY, fo["y"], fo["h"], fo["g"], fo["r"], inp["gamma"], inp["W1"], bo,
+                       L.workspace(L.CODA_OP_BWD, M, D, N, DEV))
+        for obj in (F, B):
+            if staged:
+                for i in range(obj.nstages):
+                    obj.stage(i, sp)
+            else:
+                obj.run(sp)
+        torch.cuda.synchronize()
+        res.append(dict(fo, **bo))
+    for k in res[0]:
+        assert torch.equal(res[0][k], res[1][k]), k
+    assert torch.isfinite(res[1]["r"]).all() and torch.isfinite(res[1]["y"].float()).all()
+
+
 GUARD = 4096  # elements of guard band on each side of every output
 
 
@@ -448,7 +493,8 @@ def guards_intact(buf):
     return bool(torch.all(g == 0x5A).item())
 
 
-@pytest.mark.parametrize("name,M", [("ragged", 300), ("ragged", 1), ("dims64", 300), ("dims64_rows", 24576)])
+@pytest.mark.parametrize("name,M", [("ragged", 300), ("ragged", 1), ("dims64", 300), ("dims64_rows", 24576),
+                                    ("unfolded_wide", 64)])
 def test_no_writes_outside_outputs(name, M):
     c = dict(FWD_SMALL[name], M=M)
     announce(f"canaries coda_fwd/coda_bwd {c}")
