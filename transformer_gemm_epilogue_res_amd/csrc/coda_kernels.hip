@@ -857,7 +857,7 @@ __global__ __launch_bounds__(256) void rms_combine_kernel(const float* P, float*
   float acc = 0.f;
   if (i < M) {
     const float* row = P + i * pcols;
-    if ((pcols & 3) == 0) {  // D a multiple of 256: 16-byte rows
+    if ((pcols & 3) == 0) {  // a multiple of 4 partials per row (D a multiple of 1024): 16-byte rows
       const float4* row4 = reinterpret_cast<const float4*>(row);
       for (int64_t t = l; t < pcols / 4; t += 16) {
         const float4 v = row4[t];
