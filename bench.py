@@ -210,7 +210,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the chain's kernels run on a single "
-              "device and this build has no multi-GPU path.", file=sys.stderr)
+              "device; there is no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,7 +1,7 @@
 """The host half of the C ABI (coda_host.cpp: workspace sizes, argument validation, status strings)
 built with g++ under AddressSanitizer and UndefinedBehaviorSanitizer and driven through valid and
 invalid arguments, including extreme sizes and enum fields holding arbitrary ints (CPU only; the
-HIP kernels are not part of this build)."""
+HIP kernels are not part of that compilation)."""
 import os
 import shutil
 import subprocess
