@@ -48,6 +48,13 @@ __device__ __forceinline__ void unpack8_bf16(uint4 v, float* o) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// e^v as 2^(v log2 e) on the hardware base-2 exponential (one v_exp_f32 after one multiply). Its result is
+// within a few fp32 ulps of e^v across the range the epilogues use (the rounding of v log2 e adds a relative
+// error of about |v| 2^-24), 0 where e^v underflows and +inf where it overflows -- what the softmax sums and
+// the sigmoid want at the ends. Every kernel that must agree bit for bit with another (the recomputing and
+// the stored-logits cross-entropy backward, fused and unfused) takes its exponentials from here.
+__device__ __forceinline__ float fast_exp(float v) { return __builtin_amdgcn_exp2f(v * 1.4426950408889634f); }
+
 // ------------------------------------------------------ coalesced stores
 //
 // In the MFMA layout a lane holds four adjacent columns of one row per tile, so
@@ -418,7 +425,9 @@ struct EpiRowScale {
 // four adjacent columns 16 tn + 4 (l / 16) + {0..3} of a row, i.e. two whole
 // pairs, so the activation and its backward are lane-local.
 
-__device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + expf(-v)); }
+// sigma(v) = 1 / (1 + e^-v) with the hardware reciprocal (v_rcp_f32, about 1 ulp): 0 as v -> -inf (1 / inf),
+// 1 as v -> +inf, NaN for NaN.
+__device__ __forceinline__ float sigmoidf_(float v) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-v)); }
 
 // Staging of a 128 x 32 bf16 block (64-byte rows; 16-byte chunk c of row r at
 // c ^ ((r >> 2) & 3), which spreads both passes over all 64 banks). put() takes
@@ -522,6 +531,25 @@ struct StageRows256 {
       if (i < M) *reinterpret_cast<u32x4_t*>(out + i * ldc + cb + 8 * c) = v;
     }
   }
+  // fill()'s staged layout written by LDS DMA: sixteen 1 KB instructions of four rows each; lane L fills
+  // 16-byte slot L % 16 of row 4 q + L / 16 with global chunk (L % 16) ^ (row & 15). Instruction q's
+  // descriptor is based at row mb + 4 q, so the range check (which covers the lane offset) is exact:
+  // rows past M read 0. Completes on vmcnt (wait_vm0 before get()).
+  __device__ __forceinline__ void fill_dma(const uint16_t* src, int64_t ldc, int64_t mb, int64_t cb, int64_t M) const {
+    const int rl = lane >> 4;
+    const uint16_t* p = src + mb * ldc + cb;
+    int64_t bytes = (M - mb) * ldc * 2 - cb * 2;
+    lds_char_t* dst = base;
+#pragma unroll 1  // one descriptor live at a time (the loop runs inside the mainloop's last step)
+    for (int q = 0; q < 16; ++q) {
+      const int c = (lane & 15) ^ ((4 * q + rl) & 15);
+      const uint32_t voff = uint32_t((rl * ldc + 8 * c) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p, bytes), (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+      p += 4 * ldc;
+      bytes -= 8 * ldc;
+      dst += 1024;
+    }
+  }
   __device__ __forceinline__ u32x4_t get(int row, int chunk) const {
     return *reinterpret_cast<const LDS_AS u32x4_t*>(base + off(row, chunk));
   }
@@ -539,20 +567,25 @@ struct StageRows256 {
 //   Ps[i, nb / 64] = sum over its 128 columns of dY y   (fp32 dY, bf16 y).
 // The wave's 128 x 128 block of y passes through the staging area in two halves
 // of 64 rows, read and written as whole 256-byte rows; each lane's dY replaces
-// the y it has just read, and the half is then stored.
+// the y it has just read, and the half is then stored. The first half is moved in
+// by DMA during the last K step, the second after the first has been stored.
 struct EpiSwigluBwd {
   const uint16_t* y;
   uint16_t* dY;
   float* Ps;
   int64_t M, F, pcols;
+  __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t*, int64_t mb, int64_t nb, int lane) const {
+    StageRows256{stage, lane}.fill_dma(y, 2 * F, mb, 2 * nb, M);
+  }
   __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
-                                             lds_char_t* stage) const {
+                                             lds_char_t* stage, lds_char_t*) const {
     const int li = lane & 15, lg = lane >> 4;
     const StageRows256 st{stage, lane};
+    wait_vm0();  // early()'s DMA of the first half
     auto do_half = [&](auto H) {  // H: std::integral_constant, so every acc index is a constant
       constexpr int half = decltype(H)::value;
       const int64_t hb = mb + 64 * half;  // first row of this half
-      st.fill(y, 2 * F, hb, 2 * nb, M);
+      if constexpr (half == 1) st.fill(y, 2 * F, hb, 2 * nb, M);
 #pragma unroll
       for (int t = 0; t < kTM / 2; ++t) {
         const int tm = (kTM / 2) * half + t, row = 16 * t + li;
@@ -628,7 +661,7 @@ struct EpiCeStats {
 #pragma unroll
       for (int tn = 0; tn < kTN; ++tn)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) l += expf(acc[tm][tn][e] - m);
+        for (int e = 0; e < 4; ++e) l += fast_exp(acc[tm][tn][e] - m);
       l += shfl_xor(l, 16);
       l += shfl_xor(l, 32);
       if (ok && lg == 0) Pml[i * pcols + nb / kWaveTileN] = make_float2(m, l);
@@ -689,7 +722,7 @@ struct EpiCeBwd {
       f32x4_t d;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = expf(acc[tm][tn][e] - ls[tm]);
+        const float p = fast_exp(acc[tm][tn][e] - ls[tm]);
         d[e] = dl[tm] * (p - (tc[tm] == 16 * tn + e ? 1.0f : 0.0f));
       }
       return d;
@@ -1047,7 +1080,7 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2* Pml, cons
   float l = 0.f;
   for (int64_t t = threadIdx.x; t < pcols; t += 256) {
     const float2 v = p[t];
-    l += v.y * expf(v.x - m);
+    l += v.y * fast_exp(v.x - m);
   }
   l = block_sum256(l, red);
   if (threadIdx.x == 0) {
@@ -1083,14 +1116,14 @@ __global__ __launch_bounds__(256) void ce_rows_fwd_kernel(const float* logits, c
 #pragma unroll
     for (int u = 0; u < kCeUnroll; ++u) mx = fmaxf(mx, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
     // a round always holds a real column (v0 < n4), so mx is finite
-    l *= expf(m - mx);
+    l *= fast_exp(m - mx);
 #pragma unroll
     for (int u = 0; u < kCeUnroll; ++u)
-      l += (expf(x[u].x - mx) + expf(x[u].y - mx)) + (expf(x[u].z - mx) + expf(x[u].w - mx));
+      l += (fast_exp(x[u].x - mx) + fast_exp(x[u].y - mx)) + (fast_exp(x[u].z - mx) + fast_exp(x[u].w - mx));
     m = mx;
   }
   const float mb = block_max256(m, red);
-  const float lb = block_sum256(m == -INFINITY ? 0.f : l * expf(m - mb), red);
+  const float lb = block_sum256(m == -INFINITY ? 0.f : l * fast_exp(m - mb), red);
   if (threadIdx.x == 0) {
     const float ls = mb + logf(lb);
     const int64_t t = targets[i];
@@ -1124,7 +1157,7 @@ __global__ __launch_bounds__(256) void ce_rows_bwd_kernel(const float* logits, c
         const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
         float d[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = dl * (expf(xs[e] - ls) - (4 * v + e == t ? 1.0f : 0.0f));
+        for (int e = 0; e < 4; ++e) d[e] = dl * (fast_exp(xs[e] - ls) - (4 * v + e == t ? 1.0f : 0.0f));
         dv[v] = pack4_bf16(d[0], d[1], d[2], d[3]);
       }
     }
