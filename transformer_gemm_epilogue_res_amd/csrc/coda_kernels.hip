@@ -48,6 +48,40 @@ __device__ __forceinline__ void unpack8_bf16(uint4 v, float* o) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Cross-lane reductions of the epilogues on the VALU, with no LDS round trip (shfl_xor is a ds_bpermute):
+// * across the four 16-lane rows (the lanes l, l ^ 16, l ^ 32, l ^ 48 that share an output row in the
+//   MFMA layout): the gfx950 lane swaps. v_permlane16_swap exchanges the odd rows of its first operand with
+//   the even rows of its second, so on two copies of v its two results hold rows (0, 0, 2, 2) and (1, 1, 3, 3),
+//   and combining them is v combined with lane l ^ 16; v_permlane32_swap does the same for the two halves
+//   (l ^ 32). Sums and maxima are commutative, so every lane gets the bits the xor butterfly gives.
+// * within a 16-lane row (the 16 rows of a tile held by one column of lanes): DPP quad permutations for
+//   l ^ 1 and l ^ 2, then the row's half-mirror (l <-> 7 - l) and mirror (l <-> 15 - l), which read the
+//   same values as l ^ 4 and l ^ 8 once the quads and then the octets are uniform: again the xor
+//   butterfly's bits in every lane.
+__device__ __forceinline__ float sum_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_row16(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]: l ^ 1
+  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]: l ^ 2
+  v += dpp_move<0x141>(v);  // row_half_mirror: the other quad of the octet
+  v += dpp_move<0x140>(v);  // row_mirror: the other octet of the row
+  return v;
+}
+
 // e^v as 2^(v log2 e) on the hardware base-2 exponential (one v_exp_f32 after one multiply). Its result is
 // within a few fp32 ulps of e^v across the range the epilogues use (the rounding of v log2 e adds a relative
 // error of about |v| 2^-24), 0 where e^v underflows and +inf where it overflows -- what the softmax sums and
@@ -308,8 +342,7 @@ struct EpiResidualSsq {
         }
       }
       // the 4 lanes l % 16 == li hold the rest of row i's 64 columns
-      ssq += shfl_xor(ssq, 16);
-      ssq += shfl_xor(ssq, 32);
+      ssq = sum_rows4(ssq);
       if (lane < 16) *reinterpret_cast<LDS_AS float*>(aux + kSsqAuxOffset + (16 * tm + li) * 4) = ssq;
     }
     store_block<false>(stage, lane, h, D, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
@@ -337,57 +370,58 @@ struct EpiResidualSsq {
 };
 
 // The row scales of GEMM1's epilogues, r_i = 1 / sqrt(sum_t P[i, t] / D + eps) (the deferred RMSNorm
-// factor). With P set, each wave combines them itself from the sums of squares P [M, pcols] of its 128
-// rows, brought into its staging area by DMA during the last K step (and read before the staging
-// area is reused): the four lanes of a row each add a strided share of its partials, then two
-// butterfly steps add the shares -- a fixed order that depends only on pcols, so every tile of a row
-// gets the same bits -- and the waves of tile column 0 write r. Without P (too many partials for the
-// staging area: a separate kernel combined them), r is an input, moved into aux.
+// factor). FOLD: each wave combines them itself from the sums of squares P [M, pcols] of its 128 rows,
+// brought into its staging area by DMA during the last K step (and read before the staging area is
+// reused): the four lanes of a row each add a strided share of its partials, then two butterfly steps
+// add the shares -- a fixed order that depends only on pcols, so every tile of a row gets the same
+// bits -- and the waves of tile column 0 write r. Otherwise (a separate kernel combined them) r is an
+// input, moved into aux. The two are separate instantiations, so neither carries the other's registers.
+template <bool FOLD>
 struct RowScaleSrc {
   float* r;
-  const float* P;
+  const float* P;  // FOLD only
   int64_t M, pcols;
   float D, eps;
   __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int lane) const {
-    if (P == nullptr) {
+    if constexpr (!FOLD) {
       dma_vec<2>(aux, r + mb, (M - mb) * 4, lane);
-      return;
-    }
-    // rows mb .. mb + 127 of P: 512 pcols contiguous bytes (0 past row M - 1)
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + mb * pcols, (M - mb) * pcols * 4);
-    if ((pcols & 3) == 0) {  // 16 bytes per lane: the rows are 16-byte multiples, so no chunk straddles row M
+    } else {
+      // rows mb .. mb + 127 of P: 512 pcols contiguous bytes (0 past row M - 1)
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(P + mb * pcols, (M - mb) * pcols * 4);
+      if ((pcols & 3) == 0) {  // 16 bytes per lane: the rows are 16-byte multiples, so no chunk straddles row M
 #pragma unroll 1
-      for (int q = 0; q < pcols / 2; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(stage + q * 1024), 16, uint32_t(q * 1024 + lane * 16), 0, 0, 0);
-    } else {  // 4 bytes per lane (exact to the element)
+        for (int q = 0; q < pcols / 2; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(stage + q * 1024), 16, uint32_t(q * 1024 + lane * 16), 0, 0, 0);
+      } else {  // 4 bytes per lane (exact to the element)
 #pragma unroll 1
-      for (int q = 0; q < 2 * pcols; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(stage + q * 256), 4, uint32_t(q * 256 + lane * 4), 0, 0, 0);
+        for (int q = 0; q < 2 * pcols; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(stage + q * 256), 4, uint32_t(q * 256 + lane * 4), 0, 0, 0);
+      }
     }
   }
   // rr[tm]: the scale of row mb + 16 tm + l % 16 (after early()'s DMA has landed)
   __device__ __forceinline__ void scales(float (&rr)[kTM], const lds_char_t* stage, const lds_char_t* aux, int64_t mb,
                                          int64_t nb, int lane) const {
     const int li = lane & 15, lg = lane >> 4;
-    if (P == nullptr) {
+    if constexpr (!FOLD) {
 #pragma unroll
       for (int tm = 0; tm < kTM; ++tm) rr[tm] = lds_f32(aux + (16 * tm + li) * 4);
-      return;
-    }
-#pragma unroll
-    for (int tm = 0; tm < kTM; ++tm) {
-      const int row = 16 * tm + li;
-      float s = 0.f;
-      for (int64_t q = lg; q < pcols; q += 4) s += lds_f32(stage + (row * pcols + q) * 4);
-      s += shfl_xor(s, 16);
-      s += shfl_xor(s, 32);
-      rr[tm] = 1.0f / sqrtf(s / D + eps);
-    }
-    if (nb == 0 && lg == 0) {
+    } else {
+      const int pc = int(pcols);  // at most 32 partials: 32-bit LDS offsets
 #pragma unroll
       for (int tm = 0; tm < kTM; ++tm) {
-        const int64_t i = mb + 16 * tm + li;
-        if (i < M) r[i] = rr[tm];
+        const int row = 16 * tm + li;
+        float s = 0.f;
+        for (int q = lg; q < pc; q += 4) s += lds_f32(stage + (row * pc + q) * 4);
+        s = sum_rows4(s);
+        rr[tm] = 1.0f / sqrtf(s / D + eps);
+      }
+      if (nb == 0 && lg == 0) {
+#pragma unroll
+        for (int tm = 0; tm < kTM; ++tm) {
+          const int64_t i = mb + 16 * tm + li;
+          if (i < M) r[i] = rr[tm];
+        }
       }
     }
   }
@@ -395,9 +429,9 @@ struct RowScaleSrc {
 static_assert(kWaveTileM * 4 * kFoldedCombineMaxCols <= kEpiWaveBytes, "a wave's partials fit its staging area");
 
 // GEMM1 epilogue: y = r_i * acc (the deferred RMSNorm row scale).
-template <bool F32>
+template <bool F32, bool FOLD>
 struct EpiRowScale {
-  RowScaleSrc rs;
+  RowScaleSrc<FOLD> rs;
   void* y;
   int64_t N;
   __device__ __forceinline__ void early(lds_char_t* stage, lds_char_t* aux, int64_t mb, int64_t, int lane) const {
@@ -455,9 +489,9 @@ struct StageBf16Half {
 // GEMM1 epilogue with SwiGLU: y = r_i * acc (stored in bf16: the backward needs
 // the gate and up values) and o_if = silu(y_i,2f) * y_i,2f+1 from the fp32 y,
 // stored in fp32 (F32) or bf16.
-template <bool F32>
+template <bool F32, bool FOLD>
 struct EpiRowScaleSwiglu {
-  RowScaleSrc rs;
+  RowScaleSrc<FOLD> rs;
   void* y;
   void* o;
   int64_t N;  // o has N / 2 columns
@@ -608,8 +642,7 @@ struct EpiSwigluBwd {
           st.put(row, chunk, u32x4_t{lo.x, lo.y, hi.x, hi.y});
         }
         // the 4 lanes l % 16 == li hold the rest of row i's 64 features
-        part += shfl_xor(part, 16);
-        part += shfl_xor(part, 32);
+        part = sum_rows4(part);
         const int64_t i = hb + row;
         if (lane < 16 && i < M) Ps[i * pcols + nb / kWaveTileN] = part;
       }
@@ -655,15 +688,13 @@ struct EpiCeStats {
       for (int tn = 0; tn < kTN; ++tn)
 #pragma unroll
         for (int e = 0; e < 4; ++e) m = fmaxf(m, acc[tm][tn][e]);
-      m = fmaxf(m, shfl_xor(m, 16));
-      m = fmaxf(m, shfl_xor(m, 32));
+      m = max_rows4(m);
       float l = 0.f;
 #pragma unroll
       for (int tn = 0; tn < kTN; ++tn)
 #pragma unroll
         for (int e = 0; e < 4; ++e) l += fast_exp(acc[tm][tn][e] - m);
-      l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
+      l = sum_rows4(l);
       if (ok && lg == 0) Pml[i * pcols + nb / kWaveTileN] = make_float2(m, l);
       const int64_t t = ok ? lds_i64(aux + (16 * tm + li) * 8) : -1;
       const int64_t c = t - nb;  // the target's column inside the wave tile
@@ -786,12 +817,7 @@ struct EpiRmsNormBwd {
       // column sums over the 16 lanes sharing l / 16 (they hold the 16 rows of each tile)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v = cs[e];
-        v += shfl_xor(v, 1);
-        v += shfl_xor(v, 2);
-        v += shfl_xor(v, 4);
-        v += shfl_xor(v, 8);
-        cs[e] = v;
+        cs[e] = sum_row16(cs[e]);
       }
       if (li == 0 && mb < M)  // a wave whose rows all lie past M has no Pg row
         *reinterpret_cast<float4*>(Pg + (mb / kWaveTileM) * D + j) = make_float4(cs[0], cs[1], cs[2], cs[3]);
@@ -1495,9 +1521,21 @@ hipError_t ce_bwd_products(const coda_ce_bwd_args_t* a, hipStream_t st) {
   return gemm_plain(pw, false, false, a->dW, a->D, a->dW_dtype == CODA_F32, st);
 }
 
-// GEMM1's row scales for the forward with partials P: combined in its epilogue, or read from r.
-RowScaleSrc row_scale_src(const coda_fwd_args_t* a, const float* P) {
-  return RowScaleSrc{a->r, fwd_folds_combine(a->M, a->D, a->N) ? P : nullptr, a->M, ssq_cols(a->D), float(a->D), a->eps};
+// GEMM1 g @ W1 with a row-scale epilogue Epi<F32, FOLD> (EpiRowScale or EpiRowScaleSwiglu), whose row scales
+// are combined from the partials P in the epilogue where fwd_folds_combine says so, else read from r;
+// `more` are the epilogue's fields after its row scales.
+template <template <bool, bool> class Epi, class... More>
+hipError_t launch_gemm1(const coda_fwd_args_t* a, const float* P, bool f32, hipStream_t st, More... more) {
+  const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
+  const int64_t pcols = ssq_cols(a->D);
+  if (fwd_folds_combine(a->M, a->D, a->N)) {
+    const RowScaleSrc<true> rs{a->r, P, a->M, pcols, float(a->D), a->eps};
+    return f32 ? launch_gemm<true, false>(p1, Epi<true, true>{rs, more...}, st)
+               : launch_gemm<true, false>(p1, Epi<false, true>{rs, more...}, st);
+  }
+  const RowScaleSrc<false> rs{a->r, nullptr, a->M, pcols, float(a->D), a->eps};
+  return f32 ? launch_gemm<true, false>(p1, Epi<true, false>{rs, more...}, st)
+             : launch_gemm<true, false>(p1, Epi<false, false>{rs, more...}, st);
 }
 
 // Stage `stage` of the fused forward (0 GEMM0 + epilogue, 1 r combine, 2 GEMM1 + row scale) with the
@@ -1528,10 +1566,7 @@ hipError_t fwd_stage(int stage, const coda_fwd_args_t* a, float* P, float* part,
     return hipGetLastError();
   }
   // GEMM1 g @ W1 with the row-scale epilogue
-  const GemmShape p1{a->M, a->N, a->D, a->g, a->D, a->W1, a->N};
-  const RowScaleSrc rs = row_scale_src(a, P);
-  if (a->y_dtype == CODA_F32) return launch_gemm<true, false>(p1, EpiRowScale<true>{rs, a->y, a->N}, st);
-  return launch_gemm<true, false>(p1, EpiRowScale<false>{rs, a->y, a->N}, st);
+  return launch_gemm1<EpiRowScale>(a, P, a->y_dtype == CODA_F32, st, a->y, a->N);
 }
 
 // ------------------------------------------------- no-allocation forward
@@ -1726,11 +1761,9 @@ coda_status_t coda_fwd_swiglu(const coda_fwd_swiglu_args_t* a, void* ws, size_t 
   for (int s = 0; s < 2; ++s)  // GEMM0 with its epilogue, then r
     if ((v = coda_fwd_stage(s, c, ws, ws_bytes, stream)) != CODA_OK) return v;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const GemmShape p1{c->M, c->N, c->D, c->g, c->D, c->W1, c->N};
-  const RowScaleSrc rs = row_scale_src(c, static_cast<const float*>(ws));  // P leads the workspace
-  if (a->o_dtype == CODA_F32)
-    return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<true>{rs, c->y, a->o, c->N}, st));
-  return to_status(launch_gemm<true, false>(p1, EpiRowScaleSwiglu<false>{rs, c->y, a->o, c->N}, st));
+  // P leads the workspace
+  return to_status(launch_gemm1<EpiRowScaleSwiglu>(c, static_cast<const float*>(ws), a->o_dtype == CODA_F32, st,
+                                                   c->y, a->o, c->N));
 }
 
 coda_status_t coda_bwd_swiglu(const coda_bwd_swiglu_args_t* a, void* ws, size_t ws_bytes, void* stream) {
