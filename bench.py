@@ -41,14 +41,20 @@ def log(*a):
 
 
 def stage_work(M, K0, D, N):
-    """Per-launch algorithmic work: ('flop', F) for MFMA kernels, ('byte', B) for HBM-bound ones."""
+    """Per-launch algorithmic work: ('flop', F) for MFMA kernels, ('byte', B) for HBM-bound ones. With at
+    least 16 of the dW1 GEMM's 256-row tiles (D > 3840) s comes from that GEMM's side work, as partials
+    [2 ceil(N / 256), M] that the s stage adds up; otherwise the s stage is a row kernel over dY and y."""
+    ceil = lambda a, b: -(-a // b)
+    rowdot = ceil(D, 256) >= 16
     return {
         "gemm0_residual_ssq": ("flop", 2 * M * K0 * D),
-        "rms_combine": ("byte", M * (D // 64) * 4 + M * 4),
+        "rms_combine": ("byte", M * ceil(D, 256) * 4 + M * 4),
         "gemm1_rowscale": ("flop", 2 * M * D * N),
-        "rowstat_s_rg": ("byte", 2 * M * N * 2 + 2 * M * D * 2 + 2 * M * 4),
+        "gr_transpose": ("byte", M * D * 2 + M * 4 + D * ceil(M, 64) * 64 * 2),
+        "wgrad_rowdot": ("flop", 2 * M * D * N),
+        "s_combine": ("byte", (2 * ceil(N, 256) * M * 4 if rowdot else 2 * M * N * 2) + M * 4),
         "dgrad_rmsnorm_bwd": ("flop", 2 * M * N * D),
-        "wgrad_dgamma": ("flop", 2 * M * D * N),
+        "dgamma_combine": ("byte", ceil(M, 128) * D * 4 + D * 4),
     }
 
 
@@ -588,7 +594,7 @@ def main():
                 "pct_peak": round(100 * fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / bwd_ms / 1e9, 1),
                 "pct_peak": round(100 * bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                "ms_without_rowstat": round(bwd_ms - per["rowstat_s_rg"], 4)},
+                "s_combine_ms": round(per["s_combine"], 4)},
         "configs": configs, "bwd_gemm0": bwd_gemm0, "swiglu": swiglu, "cross_entropy": ce,
         "kernels": kernels, "roofline": roof, "unfused": unfused, "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),

@@ -354,12 +354,15 @@ coda_status_t coda_fwd(const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void
 coda_status_t coda_validate_fwd_noalloc(const coda_fwd_args_t* a);
 coda_status_t coda_fwd_noalloc(const coda_fwd_args_t* a, void* stream);
 
-/* Fused backward: row statistic s and bf16(r*g) (transposed, so the dW1
- * GEMM's left operand is contiguous along its contraction) -> G = dY@W1^T with the
- * RMSNorm-backward epilogue (da, dgamma column partials) -> dW1 = bf16(r*g)^T @ dY,
- * whose blocks also reduce the dgamma partials, 64 columns at a time in a fixed
- * order, before their own tiles: the auxiliary reduction folded into the next
- * kernel. */
+/* Fused backward: bf16(r*g) transposed (so the dW1 GEMM's left operand is
+ * contiguous along its contraction) -> dW1 = bf16(r*g)^T @ dY, which also takes
+ * the row statistic s_i = sum_n dY_in y_in from the dY tiles it already streams
+ * (partials of 128 columns, hotdry blog, section "反向传播的 GEMM-Epilogue 结构":
+ * s in the kernel that reads dY) -> s, their fixed-order sum -> G = dY@W1^T with the
+ * RMSNorm-backward epilogue (da, dgamma column partials) -> dgamma, the partials'
+ * fixed-order sum. With D <= 3840 (fewer than 16 of the dW1 GEMM's 256-row tiles,
+ * too few to deal a K step's 64 rows over) a row kernel over dY and y computes s
+ * instead. */
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
 /* The stages of coda_fwd and coda_bwd, one kernel each (two for a split GEMM), for callers that
@@ -372,11 +375,12 @@ coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void
  *   forward : 0 GEMM0 + residual/h/g/sum-of-squares epilogue, 1 r combine (launches
  *             nothing where GEMM1's epilogue combines r itself, see coda_fwd),
  *             2 GEMM1 + row-scale epilogue
- *   backward: 0 s, then bf16(r*g) transposed for the dW1 GEMM (two kernels),
- *             1 G = dY@W1^T + RMSNorm-backward epilogue, 2 dW1 GEMM, whose blocks
- *             also reduce the dgamma partials */
+ *   backward: 0 bf16(r*g) transposed for the dW1 GEMM, 1 dW1 GEMM (and s's
+ *             partials, D > 3840), 2 s (the partials' sum, or the row kernel),
+ *             3 G = dY@W1^T + RMSNorm-backward epilogue, 4 dgamma (the column
+ *             partials' sum) */
 #define CODA_FWD_STAGES 3
-#define CODA_BWD_STAGES 3
+#define CODA_BWD_STAGES 5
 coda_status_t coda_fwd_stage(int stage, const coda_fwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream);
 
@@ -387,9 +391,10 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
  *     add+RMSNorm row kernel (h, r, n = bf16(r*h*gamma) into the workspace) ->
  *     y = n@W1. Writes h, r and y; g is not written (this chain feeds n, not g,
  *     to the second GEMM).
- *   op = CODA_OP_BWD, args = coda_bwd_args_t*: same s / bf16(r*g) kernel ->
- *     G = dY@W1^T stored as bf16 in the workspace -> RMSNorm-backward row kernel
- *     (da, dgamma partials) -> dgamma combine -> same dW1 GEMM.
+ *   op = CODA_OP_BWD, args = coda_bwd_args_t*: a row kernel for s and bf16(r*g)
+ *     (row layout) -> G = dY@W1^T stored as bf16 in the workspace ->
+ *     RMSNorm-backward row kernel (da, dgamma partials) -> dgamma combine ->
+ *     dW1 GEMM on the row-layout bf16(r*g).
  *   op = CODA_OP_FWD_SWIGLU, args = coda_fwd_swiglu_args_t*: the fused chain
  *     forward (coda_fwd, y stored bf16) -> a row kernel o = silu(gate) * up from
  *     the stored y. Only the SwiGLU step is unfused.

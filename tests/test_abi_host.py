@@ -99,10 +99,20 @@ def test_workspace_sizes():
     assert L.workspace_bytes(L.CODA_OP_BWD, M, D, N) == (
         gr_bytes(M, D) + a256(math.ceil(M / 8) * D * 4) + a256(S * M * D * 4))
     assert dgrad_split(8192, 4096, 28672) == (1, 0)  # the Llama-3-8B step: 512 tiles, no split
-    assert L.workspace_bytes(L.CODA_OP_BWD, 8192, 4096, 28672) == a256(8192 * 4096 * 2) + a256(64 * 4096 * 4)
+    # with at least 16 row tiles in the dW1 GEMM (D > 3840) s comes from that GEMM's row-dot partials
+    # Ps [ceil(N / 256), M], which follow the rest
+    assert L.workspace_bytes(L.CODA_OP_BWD, 8192, 4096, 28672) == (
+        a256(8192 * 4096 * 2) + a256(64 * 4096 * 4) + a256(112 * 8192 * 4))
     assert dgrad_split(1024, 4096, 28672) == (4, 7168)  # a data-parallel shard: 64 tiles -> 4 slices
     assert L.workspace_bytes(L.CODA_OP_BWD, 1024, 4096, 28672) == (
-        a256(1024 * 4096 * 2) + a256(1024 // 8 * 4096 * 4) + a256(4 * 1024 * 4096 * 4))  # dgamma partials of 8-row groups
+        a256(1024 * 4096 * 2) + a256(1024 // 8 * 4096 * 4) + a256(4 * 1024 * 4096 * 4)  # dgamma partials of 8-row groups
+        + a256(112 * 1024 * 4))
+    for Dr, rowdot in ((3840, False), (3904, True)):  # 15 and 16 (61 x 64: the last one ragged) row tiles
+        Sr, _ = dgrad_split(300, Dr, 576)
+        assert Sr == 2
+        assert L.workspace_bytes(L.CODA_OP_BWD, 300, Dr, 576) == (
+            gr_bytes(300, Dr) + a256(math.ceil(300 / 8) * Dr * 4) + a256(2 * 300 * Dr * 4)
+            + (a256(3 * 300 * 4) if rowdot else 0))
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_FWD, M, D, N) == 2 * a256(M * D * 2)
     assert L.workspace_bytes(L.CODA_OP_UNFUSED_BWD, M, D, N) == 2 * a256(M * D * 2) + a256(math.ceil(M / 32) * D * 4)
     assert L.workspace_bytes(L.CODA_OP_FWD, 0, D, N) == 0

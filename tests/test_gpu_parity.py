@@ -218,6 +218,13 @@ BWD_SMALL = {
     "two_k_steps": dict(M=100, K0=256, D=256, N=512),  # dW1 contracts over two K steps (rows padded to 128)
     "dims64": dict(M=300, K0=192, D=320, N=576),          # the data gradient split in 2 slices
     "dims64_rows": dict(M=24576, K0=192, D=320, N=576),   # unsplit: the last column tile has one live wave
+    # s from the dW1 GEMM's side work (at least 16 row tiles, D > 3840): its K steps are 64 rows of M
+    "rowdot": dict(M=300, K0=256, D=4096, N=576),         # 5 K steps, a ragged last one; 64 live columns in the last tile
+    "rowdot_k1": dict(M=40, K0=256, D=3904, N=320),       # one K step; 61 x 64 = 16 row tiles, the last one ragged
+    "rowdot_k2": dict(M=100, K0=256, D=4096, N=256),      # two K steps
+    "rowdot_k3": dict(M=150, K0=256, D=4096, N=512),      # three: the first, the one without a next DMA, the last
+    "rowdot_wide": dict(M=130, K0=256, D=8192, N=320),    # 32 row tiles: one row per block and K step
+    "rowdot_flush": dict(M=4100, K0=256, D=4096, N=320),  # 65 K steps: a flush after 64 and a tail of one
 }
 
 
@@ -415,9 +422,14 @@ def test_bwd_gemm0_llama3_8b_sampled():
 
 # ------------------------------------------------------ determinism, canaries
 
-def test_run_to_run_bitwise_determinism():
-    c = FWD_SMALL["ragged"]
-    announce(f"determinism coda_fwd/coda_bwd {c}")
+def shape(name):
+    return FWD_SMALL[name] if name in FWD_SMALL else BWD_SMALL[name]
+
+
+@pytest.mark.parametrize("name", ["ragged", "rowdot"])
+def test_run_to_run_bitwise_determinism(name):
+    c = shape(name)
+    announce(f"determinism coda_fwd/coda_bwd {name} {c}")
     inp = to_dev(inputs.forward_inputs(**c, seed=1))
     a = L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
     b = L.fwd(inp["x"], inp["W0"], inp["z"], inp["gamma"], inp["W1"], EPS)
@@ -432,11 +444,12 @@ def test_run_to_run_bitwise_determinism():
         assert torch.equal(p[k], q[k]), k
 
 
-@pytest.mark.parametrize("name", ["ragged", "unfolded_wide"])
+@pytest.mark.parametrize("name", ["ragged", "unfolded_wide", "rowdot"])
 def test_stages_match_whole_call(name):
     """coda_fwd_stage / coda_bwd_stage 0..n-1 in order give the whole call's results bit for bit, whether
-    GEMM1 combines r itself (ragged: stage 1 launches nothing) or a separate kernel does (unfolded_wide)."""
-    c = FWD_SMALL[name]
+    GEMM1 combines r itself (ragged: stage 1 launches nothing) or a separate kernel does (unfolded_wide), and
+    whether s comes from a row kernel or from the dW1 GEMM's side work (rowdot)."""
+    c = shape(name)
     announce(f"stages vs whole call {name} {c}")
     M, D, N = c["M"], c["D"], c["N"]
     inp = to_dev(inputs.forward_inputs(**c, seed=5))
@@ -494,9 +507,9 @@ def guards_intact(buf):
 
 
 @pytest.mark.parametrize("name,M", [("ragged", 300), ("ragged", 1), ("dims64", 300), ("dims64_rows", 24576),
-                                    ("unfolded_wide", 64)])
+                                    ("unfolded_wide", 64), ("rowdot", 300), ("rowdot_k1", 1), ("rowdot_wide", 130)])
 def test_no_writes_outside_outputs(name, M):
-    c = dict(FWD_SMALL[name], M=M)
+    c = dict(shape(name), M=M)
     announce(f"canaries coda_fwd/coda_bwd {c}")
     inp = to_dev(inputs.forward_inputs(**c, seed=2))
     D, N = c["D"], c["N"]
@@ -521,11 +534,12 @@ def test_no_writes_outside_outputs(name, M):
     assert torch.isfinite(out["y"].float()).all() and torch.isfinite(bo["da"]).all()
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("name", ["ragged", "rowdot"])
+def test_graph_capture_replays_match_eager(name):
     """The step (coda_fwd + coda_bwd) captured into a HIP graph: the library allocates, frees and
     clears nothing, so every replay reproduces the eager results bit for bit."""
-    c = FWD_SMALL["ragged"]
-    announce(f"graph capture coda_fwd + coda_bwd {c}")
+    c = shape(name)
+    announce(f"graph capture coda_fwd + coda_bwd {name} {c}")
     M, D, N = c["M"], c["D"], c["N"]
     inp = to_dev(inputs.forward_inputs(**c, seed=4))
     dY = inputs.output_grad(M, N, seed=4).to(DEV)

@@ -24,9 +24,9 @@ CODA_BF16, CODA_F32 = 0, 1
  CODA_OP_CE_FWD, CODA_OP_CE_BWD, CODA_OP_UNFUSED_FWD_SWIGLU, CODA_OP_UNFUSED_BWD_SWIGLU,
  CODA_OP_UNFUSED_CE_FWD, CODA_OP_UNFUSED_CE_BWD) = range(12)
 CODA_ROW, CODA_COL = 0, 1
-CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 3
+CODA_FWD_STAGES, CODA_BWD_STAGES = 3, 5
 FWD_STAGE_NAMES = ("gemm0_residual_ssq", "rms_combine", "gemm1_rowscale")
-BWD_STAGE_NAMES = ("rowstat_s_rg", "dgrad_rmsnorm_bwd", "wgrad_dgamma")
+BWD_STAGE_NAMES = ("gr_transpose", "wgrad_rowdot", "s_combine", "dgrad_rmsnorm_bwd", "dgamma_combine")
 
 
 class FwdArgs(ctypes.Structure):

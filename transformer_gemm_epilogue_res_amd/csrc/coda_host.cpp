@@ -99,7 +99,7 @@ size_t coda_workspace_bytes(coda_op_t op, int64_t M, int64_t D, int64_t N) {
   if (!rows_ok(M) || !dim_ok(D)) return 0;
   switch (op) {
     case CODA_OP_FWD: return fwd_ws(M, D);
-    case CODA_OP_BWD: return dim_ok(N) ? bwd_ws(M, D, N) : 0;
+    case CODA_OP_BWD: return dim_ok(N) ? bwd_chain_ws(M, D, N) : 0;
     case CODA_OP_UNFUSED_FWD: return unfused_fwd_ws(M, D);
     case CODA_OP_UNFUSED_BWD: return unfused_bwd_ws(M, D);
     case CODA_OP_FWD_SWIGLU: return (dim_ok(N) && N % 128 == 0) ? fwd_ws(M, D) : 0;
@@ -130,7 +130,7 @@ coda_status_t coda_validate_fwd_noalloc(const coda_fwd_args_t* a) {
 coda_status_t coda_validate_bwd(const coda_bwd_args_t* a, const void* ws, size_t ws_bytes) {
   coda_status_t st = validate_bwd_common(a);
   if (st != CODA_OK) return st;
-  return check_ws(ws, ws_bytes, bwd_ws(a->M, a->D, a->N));
+  return check_ws(ws, ws_bytes, bwd_chain_ws(a->M, a->D, a->N));
 }
 
 // Used by the unfused entry point (g is optional there).

@@ -116,6 +116,15 @@ inline size_t bwd_ws(int64_t M, int64_t D, int64_t N) {
   const KSplit k = dgrad_split(M, D, N);
   return bwd_ws_part(M, D, N) + (k.S > 1 ? align256(size_t(k.S) * size_t(M) * size_t(D) * 4) : 0);
 }
+// The fused chain backward takes s as side work of its weight-gradient GEMM when each K step's 64 rows
+// can be dealt over that GEMM's row tiles at four per block: at least 16 row tiles (D > 3840); with
+// fewer, a row kernel computes s. The side work's partials Ps[rowdot_cols(N), M] (one per row and
+// 256-column tile) follow the shared backward workspace.
+inline bool bwd_rowdot(int64_t D) { return ceil_div(D, kBN) >= 16; }
+inline int64_t rowdot_cols(int64_t N) { return ceil_div(N, kBN); }
+inline size_t bwd_chain_ws(int64_t M, int64_t D, int64_t N) {
+  return bwd_ws(M, D, N) + (bwd_rowdot(D) ? align256(size_t(rowdot_cols(N)) * size_t(M) * 4) : 0);
+}
 // SwiGLU backward workspace: the fused backward's, then the s partials Ps.
 inline size_t bwd_swiglu_ws(int64_t M, int64_t D, int64_t N) {
   return bwd_ws(M, D, N) + align256(size_t(M) * size_t(swiglu_s_cols(N)) * 4);

@@ -302,6 +302,117 @@ struct EpiStoreDgamma {
   }
 };
 
+// The RMSNorm backward's row statistic s_i = sum_n dY_in y_in (hotdry blog, section "反向传播的 GEMM-Epilogue
+// 结构": the row dot product of the output gradient with the saved output), as side work of the weight-gradient
+// GEMM dW1 = bf16(r g)^T @ dY, which already streams dY: its B tile of K step k holds dY's rows 64 k .. 64 k + 63,
+// columns n0 .. n0 + 255 (a K-cols tile). In step k the block of row tile j (of ndt >= 16 row tiles) takes the
+// step's rows j + ndt p, p = 0 .. 3, that are below 64 -- every row of every step then has exactly one block
+// and slot -- over its 256 columns, wave p of group 0 row slot p: lane l the columns 4 l .. 4 l + 3. Per step a
+// lane multiplies the four dY values (read from the B tile with its fragments) by the four y values (loaded one
+// step ahead) and adds them (two v_dot2c_f32_bf16); the wave sums the products of each 16-lane row (its 64
+// columns) and shifts those sums into a per-row register (lane i of a row: the sum of step k - i), one stage
+// after each of six consecutive MFMAs of the step, so that the MFMAs cover the stages' latencies. Every 16
+// steps the four rows are added, giving the 16 steps' sums over the tile's 256 columns, which lanes 0 .. 15
+// store to Ps[tile_n, i] (i the row). colsum_kernel adds a row's ceil(N / 256) partials in a fixed order.
+struct RowDotSide {
+  static constexpr bool kActive = true;
+  static constexpr int kAt = 8;      // step() follows this MFMA of C(k)
+  static constexpr int kFlush = 16;  // steps per flush: the lanes of one row
+  const char* y0;                    // &y[0, n0]
+  int64_t ld, rows, tail;            // N, M, bytes of y from y0 on
+  float* Ps;                         // this tile's partials: Ps[tile_n, 0 ..]
+  uint32_t voff;                     // (row N + 4 l) * 2; past every record when the lane has no row or column
+  uint32_t lds;                      // LDS address of the lane's dY values in B slot 0
+  int row;                           // the wave's row within a K step, -1 if none
+  bool col_ok;
+  u32x2_t yv, dv;
+  float pv;                          // this step's products, then their 16-lane row sum
+  float acc;                         // lane i of each 16-lane row: that row's sum of step k - i
+
+  __device__ __forceinline__ void load(int k) {
+    const int64_t k0 = int64_t(k) * kBK;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(y0 + k0 * ld * 2, tail - k0 * ld * 2);
+    yv = __builtin_amdgcn_raw_buffer_load_b64(rs, int(voff), 0, 0);
+  }
+  __device__ __forceinline__ void read(int k) {
+    asm volatile("ds_read_b64 %0, %1" : "=v"(dv) : "v"(lds + uint32_t(k & 1) * kTileBytes));
+  }
+  __device__ __forceinline__ void landed() { asm volatile("" : "+v"(dv)); }
+  // After MFMA I of C(k), from I = kAt on, one stage each (an empty volatile asm holds each stage's result
+  // there: left alone, the compiler sinks the chain below the last MFMA, onto the phase's critical path):
+  // the products, the four adds of the 16-lane row sum, the shift.
+  template <int I>
+  __device__ __forceinline__ void work() {
+    if constexpr (I == kAt) {
+      // the halves as scalars first: __builtin_bit_cast of a vector component (dv.y) reads component 0 here
+      const uint32_t d0 = dv.x, d1 = dv.y, y0v = yv.x, y1v = yv.y;
+      const float v = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2_t, d0), __builtin_bit_cast(bf16x2_t, y0v),
+          __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, d1), __builtin_bit_cast(bf16x2_t, y1v), 0.f, false),
+          false);
+      pv = col_ok ? v : 0.f;
+    } else if constexpr (I == kAt + 1) {
+      pv += dpp_move<0xB1>(pv);   // l ^ 1
+    } else if constexpr (I == kAt + 2) {
+      pv += dpp_move<0x4E>(pv);   // l ^ 2
+    } else if constexpr (I == kAt + 3) {
+      pv += dpp_move<0x141>(pv);  // the other quad of the octet
+    } else if constexpr (I == kAt + 4) {
+      pv += dpp_move<0x140>(pv);  // the other octet: the row's 64 columns, in all its lanes
+    } else if constexpr (I == kAt + 5) {
+      // acc moves up one lane within each row (DPP row_shr:1); lane 0 of a row, which has no source, keeps pv
+      acc = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(pv), __float_as_int(acc), 0x111, 0xF, 0xF, false));
+      asm volatile("" : "+v"(acc));
+      return;
+    }
+    if constexpr (I >= kAt && I < kAt + 5) asm volatile("" : "+v"(pv));
+  }
+  // Steps k0 .. k0 + n - 1 (n <= 16) since the last flush: lane i < n of each row holds step k0 + n - 1 - i.
+  __device__ __forceinline__ void flush(int k0, int n) const {
+    if (row < 0) return;
+    const float tot = sum_rows4(acc);
+    const int l = int(__lane_id());
+    const int64_t i = (int64_t(k0) + n - 1 - l) * kBK + row;
+    if (l < n && i < rows) Ps[i] = tot;
+  }
+  __device__ __forceinline__ void flush(int k) const { flush(k - kFlush, kFlush); }
+};
+
+// The weight-gradient GEMM's plain store of dW1 [D, N], with the row statistic's partials as side work (the
+// chain's M rows are this GEMM's contraction; Ps is [ceil(N / 256), M]).
+template <bool F32>
+struct EpiStoreRowDot {
+  void* C;
+  int64_t ldc, M;
+  const uint16_t* y;
+  float* Ps;
+  int64_t N, rows;
+  int ndt;
+  __device__ __forceinline__ RowDotSide side(int tile_m, int tile_n, int64_t n0, int wave, int lane,
+                                             lds_char_t* smem) const {
+    RowDotSide s;
+    const int r = tile_m + ndt * (wave & 3);
+    s.row = (wave < 4 && r < kBK) ? r : -1;
+    const int col = 4 * lane;
+    s.col_ok = n0 + col < N;
+    const int rr = s.row < 0 ? 0 : s.row;
+    s.voff = (s.row >= 0 && s.col_ok) ? uint32_t((int64_t(rr) * N + col) * 2) : 0x80000000u;
+    s.lds = lds_u32(smem) + uint32_t(kBBase + rr * 512 + ((((col >> 3) ^ swz_kcols(rr)) << 4) | ((col & 7) * 2)));
+    s.y0 = reinterpret_cast<const char*>(y + n0);
+    s.ld = N;
+    s.rows = rows;
+    s.tail = (rows * N - n0) * 2;
+    s.Ps = Ps + int64_t(tile_n) * rows;
+    s.yv = s.dv = u32x2_t{0u, 0u};
+    s.pv = s.acc = 0.f;
+    return s;
+  }
+  __device__ __forceinline__ void operator()(f32x4_t (&acc)[kTM][kTN], int64_t mb, int64_t nb, int lane,
+                                             lds_char_t* stage) const {
+    store_block<F32>(stage, lane, C, ldc, mb, nb, M, [&](int tm, int tn) { return acc[tm][tn]; });
+  }
+};
+
 // GEMM0 epilogue: h = acc + z (fp32) -> store bf16 h; g = bf16(h * gamma) from
 // the fp32 h; per-row sum of squares of the fp32 h over the wave's 64 columns,
 // left in the wave's auxiliary LDS; after a block barrier finish() adds the four
@@ -847,6 +958,19 @@ struct HasFinish : std::false_type {};
 template <class Epi>
 struct HasFinish<Epi, decltype(std::declval<const Epi&>().finish(nullptr, 0, 0, 0, 0), void())> : std::true_type {};
 
+// ... and side work in the mainloop (side(tile_m, tile_n, n0, wave, lane, smem) gives the wave's side
+// object, see NoSide); such a GEMM is never split over its contraction.
+template <class Epi, class = void>
+struct HasSide : std::false_type {};
+template <class Epi>
+struct HasSide<Epi, decltype(std::declval<const Epi&>().side(0, 0, 0, 0, 0, nullptr), void())> : std::true_type {};
+template <class Epi>
+__device__ __forceinline__ auto make_side(const Epi& epi, int tile_m, int tile_n, int64_t n0, int wave, int lane,
+                                          lds_char_t* smem) {
+  if constexpr (HasSide<Epi>::value) return epi.side(tile_m, tile_n, n0, wave, lane, smem);
+  else return NoSide{};
+}
+
 template <bool A_K, bool B_K, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, const Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSmemBytes];
@@ -872,10 +996,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
   // N: in the last column tile, a wave past N runs the mainloop (its loads read zeros or other rows'
   // values, in bounds) but writes nothing -- no output, no partial statistics.
   const bool cols_in = nb < p.N;
+  auto side = make_side(epi, tile_m, tile_n, n0, wave, lane, smem);
   if (wave < 4) {
     mainloop<A_K, B_K, 0>(p, m0, n0, smem, acc, [&] {
       if constexpr (HasEarly<Epi>::value) epi.early(stage, aux, m0, nb, lane);
-    });
+    }, side);
     if (!cols_in) {
       wait_vm0();
     } else if constexpr (HasEarly<Epi>::value) {
@@ -886,7 +1011,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
   } else {
     mainloop<A_K, B_K, 1>(p, m0, n0, smem, acc, [&] {
       if constexpr (HasEarly<Epi>::value) epi.early(stage, aux, m0 + kWaveTileM, nb, lane);
-    });
+    }, side);
     if (!cols_in) {
       wait_vm0();
     } else if constexpr (HasEarly<Epi>::value) {
@@ -894,6 +1019,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmShape p0, cons
     } else {
       epi(acc, m0 + kWaveTileM, nb, lane, stage);
     }
+  }
+  if constexpr (decltype(side)::kActive) {  // the steps since the loop's last flush
+    const int KT = int(dceil_div(p.K, kBK)), F = decltype(side)::kFlush;
+    side.flush((KT - 1) / F * F, (KT - 1) % F + 1);
   }
   if constexpr (HasFinish<Epi>::value) {
     wait_lgkm0();  // this wave's LDS writes for finish()
@@ -1013,25 +1142,36 @@ __global__ __launch_bounds__(kRowThreads) void rowstat_kernel(const uint16_t* dY
   if (threadIdx.x == 0) s[i] = tot;
 }
 
-// dgamma_j = sum_t Pg[t, j]. A 256-thread block covers 32 columns; its 8 row
-// groups each sum every 8th partial row, then the 8 group sums are added in a
-// fixed order.
+// Column sums out_j = sum_t P[t, j] of partials P[rows, D]: dgamma from the data-gradient GEMM's
+// column partials, and s from the weight-gradient GEMM's row-dot partials (stored with the row index as
+// the column). A 256-thread block covers 32 columns; its 8 row groups each sum every 8th partial row,
+// four rows per round in four independent sums (four loads in flight), which are then added in a fixed
+// order, as are the 8 group sums.
 constexpr int kDgCols = 32, kDgGroups = 8;
-__global__ __launch_bounds__(256) void dgamma_combine_kernel(const float* Pg, float* dgamma, int64_t rows,
-                                                             int64_t D) {
+__global__ __launch_bounds__(256) void colsum_kernel(const float* P, float* out, int64_t rows, int64_t D) {
   __shared__ float part[kDgGroups][kDgCols];
   const int c = threadIdx.x % kDgCols, q = threadIdx.x / kDgCols;
   const int64_t j = int64_t(blockIdx.x) * kDgCols + c;
   float acc = 0.f;
-  if (j < D)
-    for (int64_t t = q; t < rows; t += kDgGroups) acc += Pg[t * D + j];
+  if (j < D) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    int64_t t = q;
+    for (; t + 3 * kDgGroups < rows; t += 4 * kDgGroups) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] += P[(t + u * kDgGroups) * D + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u)  // the last rounds' rows (fewer than four)
+      if (t + u * kDgGroups < rows) a[u] += P[(t + u * kDgGroups) * D + j];
+    acc = (a[0] + a[1]) + (a[2] + a[3]);
+  }
   part[q][c] = acc;
   __syncthreads();
   if (q == 0 && j < D) {
     float tot = 0.f;
 #pragma unroll
     for (int g = 0; g < kDgGroups; ++g) tot += part[g][c];
-    dgamma[j] = tot;
+    out[j] = tot;
   }
 }
 
@@ -1418,22 +1558,12 @@ hipError_t gemm_plain(const GemmShape& p, bool a_k, bool b_k, void* C, int64_t l
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
-// s and bf16(r * g), then the weight gradient dW1 = bf16(r g)^T @ dY.
-// bf16(r g) transposed into grT [D, gr_cols(M)] for the weight-gradient GEMM.
+// bf16(r g) transposed into grT [D, gr_cols(M)] for the weight-gradient GEMM dW1 = bf16(r g)^T @ dY.
 hipError_t gr_transpose(const uint16_t* g, const float* r, uint16_t* grT, int64_t M, int64_t D, hipStream_t st) {
   const int64_t ldt = gr_cols(M);  // ldt / 64 <= 2^22 / 64 = 65536 blocks, the device's grid-y limit
   hipLaunchKernelGGL(gr_transpose_kernel, dim3(unsigned(D / 64), unsigned(ldt / 64)), dim3(256), 0, st, g, r, grT, M, D,
                      ldt);
   return hipGetLastError();
-}
-
-// Fused path: s, then bf16(r g) transposed.
-hipError_t bwd_rowstat(const coda_bwd_args_t* a, uint16_t* grT, hipStream_t st) {
-  hipLaunchKernelGGL(rowstat_kernel<false>, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)a->dY,
-                     (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, a->s, grT, a->N, a->D);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return gr_transpose((const uint16_t*)a->g, a->r, grT, a->M, a->D, st);
 }
 
 // Unfused baseline: s and bf16(r g) in row layout from one row kernel.
@@ -1460,9 +1590,31 @@ hipError_t bwd_wgrad_dgamma(const coda_bwd_args_t* a, const uint16_t* grT, const
   return launch_gemm<true, false>(p, EpiStoreDgamma<false>{a->dW1, a->N, p.M, Pg, a->dgamma, rows, a->D}, st);
 }
 
+hipError_t colsum(const float* P, float* out, int64_t rows, int64_t D, hipStream_t st) {
+  hipLaunchKernelGGL(colsum_kernel, dim3(unsigned(ceil_div(D, kDgCols))), dim3(256), 0, st, P, out, rows, D);
+  return hipGetLastError();
+}
 hipError_t bwd_dgamma(const float* Pg, int64_t rows, const coda_bwd_args_t* a, hipStream_t st) {
-  hipLaunchKernelGGL(dgamma_combine_kernel, dim3(unsigned(ceil_div(a->D, kDgCols))), dim3(256), 0, st, Pg, a->dgamma,
-                     rows, a->D);
+  return colsum(Pg, a->dgamma, rows, a->D, st);
+}
+
+// The fused chain backward's weight gradient (dW1 only; its dgamma is combined after the data gradient),
+// with s's partials Ps as side work where bwd_rowdot(D) holds. Shapes as in bwd_wgrad_dgamma.
+hipError_t bwd_wgrad_rowdot(const coda_bwd_args_t* a, const uint16_t* grT, float* Ps, hipStream_t st) {
+  const GemmShape p{a->D, a->N, a->M, grT, gr_cols(a->M), a->dY, a->N};
+  const bool f32 = a->dW1_dtype == CODA_F32;
+  if (!bwd_rowdot(a->D)) return launch_store<true, false>(p, a->dW1, a->N, f32, st);
+  const int ndt = int(ceil_div(a->D, kBN));
+  if (f32)
+    return launch_gemm<true, false>(p, EpiStoreRowDot<true>{a->dW1, a->N, p.M, (const uint16_t*)a->y, Ps, a->N, a->M, ndt}, st);
+  return launch_gemm<true, false>(p, EpiStoreRowDot<false>{a->dW1, a->N, p.M, (const uint16_t*)a->y, Ps, a->N, a->M, ndt}, st);
+}
+
+// s from the side work's partials, or (fewer than 16 row tiles) from a row kernel over dY and y.
+hipError_t bwd_s(const coda_bwd_args_t* a, const float* Ps, hipStream_t st) {
+  if (bwd_rowdot(a->D)) return colsum(Ps, a->s, rowdot_cols(a->N), a->M, st);
+  hipLaunchKernelGGL(rowstat_kernel<false>, dim3(unsigned(a->M)), dim3(kRowThreads), 0, st, (const uint16_t*)a->dY,
+                     (const uint16_t*)a->y, (const uint16_t*)a->g, a->r, a->s, (uint16_t*)nullptr, a->N, a->D);
   return hipGetLastError();
 }
 
@@ -1649,9 +1801,14 @@ coda_status_t coda_bwd_stage(int stage, const coda_bwd_args_t* a, void* ws, size
   if (stage < 0 || stage >= CODA_BWD_STAGES) return CODA_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const BwdWorkspace w = bwd_workspace(ws, a->M, a->D, a->N);
-  if (stage == 0) return to_status(bwd_rowstat(a, w.gr, st));
-  if (stage == 1) return to_status(bwd_dgrad(a, w.Pg, w.part, st));
-  return to_status(bwd_wgrad_dgamma(a, w.gr, w.Pg, w.pg_rows, st));
+  float* Ps = reinterpret_cast<float*>(ws_at(ws, bwd_ws(a->M, a->D, a->N)));
+  switch (stage) {
+    case 0: return to_status(gr_transpose((const uint16_t*)a->g, a->r, w.gr, a->M, a->D, st));
+    case 1: return to_status(bwd_wgrad_rowdot(a, w.gr, Ps, st));
+    case 2: return to_status(bwd_s(a, Ps, st));
+    case 3: return to_status(bwd_dgrad(a, w.Pg, w.part, st));
+    default: return to_status(bwd_dgamma(w.Pg, w.pg_rows, a, st));
+  }
 }
 
 coda_status_t coda_bwd(const coda_bwd_args_t* a, void* ws, size_t ws_bytes, void* stream) {

@@ -284,6 +284,8 @@ __device__ __forceinline__ void mfma_drain(f32x4_t (&acc)[kTM][kTN]) {
 }
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Keeps the compiler from moving memory operations across this point (emits nothing).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
@@ -399,15 +401,69 @@ __device__ __forceinline__ void epi_regions(lds_char_t* smem, int wave, int KT, 
 }
 static_assert(kTileBytes == 2 * kEpiWaveBytes && kWaves * kAuxWaveBytes <= kTileBytes, "epilogue LDS layout");
 
+// Work a kernel may run beside its GEMM, in group 0's phases of the mainloop (group 1 runs the loop
+// unchanged). A side with kActive has, per K step k of a group-0 wave:
+//   flush(k)     at the start of L(k) when k is a positive multiple of kFlush (before the phase's DMA,
+//                so the end-of-phase wait covers its stores): the output of steps k - kFlush .. k - 1;
+//   read(k)      LDS reads of step k's B tile (slot k % 2) after the L(k) fragment reads, covered by
+//                the same LDS wait; landed() follows that wait (asm reads give the compiler no reason
+//                to keep their uses behind it);
+//   work<I>()    after MFMA I of C(k): the arithmetic on what read(k) and load(k) brought, from I = kAt on;
+//   load(k + 1)  right after work<kAt>: one vector-memory load of step k + 1's data into the register
+//                work<kAt> has just read (load(0) in the prologue, after B(0)'s DMA).
+// The load is then the newest vector-memory operation at the end of C(k), so the wait there for B(k + 1)
+// becomes vmcnt(1) and leaves it in flight until C(k + 1); the kernel flushes the last steps after its
+// epilogue.
+struct NoSide {
+  static constexpr bool kActive = false;
+};
+
+// Group 0's side of mainloop (below) with a side's work in it.
+template <bool A_K, bool B_K, class Early, class Side>
+__device__ __forceinline__ void mainloop_side(const Loop<A_K, B_K>& L, int KT, f32x4_t (&acc)[kTM][kTN],
+                                              Frag (&a)[2][kTM], Frag (&b)[2][kTN], Early& early, Side& side) {
+  L.dma_b(0);
+  compiler_fence();  // the side's load is issued after the DMA, as the vmcnt(1) waits assume
+  side.load(0);
+  wait_vm<1>();  // B(0); the side's load stays in flight
+  block_barrier();
+  auto step = [&](int k, auto first, auto last) {
+    if (k > 0 && k % Side::kFlush == 0) side.flush(k);
+    if constexpr (decltype(last)::value) early();
+    else L.dma_b(k + 1);
+    L.load(k, a, b);
+    side.read(k);
+    wait_lgkm0();
+    side.landed();
+    block_barrier();
+    prio_high();
+    compute<decltype(first)::value>(acc, a, b, [&](auto I) {
+      side.template work<decltype(I)::value>();
+      if constexpr (decltype(I)::value == Side::kAt && !decltype(last)::value) side.load(k + 1);
+    });
+    prio_low();
+    if constexpr (!decltype(last)::value) wait_vm<1>();  // B(k + 1); the side's load of step k + 1 stays in flight
+    block_barrier();
+  };
+  if (KT == 1) {
+    step(0, std::true_type{}, std::true_type{});
+  } else {
+    step(0, std::true_type{}, std::false_type{});
+    for (int k = 1; k < KT - 1; ++k) step(k, std::false_type{}, std::false_type{});
+    step(KT - 1, std::false_type{}, std::true_type{});
+  }
+  mfma_drain(acc);
+}
+
 // Group G's side of the loop, for wave 4 G + p:
 //   acc[tm][tn] (lane l, reg e) = C[m0 + 128 G + 16 tm + l % 16][n0 + 64 p + 16 tn + 4 (l / 16) + e].
 // Both groups pass the same number of barriers (1 + 2 KT). early() issues the
 // epilogue's DMA into its LDS (epi_regions) during the last K step: group 0 at the
 // start of that step, group 1 after its last barrier; it adds only to vmcnt, which
 // the epilogue waits for.
-template <bool A_K, bool B_K, int G, class Early>
+template <bool A_K, bool B_K, int G, class Early, class Side>
 __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t n0, lds_char_t* smem,
-                                         f32x4_t (&acc)[kTM][kTN], Early&& early) {
+                                         f32x4_t (&acc)[kTM][kTN], Early&& early, Side& side) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Loop<A_K, B_K> L;
@@ -422,6 +478,10 @@ __device__ __forceinline__ void mainloop(const GemmShape& p, int64_t m0, int64_t
   const int KT = int(dceil_div(p.K, kBK));
 
   Frag a[2][kTM], b[2][kTN];
+  if constexpr (Side::kActive && G == 0) {
+    mainloop_side(L, KT, acc, a, b, early, side);
+    return;
+  }
   auto none = [](auto) {};
   // step(k, first, last): the last step is peeled off (its DMA is the epilogue's), so the
   // loop body carries none of it.
