@@ -403,8 +403,9 @@ static_assert(kTileBytes == 2 * kEpiWaveBytes && kWaves * kAuxWaveBytes <= kTile
 
 // Work a kernel may run beside its GEMM, in group 0's phases of the mainloop (group 1 runs the loop
 // unchanged). A side with kActive has, per K step k of a group-0 wave:
-//   flush(k)     at the start of L(k) when k is a positive multiple of kFlush (before the phase's DMA,
+//   flush(k)     after MFMA 1 of C(k) when k is a positive multiple of kFlush (ahead of the phase's load,
 //                so the end-of-phase wait covers its stores): the output of steps k - kFlush .. k - 1;
+//                in L(k), ahead of the DMA, it delayed the DMA's issue (the dW1 GEMM measured 7 us slower);
 //   read(k)      LDS reads of step k's B tile (slot k % 2) after the L(k) fragment reads, covered by
 //                the same LDS wait; landed() follows that wait (asm reads give the compiler no reason
 //                to keep their uses behind it);
@@ -428,7 +429,6 @@ __device__ __forceinline__ void mainloop_side(const Loop<A_K, B_K>& L, int KT, f
   wait_vm<1>();  // B(0); the side's load stays in flight
   block_barrier();
   auto step = [&](int k, auto first, auto last) {
-    if (k > 0 && k % Side::kFlush == 0) side.flush(k);
     if constexpr (decltype(last)::value) early();
     else L.dma_b(k + 1);
     L.load(k, a, b);
@@ -438,6 +438,9 @@ __device__ __forceinline__ void mainloop_side(const Loop<A_K, B_K>& L, int KT, f
     block_barrier();
     prio_high();
     compute<decltype(first)::value>(acc, a, b, [&](auto I) {
+      if constexpr (decltype(I)::value == 1) {
+        if (k > 0 && k % Side::kFlush == 0) side.flush(k);
+      }
       side.template work<decltype(I)::value>();
       if constexpr (decltype(I)::value == Side::kAt && !decltype(last)::value) side.load(k + 1);
     });
