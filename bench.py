@@ -58,16 +58,41 @@ def stage_work(M, K0, D, N):
     }
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the sources the device code is built from (identifies a counter measurement; the
-    host-only validation in coda_host.cpp is left out)."""
+def _code_only(src: str) -> str:
+    """C/C++ source without its comments and with runs of whitespace collapsed (string and character
+    literals kept as they are), so that editing a comment does not change the digest."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_digest(d=None) -> str:
+    """sha256 over the code (comments and whitespace aside) of the sources the device code is built from;
+    it identifies a counter measurement. The host-only validation in coda_host.cpp is left out."""
     import hashlib
-    d = os.path.join(ROOT, "transformer_gemm_epilogue_res_amd", "csrc")
+    d = d or os.path.join(ROOT, "transformer_gemm_epilogue_res_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(d)):
         if name.endswith((".hip", ".hpp", ".h")):
             h.update(name.encode())
-            h.update(open(os.path.join(d, name), "rb").read())
+            h.update(_code_only(open(os.path.join(d, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -556,8 +556,8 @@ struct EpiRowScale {
     wait_vm0();
     float rr[kTM];
     rs.scales(rr, stage, aux, mb, nb, lane);
-    // y non-temporally: the forward does not read it again, and the backward's row-statistic
-    // pass reads it from HBM faster this way (about 30 us less at the 8B shape)
+    // y non-temporally: the forward does not read it again and the backward reads it once (the dW1 GEMM's
+    // side work, or the row-statistic kernel, which this made about 30 us faster at the 8B shape)
     store_block<F32, true>(stage, lane, y, N, mb, nb, rs.M, [&](int tm, int tn) {
       f32x4_t v = acc[tm][tn];
 #pragma unroll
