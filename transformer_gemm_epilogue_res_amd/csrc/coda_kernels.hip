@@ -1180,37 +1180,48 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* P, float* out,
 
 // bf16(r g) transposed for the weight-gradient GEMM, whose contraction runs over the
 // rows i: grT[j, i] = bf16(r_i g_ij) for i < M and 0 for M <= i < ldt (the pad to the
-// K step). A 256-thread block moves a 64 x 64 tile through LDS: 16-byte row loads of g,
-// 2-byte transposed LDS writes, 16-byte row stores of grT.
+// K step). A 256-thread block moves a 64 x 64 tile through LDS: 16-byte row loads of g
+// and 16-byte LDS row writes, 2-byte LDS column reads, 16-byte row stores of grT (the
+// transposed 2-byte writes of an earlier version met bank conflicts: about 1.3 us slower
+// at the 8B shape).
 __global__ __launch_bounds__(256) void gr_transpose_kernel(const uint16_t* g, const float* r, uint16_t* grT, int64_t M,
                                                            int64_t D, int64_t ldt) {
-  constexpr int kT = 64, kLd = 72;  // LDS row stride 144 bytes: 16-byte aligned rows, spread banks
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kT * kLd];
+  // 64 rows i x 64 columns j through LDS, 128 bytes per row; 16-byte chunk c of row i is stored at chunk
+  // c ^ s(i), s(i) = (i & 7) ^ (i >> 3): a row's 8 chunks are a permutation (16-byte row writes hit every bank
+  // once per 8 lanes), and the column reads -- the same column of rows 8 q + e, q = 0 .. 7 -- fall in 8
+  // different chunks.
+  constexpr int kT = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kT * kT];
   const int64_t j0 = int64_t(blockIdx.x) * kT, i0 = int64_t(blockIdx.y) * kT;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int c = threadIdx.x + 256 * q, row = c >> 3, chunk = c & 7;  // row i0 + row, columns j0 + 8 chunk ..
     const int64_t i = i0 + row;
-    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
     if (i < M) {
+      float f[8];
       unpack8_bf16(*reinterpret_cast<const uint4*>(g + i * D + j0 + 8 * chunk), f);
       const float ri = r[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= ri;
+      o = make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]), pack2_bf16(f[6], f[7]));
     }
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint32_t pk = pack2_bf16(f[e], f[e + 1]);
-      tile[(8 * chunk + e) * kLd + row] = uint16_t(pk & 0xffffu);
-      tile[(8 * chunk + e + 1) * kLd + row] = uint16_t(pk >> 16);
-    }
+    const int s = (row & 7) ^ (row >> 3);
+    *reinterpret_cast<uint4*>(&tile[row * kT + 8 * (chunk ^ s)]) = o;
   }
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int c = threadIdx.x + 256 * q, jr = c >> 3, chunk = c & 7;  // grT row j0 + jr, columns i0 + 8 chunk ..
-    const uint4 v = *reinterpret_cast<const uint4*>(&tile[jr * kLd + 8 * chunk]);
-    *reinterpret_cast<uint4*>(grT + (j0 + jr) * ldt + i0 + 8 * chunk) = v;
+    const int c = threadIdx.x + 256 * q, jr = c >> 3, ic = c & 7;  // grT row j0 + jr, columns i0 + 8 ic ..
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int ra = 8 * ic + e, rb = ra + 1;
+      const uint32_t a = tile[ra * kT + 8 * ((jr >> 3) ^ ((ra & 7) ^ (ra >> 3))) + (jr & 7)];
+      const uint32_t b = tile[rb * kT + 8 * ((jr >> 3) ^ ((rb & 7) ^ (rb >> 3))) + (jr & 7)];
+      w[e / 2] = a | (b << 16);
+    }
+    *reinterpret_cast<uint4*>(grT + (j0 + jr) * ldt + i0 + 8 * ic) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
