@@ -426,7 +426,7 @@ def shape(name):
     return FWD_SMALL[name] if name in FWD_SMALL else BWD_SMALL[name]
 
 
-@pytest.mark.parametrize("name", ["ragged", "rowdot"])
+@pytest.mark.parametrize("name", ["ragged", "rowdot", "rowdot_flush"])
 def test_run_to_run_bitwise_determinism(name):
     c = shape(name)
     announce(f"determinism coda_fwd/coda_bwd {name} {c}")
@@ -444,11 +444,12 @@ def test_run_to_run_bitwise_determinism(name):
         assert torch.equal(p[k], q[k]), k
 
 
-@pytest.mark.parametrize("name", ["ragged", "unfolded_wide", "rowdot"])
+@pytest.mark.parametrize("name", ["ragged", "unfolded_wide", "rowdot", "rowdot_flush"])
 def test_stages_match_whole_call(name):
     """coda_fwd_stage / coda_bwd_stage 0..n-1 in order give the whole call's results bit for bit, whether
-    GEMM1 combines r itself (ragged: stage 1 launches nothing) or a separate kernel does (unfolded_wide), and
-    whether s comes from a row kernel or from the dW1 GEMM's side work (rowdot)."""
+    GEMM1 combines r itself (ragged: stage 1 launches nothing) or a separate kernel does (unfolded_wide),
+    whether s comes from a row kernel or from the dW1 GEMM's side work (rowdot), and whether the data
+    gradient is split over its contraction (rowdot) or not (rowdot_flush, 17 row tiles)."""
     c = shape(name)
     announce(f"stages vs whole call {name} {c}")
     M, D, N = c["M"], c["D"], c["N"]
@@ -534,7 +535,7 @@ def test_no_writes_outside_outputs(name, M):
     assert torch.isfinite(out["y"].float()).all() and torch.isfinite(bo["da"]).all()
 
 
-@pytest.mark.parametrize("name", ["ragged", "rowdot"])
+@pytest.mark.parametrize("name", ["ragged", "rowdot", "rowdot_flush"])
 def test_graph_capture_replays_match_eager(name):
     """The step (coda_fwd + coda_bwd) captured into a HIP graph: the library allocates, frees and
     clears nothing, so every replay reproduces the eager results bit for bit."""
